@@ -1,0 +1,673 @@
+// Causal multi-head attention, forward and backward, without materialising T x T.
+//
+// What is computed: per (batch, head), out = softmax(Q K^T / sqrt(hs)) V over keys u <= t
+// (the LLM primer page "从Andrej Karpathy《深入了解ChatGPT之类的大语言模型》入门LLMs" gives
+// softmax(QK^T/sqrt(d_k))V; GPT-2 masks the future). The llm.c tour ("Karpathy 的 llm.c：从零理解
+// 大模型训练的 C/CUDA 实现", sections 代码解剖 and 性能对比) describes hand-written warp
+// reductions for the softmax and an attention fused into two kernels; here the whole forward is
+// one kernel with an online softmax (running max and sum), which keeps nothing T x T in HBM, and
+// the backward recomputes the probabilities from the saved log-sum-exp.
+//
+// Layout: qkv [B, T, 3C] with Q | K | V thirds, head h at columns h*hs .. h*hs+hs-1 of each
+// third; out [B, T, C]; lse [B, H, T] (natural log). dqkv uses the qkv layout.
+//
+// Backward (D = rowsum(dO * O)):  P = exp(S - lse);  dV = P^T dO;  dP = dO V^T;
+//   dS = P * (dP - D);  dQ = dS K / sqrt(hs);  dK = dS^T Q / sqrt(hs).
+// dK, dV are owned by key blocks and dQ by query blocks (two kernels), so no float atomics are
+// needed and results are bitwise reproducible.
+//
+// Two implementations:
+//  * bf16, hs = 64: MFMA 32x32x16 kernels. The softmax runs on S^T tiles (keys as MFMA rows,
+//    queries as columns) so each lane owns one query: the row max/sum over keys is a register
+//    reduction plus one v_permlane32_swap with the other half-wave. The fp32 accumulator of one
+//    MFMA is fed, converted to bf16, straight into the next MFMA as an operand; the operand it
+//    meets is read from an LDS tile stored transposed, in the same key order.
+//  * fp32 (any hs <= 64): one thread per query (forward, dQ) or per key (dK/dV), K/V or Q/dO
+//    tiles staged in LDS; exact fp32 math for the fp32 training configurations.
+#include "common.h"
+#include "kernels.h"
+
+namespace g2 {
+
+// =====================================================================================
+// fp32 reference-precision kernels (vector ALU)
+// =====================================================================================
+constexpr int AT = 64;  // tile of queries / keys per block
+
+template <int HS>
+__global__ __launch_bounds__(AT) void attn_fwd_f32(int T, int H, const float* __restrict__ qkv,
+                                                   float* __restrict__ out, float* __restrict__ lse, float scale) {
+  __shared__ float Ks[AT][HS + 1], Vs[AT][HS + 1];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int C = H * HS, C3 = 3 * C;
+  const int q0 = blockIdx.x * AT;
+  const int qi = q0 + threadIdx.x;
+  const float* base = qkv + (size_t)b * T * C3;
+  float q[HS], o[HS];
+  for (int d = 0; d < HS; ++d) {
+    q[d] = qi < T ? base[(size_t)qi * C3 + h * HS + d] * scale : 0.f;
+    o[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = min(T, q0 + AT);
+  for (int k0 = 0; k0 < kend; k0 += AT) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < AT * HS; i += AT) {
+      const int r = i / HS, d = i % HS;
+      const int kr = k0 + r;
+      Ks[r][d] = kr < T ? base[(size_t)kr * C3 + C + h * HS + d] : 0.f;
+      Vs[r][d] = kr < T ? base[(size_t)kr * C3 + 2 * C + h * HS + d] : 0.f;
+    }
+    __syncthreads();
+    if (qi < T) {
+      const int jn = min(AT, qi - k0 + 1);
+      for (int j = 0; j < jn; ++j) {
+        float s = 0.f;
+        for (int d = 0; d < HS; ++d) s += q[d] * Ks[j][d];
+        const float mn = fmaxf(m, s);
+        const float corr = expf(m - mn);
+        const float pj = expf(s - mn);
+        l = l * corr + pj;
+        for (int d = 0; d < HS; ++d) o[d] = o[d] * corr + pj * Vs[j][d];
+        m = mn;
+      }
+    }
+  }
+  if (qi < T) {
+    const float inv = 1.f / l;
+    for (int d = 0; d < HS; ++d) out[((size_t)b * T + qi) * C + h * HS + d] = o[d] * inv;
+    lse[(size_t)bh * T + qi] = m + logf(l);
+  }
+}
+
+// D[b,h,t] = sum_d dO * O  (fp32 or bf16 inputs)
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_dvec(int BT, int T_, int H, int hs, const T* __restrict__ out,
+                                                     const T* __restrict__ dout, float* __restrict__ dvec) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // over B*T*H
+  if (i >= BT * H) return;
+  const int row = i / H, h = i % H;
+  const int C = H * hs;
+  const size_t o = (size_t)row * C + h * hs;
+  float s = 0.f;
+  for (int d = 0; d < hs; d += Elt<T>::VEC) {
+    V16<T> a, c;
+    a.load(out + o + d);
+    c.load(dout + o + d);
+#pragma unroll
+    for (int e = 0; e < Elt<T>::VEC; ++e) s += a.v[e] * c.v[e];
+  }
+  const int b = row / T_, t = row % T_;
+  dvec[((size_t)b * H + h) * T_ + t] = s;
+}
+
+// dK, dV: one thread per key
+template <int HS>
+__global__ __launch_bounds__(AT) void attn_bwd_kv_f32(int T, int H, const float* __restrict__ qkv,
+                                                      const float* __restrict__ dout, const float* __restrict__ lse,
+                                                      const float* __restrict__ dvec, float* __restrict__ dqkv,
+                                                      float scale) {
+  __shared__ float Qs[AT][HS + 1], dOs[AT][HS + 1], Ls[AT], Ds[AT];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int C = H * HS, C3 = 3 * C;
+  const int k0 = blockIdx.x * AT;
+  const int kj = k0 + threadIdx.x;
+  const float* base = qkv + (size_t)b * T * C3;
+  float k[HS], v[HS], dk[HS], dv[HS];
+  for (int d = 0; d < HS; ++d) {
+    k[d] = kj < T ? base[(size_t)kj * C3 + C + h * HS + d] : 0.f;
+    v[d] = kj < T ? base[(size_t)kj * C3 + 2 * C + h * HS + d] : 0.f;
+    dk[d] = dv[d] = 0.f;
+  }
+  for (int q0 = k0; q0 < T; q0 += AT) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < AT * HS; i += AT) {
+      const int r = i / HS, d = i % HS;
+      const int qr = q0 + r;
+      Qs[r][d] = qr < T ? base[(size_t)qr * C3 + h * HS + d] : 0.f;
+      dOs[r][d] = qr < T ? dout[((size_t)b * T + qr) * C + h * HS + d] : 0.f;
+    }
+    if (threadIdx.x < AT) {
+      const int qr = q0 + threadIdx.x;
+      Ls[threadIdx.x] = qr < T ? lse[(size_t)bh * T + qr] : 0.f;
+      Ds[threadIdx.x] = qr < T ? dvec[(size_t)bh * T + qr] : 0.f;
+    }
+    __syncthreads();
+    if (kj < T) {
+      for (int i = 0; i < AT; ++i) {
+        const int qi = q0 + i;
+        if (qi >= T) break;
+        if (qi < kj) continue;
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < HS; ++d) {
+          s += Qs[i][d] * k[d];
+          dp += dOs[i][d] * v[d];
+        }
+        const float p = expf(s * scale - Ls[i]);
+        const float ds = p * (dp - Ds[i]);
+        for (int d = 0; d < HS; ++d) {
+          dv[d] += p * dOs[i][d];
+          dk[d] += ds * Qs[i][d];
+        }
+      }
+    }
+  }
+  if (kj < T) {
+    float* dst = dqkv + ((size_t)b * T + kj) * C3 + h * HS;
+    for (int d = 0; d < HS; ++d) {
+      dst[C + d] = dk[d] * scale;
+      dst[2 * C + d] = dv[d];
+    }
+  }
+}
+
+// dQ: one thread per query
+template <int HS>
+__global__ __launch_bounds__(AT) void attn_bwd_q_f32(int T, int H, const float* __restrict__ qkv,
+                                                     const float* __restrict__ dout, const float* __restrict__ lse,
+                                                     const float* __restrict__ dvec, float* __restrict__ dqkv,
+                                                     float scale) {
+  __shared__ float Ks[AT][HS + 1], Vs[AT][HS + 1];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int C = H * HS, C3 = 3 * C;
+  const int q0 = blockIdx.x * AT;
+  const int qi = q0 + threadIdx.x;
+  const float* base = qkv + (size_t)b * T * C3;
+  float q[HS], dO[HS], dq[HS];
+  for (int d = 0; d < HS; ++d) {
+    q[d] = qi < T ? base[(size_t)qi * C3 + h * HS + d] : 0.f;
+    dO[d] = qi < T ? dout[((size_t)b * T + qi) * C + h * HS + d] : 0.f;
+    dq[d] = 0.f;
+  }
+  const float L = qi < T ? lse[(size_t)bh * T + qi] : 0.f;
+  const float Dq = qi < T ? dvec[(size_t)bh * T + qi] : 0.f;
+  const int kend = min(T, q0 + AT);
+  for (int k0 = 0; k0 < kend; k0 += AT) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < AT * HS; i += AT) {
+      const int r = i / HS, d = i % HS;
+      const int kr = k0 + r;
+      Ks[r][d] = kr < T ? base[(size_t)kr * C3 + C + h * HS + d] : 0.f;
+      Vs[r][d] = kr < T ? base[(size_t)kr * C3 + 2 * C + h * HS + d] : 0.f;
+    }
+    __syncthreads();
+    if (qi < T) {
+      const int jn = min(AT, qi - k0 + 1);
+      for (int j = 0; j < jn; ++j) {
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < HS; ++d) {
+          s += q[d] * Ks[j][d];
+          dp += dO[d] * Vs[j][d];
+        }
+        const float p = expf(s * scale - L);
+        const float ds = p * (dp - Dq);
+        for (int d = 0; d < HS; ++d) dq[d] += ds * Ks[j][d];
+      }
+    }
+  }
+  if (qi < T) {
+    float* dst = dqkv + ((size_t)b * T + qi) * C3 + h * HS;
+    for (int d = 0; d < HS; ++d) dst[d] = dq[d] * scale;
+  }
+}
+
+template <int HS>
+static void f32_fwd(int B, int T, int H, const float* qkv, float* out, float* lse, hipStream_t s) {
+  dim3 grid(cdiv(T, AT), B * H);
+  attn_fwd_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, out, lse, 1.0f / sqrtf((float)HS));
+}
+template <int HS>
+static void f32_bwd(int B, int T, int H, const float* qkv, const float* dout, const float* lse, const float* dvec,
+                    float* dqkv, hipStream_t s) {
+  dim3 grid(cdiv(T, AT), B * H);
+  attn_bwd_kv_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, dout, lse, dvec, dqkv, 1.0f / sqrtf((float)HS));
+  attn_bwd_q_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, dout, lse, dvec, dqkv, 1.0f / sqrtf((float)HS));
+}
+
+// =====================================================================================
+// bf16 MFMA kernels, hs = 64
+// =====================================================================================
+constexpr int HD = 64;          // head size
+constexpr int KT = 64;          // keys (or queries) per LDS tile
+constexpr int LDP = HD + 8;     // LDS pitch (elements) of a 64-wide bf16 tile, 16-byte pad
+constexpr int BQ = 128;         // rows owned by a block (4 waves x 32)
+
+__device__ __forceinline__ bf16x8 lds_frag16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+// two 8-byte LDS reads: slots 0..3 from p0, 4..7 from p1
+__device__ __forceinline__ bf16x8 lds_frag8x2(const uint16_t* p0, const uint16_t* p1) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
+  const u32x4 r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ bf16x8 pack_frag(const float* x) {  // 8 fp32 -> bf16x8
+  const u32x4 r = {pack2bf(x[0], x[1]), pack2bf(x[2], x[3]), pack2bf(x[4], x[5]), pack2bf(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+// row (M index) of accumulator element i for lane group g (= lane / 32)
+__device__ __forceinline__ int acc_row(int i, int g) { return (i >> 2) * 8 + g * 4 + (i & 3); }
+
+// A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile).
+struct Piece {
+  u32x4 r[4];
+  __device__ __forceinline__ void load(const uint16_t* src, long ld, int row0, int nrows, int p) {
+    const int rg = (p >> 3) * 4, cg = (p & 7) * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = row0 + rg + j;
+      r[j] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + cg) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store_rows(uint16_t* lds, int p) const {  // lds[row][col]
+    const int rg = (p >> 3) * 4, cg = (p & 7) * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + j) * LDP + cg) = r[j];
+  }
+  __device__ __forceinline__ void store_cols(uint16_t* lds, int p) const {  // lds[col][row]
+    const int rg = (p >> 3) * 4, cg = (p & 7) * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d = c >> 1;
+      u32x2 o;
+      if ((c & 1) == 0) {
+        o[0] = (r[0][d] & 0xffffu) | (r[1][d] << 16);
+        o[1] = (r[2][d] & 0xffffu) | (r[3][d] << 16);
+      } else {
+        o[0] = (r[0][d] >> 16) | (r[1][d] & 0xffff0000u);
+        o[1] = (r[2][d] >> 16) | (r[3][d] & 0xffff0000u);
+      }
+      *reinterpret_cast<u32x2*>(lds + (cg + c) * LDP + rg) = o;
+    }
+  }
+};
+
+// ---------------------------------------------------------------- forward
+// grid (T/128, B*H), 256 threads. Wave w owns queries q0 + 32w .. +31.
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint16_t* __restrict__ qkv,
+                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * LDP];  // [d][key]
+  const int nqt = gridDim.x;
+  const int qt = nqt - 1 - blockIdx.x;  // heaviest tiles first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int C = H * HD;
+  const long C3 = 3L * C;
+  const uint16_t* base = qkv + (size_t)b * T * C3;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int q0 = qt * BQ;
+  const int qw0 = q0 + 32 * w;
+  const int myq = qw0 + l32;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[myq][16s + 8g .. +8]
+  bf16x8 qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (myq < T) x = *reinterpret_cast<const u32x4*>(base + (size_t)myq * C3 + h * HD + 16 * s + 8 * g);
+    qf[s] = __builtin_bit_cast(bf16x8, x);
+  }
+  const float c2 = LOG2E / sqrtf((float)HD);  // scale folded into base-2 exponent
+  f32x16 o[2] = {zero16(), zero16()};         // O^T: rows d (2 x 32), columns = queries
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = min(T, q0 + BQ);
+  const int ntiles = cdiv(kend, KT);
+  Piece pc;
+  const int p = tid & 127;
+  const bool is_k = tid < 128;
+  auto load_tile = [&](int kt) {
+    pc.load(base + (is_k ? C : 2 * C) + h * HD, C3, kt * KT, T, p);
+  };
+  load_tile(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    if (is_k) pc.store_rows(Ks, p);
+    else pc.store_cols(Vt, p);
+    __syncthreads();
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb = kt * KT + sb * 32;
+      if (kb > qw0 + 31) continue;  // entirely in the future of this wave's queries
+      f32x16 st = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) st = mfma(lds_frag16(Ks + (sb * 32 + l32) * LDP + 16 * s + 8 * g), qf[s], st);
+      float sc[16];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + acc_row(i, g);
+        sc[i] = key <= myq ? st[i] * c2 : -INFINITY;
+        mloc = fmaxf(mloc, sc[i]);
+      }
+      mloc = pair_max(mloc);
+      const float m_new = fmaxf(m_run, mloc);
+      const float corr = fast_exp2(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = fast_exp2(sc[i] - m_new);
+        psum += sc[i];
+      }
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= corr;
+      // O^T += V^T P^T : A = V^T (rows d, k = keys), B = P^T (k = keys, columns = queries)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pf = pack_frag(sc + 8 * ks);
+        const int kofs = sb * 32 + 16 * ks + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const uint16_t* vrow = Vt + (db * 32 + l32) * LDP;
+          o[db] = mfma(lds_frag8x2(vrow + kofs, vrow + kofs + 8), pf, o[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const float l_tot = pair_sum(l_run);
+  if (myq < T) {
+    const float inv = 1.f / l_tot;
+    uint16_t* dst = out + ((size_t)b * T + myq) * C + h * HD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + r4 * 8 + 4 * g;
+        const u32x2 v = {pack2bf(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv),
+                         pack2bf(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + d) = v;
+      }
+    if (g == 0) lse[(size_t)bh * T + myq] = (m_run + __log2f(l_tot)) / LOG2E;
+  }
+}
+
+// ---------------------------------------------------------------- backward: dK, dV
+// grid (T/128, B*H): block owns 128 keys (wave w: 32 keys), loops over 64-query tiles.
+__global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const uint16_t* __restrict__ qkv,
+                                                           const uint16_t* __restrict__ dout,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ dvec,
+                                                           uint16_t* __restrict__ dqkv) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[KT * LDP];   // [q][d]
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[KT * LDP];  // [q][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[HD * LDP];   // [d][q]
+  __shared__ __attribute__((aligned(16))) uint16_t dOt[HD * LDP];  // [d][q]
+  __shared__ float Ls[KT], Dsh[KT];
+  const int nkt = gridDim.x;
+  const int kt_blk = nkt - 1 - blockIdx.x;  // heaviest (earliest keys) first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int C = H * HD;
+  const long C3 = 3L * C;
+  const uint16_t* base = qkv + (size_t)b * T * C3;
+  const uint16_t* dbase = dout + (size_t)b * T * C;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int k0 = kt_blk * BQ;
+  const int kw0 = k0 + 32 * w;
+  const int mykey = kw0 + l32;
+  const float c2 = LOG2E / sqrtf((float)HD);
+
+  // K and V of this lane's key as B operands (S = Q K^T, dP = dO V^T)
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+    if (mykey < T) {
+      xk = *reinterpret_cast<const u32x4*>(base + (size_t)mykey * C3 + C + h * HD + 16 * s + 8 * g);
+      xv = *reinterpret_cast<const u32x4*>(base + (size_t)mykey * C3 + 2 * C + h * HD + 16 * s + 8 * g);
+    }
+    kf[s] = __builtin_bit_cast(bf16x8, xk);
+    vf[s] = __builtin_bit_cast(bf16x8, xv);
+  }
+  f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};  // rows = keys, cols = d
+
+  const int qstart = (k0 / KT) * KT;
+  const int ntiles = cdiv(T - qstart, KT);
+  Piece pc;
+  const int p = tid & 127;
+  const bool is_q = tid < 128;
+  auto load_tile = [&](int it) {
+    const int qt0 = qstart + it * KT;
+    if (is_q) pc.load(base + h * HD, C3, qt0, T, p);
+    else pc.load(dbase + h * HD, C, qt0, T, p);
+  };
+  if (ntiles > 0) load_tile(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int qt0 = qstart + it * KT;
+    if (is_q) {
+      pc.store_rows(Qs, p);
+      pc.store_cols(Qt, p);
+    } else {
+      pc.store_rows(dOs, p);
+      pc.store_cols(dOt, p);
+    }
+    if (tid < KT) {
+      const int qr = qt0 + tid;
+      Ls[tid] = qr < T ? lse[(size_t)bh * T + qr] * LOG2E : 0.f;
+      Dsh[tid] = qr < T ? dvec[(size_t)bh * T + qr] : 0.f;
+    }
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(it + 1);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qq0 = qt0 + 32 * qb;
+      if (qq0 + 31 < kw0) continue;  // all queries before this wave's keys
+      f32x16 sacc = zero16(), dpacc = zero16();  // rows = queries, cols = keys
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 qa = lds_frag16(Qs + (32 * qb + l32) * LDP + 16 * s + 8 * g);
+        const bf16x8 da = lds_frag16(dOs + (32 * qb + l32) * LDP + 16 * s + 8 * g);
+        sacc = mfma(qa, kf[s], sacc);
+        dpacc = mfma(da, vf[s], dpacc);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qr = 32 * qb + acc_row(i, g);
+        const int q = qt0 + qr;
+        const float pv = (mykey <= q && q < T) ? fast_exp2(sacc[i] * c2 - Ls[qr]) : 0.f;
+        pr[i] = pv;
+        ds[i] = pv * (dpacc[i] - Dsh[qr]);
+      }
+      // dV += P^T dO ; dK += dS^T Q  (A = accumulator as [key][q], B from transposed tiles)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pa = pack_frag(pr + 8 * ks);
+        const bf16x8 sa = pack_frag(ds + 8 * ks);
+        const int qofs = 32 * qb + 16 * ks + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const uint16_t* dorow = dOt + (db * 32 + l32) * LDP;
+          const uint16_t* qrow = Qt + (db * 32 + l32) * LDP;
+          dv[db] = mfma(pa, lds_frag8x2(dorow + qofs, dorow + qofs + 8), dv[db]);
+          dk[db] = mfma(sa, lds_frag8x2(qrow + qofs, qrow + qofs + 8), dk[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // store: accumulator rows = keys, columns = d
+  const float sc = 1.0f / sqrtf((float)HD);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int d = db * 32 + l32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kw0 + acc_row(i, g);
+      if (key < T) {
+        uint16_t* dst = dqkv + ((size_t)b * T + key) * C3 + h * HD + d;
+        dst[C] = f2bf(dk[db][i] * sc);
+        dst[2 * C] = f2bf(dv[db][i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- backward: dQ
+// grid (T/128, B*H): block owns 128 queries (wave w: 32), loops over 64-key tiles.
+__global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const uint16_t* __restrict__ qkv,
+                                                          const uint16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ dvec,
+                                                          uint16_t* __restrict__ dqkv) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[HD * LDP];  // [d][key]
+  const int nqt = gridDim.x;
+  const int qt = nqt - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int C = H * HD;
+  const long C3 = 3L * C;
+  const uint16_t* base = qkv + (size_t)b * T * C3;
+  const uint16_t* dbase = dout + (size_t)b * T * C;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int q0 = qt * BQ;
+  const int qw0 = q0 + 32 * w;
+  const int myq = qw0 + l32;
+  const float c2 = LOG2E / sqrtf((float)HD);
+
+  bf16x8 qf[4], df[4];  // B operands: Q[myq], dO[myq]
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
+    if (myq < T) {
+      xq = *reinterpret_cast<const u32x4*>(base + (size_t)myq * C3 + h * HD + 16 * s + 8 * g);
+      xd = *reinterpret_cast<const u32x4*>(dbase + (size_t)myq * C + h * HD + 16 * s + 8 * g);
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, xq);
+    df[s] = __builtin_bit_cast(bf16x8, xd);
+  }
+  const float L2 = myq < T ? lse[(size_t)bh * T + myq] * LOG2E : 0.f;
+  const float Dq = myq < T ? dvec[(size_t)bh * T + myq] : 0.f;
+  f32x16 dq[2] = {zero16(), zero16()};  // rows = queries, cols = d
+
+  const int kend = min(T, q0 + BQ);
+  const int ntiles = cdiv(kend, KT);
+  Piece pc;
+  const int p = tid & 127;
+  const bool is_k = tid < 128;
+  auto load_tile = [&](int kt) { pc.load(base + (is_k ? C : 2 * C) + h * HD, C3, kt * KT, T, p); };
+  load_tile(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    if (is_k) {
+      pc.store_rows(Ks, p);
+      pc.store_cols(Kt, p);
+    } else {
+      pc.store_rows(Vs, p);
+    }
+    __syncthreads();
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb = kt * KT + sb * 32;
+      if (kb > qw0 + 31) continue;
+      f32x16 st = zero16(), dpt = zero16();  // rows = keys, cols = queries
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        st = mfma(lds_frag16(Ks + (sb * 32 + l32) * LDP + 16 * s + 8 * g), qf[s], st);
+        dpt = mfma(lds_frag16(Vs + (sb * 32 + l32) * LDP + 16 * s + 8 * g), df[s], dpt);
+      }
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + acc_row(i, g);
+        const float pv = (key <= myq && myq < T) ? fast_exp2(st[i] * c2 - L2) : 0.f;
+        ds[i] = pv * (dpt[i] - Dq);
+      }
+      // dQ += dS K : A = dS (rows q, k = keys) from the accumulator, B = K from Kt [d][key]
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 sa = pack_frag(ds + 8 * ks);
+        const int kofs = sb * 32 + 16 * ks + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const uint16_t* krow = Kt + (db * 32 + l32) * LDP;
+          dq[db] = mfma(sa, lds_frag8x2(krow + kofs, krow + kofs + 8), dq[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const float sc = 1.0f / sqrtf((float)HD);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int d = db * 32 + l32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = qw0 + acc_row(i, g);
+      if (q < T) dqkv[((size_t)b * T + q) * C3 + h * HD + d] = f2bf(dq[db][i] * sc);
+    }
+  }
+}
+
+// =====================================================================================
+hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,
+                                hipStream_t s) {
+  if (B * T <= 0) return hipSuccess;
+  if (dt == DT_BF16) {
+    if (hs != HD) return hipErrorInvalidValue;
+    dim3 grid(cdiv(T, BQ), B * H);
+    attn_fwd_bf16<<<grid, 256, 0, s>>>(T, H, reinterpret_cast<const uint16_t*>(qkv),
+                                       reinterpret_cast<uint16_t*>(out), lse);
+    return hipGetLastError();
+  }
+  auto Q = reinterpret_cast<const float*>(qkv);
+  auto O = reinterpret_cast<float*>(out);
+  switch (hs) {
+    case 4: f32_fwd<4>(B, T, H, Q, O, lse, s); break;
+    case 8: f32_fwd<8>(B, T, H, Q, O, lse, s); break;
+    case 16: f32_fwd<16>(B, T, H, Q, O, lse, s); break;
+    case 32: f32_fwd<32>(B, T, H, Q, O, lse, s); break;
+    case 64: f32_fwd<64>(B, T, H, Q, O, lse, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
+                                const void* dout, const float* lse, void* dqkv, float* dvec, hipStream_t s) {
+  if (B * T <= 0) return hipSuccess;
+  const int BT = B * T;
+  if (dt == DT_BF16) {
+    if (hs != HD) return hipErrorInvalidValue;
+    attn_bwd_dvec<bf16><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, hs, reinterpret_cast<const bf16*>(out),
+                                                                reinterpret_cast<const bf16*>(dout), dvec);
+    dim3 grid(cdiv(T, BQ), B * H);
+    auto Q = reinterpret_cast<const uint16_t*>(qkv);
+    auto dO = reinterpret_cast<const uint16_t*>(dout);
+    auto dQ = reinterpret_cast<uint16_t*>(dqkv);
+    attn_bwd_kv_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
+    attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
+    return hipGetLastError();
+  }
+  attn_bwd_dvec<float><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, hs, reinterpret_cast<const float*>(out),
+                                                              reinterpret_cast<const float*>(dout), dvec);
+  auto Q = reinterpret_cast<const float*>(qkv);
+  auto dO = reinterpret_cast<const float*>(dout);
+  auto dQ = reinterpret_cast<float*>(dqkv);
+  switch (hs) {
+    case 4: f32_bwd<4>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
+    case 8: f32_bwd<8>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
+    case 16: f32_bwd<16>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
+    case 32: f32_bwd<32>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
+    case 64: f32_bwd<64>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace g2

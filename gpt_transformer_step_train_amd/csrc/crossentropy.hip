@@ -1,0 +1,155 @@
+// Fused softmax cross-entropy + logit gradient, and the deterministic loss mean.
+//
+// The llm.c tour ("Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 代码解剖)
+// says the backward starts from the gradient of the loss w.r.t. the logits; the GPT-2
+// reproduction post ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section PyTorch 对比)
+// credits a fused classifier. Here one block per row reads the row once into registers, takes
+// its max and sum of exponentials over the V real classes (fp32, wave64 DPP reductions), writes
+// the row loss lse - logit[target], and overwrites the logits in place with
+// (softmax - onehot(target)) * dloss; padded columns v >= V and ignored rows get 0.
+// dloss = 1 / (number of valid targets * micro-steps per update) is read from device memory,
+// computed by count_targets, so no host round trip is needed.
+#include "common.h"
+#include "kernels.h"
+
+namespace g2 {
+
+constexpr int CE_THREADS = 1024;
+constexpr int CE_WAVES = CE_THREADS / 64;
+
+// dloss_out = 1/(n_valid * accum) (0 when n_valid == 0); nvalid_out = n_valid; err |= 2 on bad target
+__global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __restrict__ targets, int rows, int V,
+                                                             int accum, float* dloss_out, int* nvalid_out, int* err) {
+  __shared__ float red[16];
+  float c = 0.f;
+  bool bad = false;
+  for (int i = threadIdx.x; i < rows; i += 1024) {
+    const int t = targets[i];
+    if (t >= 0 && t < V) c += 1.f;
+    if (t >= V) bad = true;
+  }
+  if (bad) atomicOr(err, 2);
+  const float n = block_sum<16>(c, red);
+  if (threadIdx.x == 0) {
+    *nvalid_out = (int)n;
+    *dloss_out = n > 0.f ? (float)(1.0 / ((double)n * accum)) : 0.f;
+  }
+}
+
+template <typename T, int NVT>
+__global__ __launch_bounds__(CE_THREADS) void ce_kernel(int V, int ld, T* __restrict__ logits,
+                                                        const int32_t* __restrict__ targets,
+                                                        const float* __restrict__ dloss_p, float* __restrict__ losses) {
+  constexpr int VEC = Elt<T>::VEC;
+  __shared__ float red[CE_WAVES];
+  __shared__ float xt_sh;
+  const int row = blockIdx.x;
+  T* x = logits + (size_t)row * ld;
+  int tgt = targets ? targets[row] : -1;
+  if (tgt >= V) tgt = -1;  // reported by count_targets
+  const int nvec = ld / VEC;
+  if (threadIdx.x == 0) xt_sh = tgt >= 0 ? ld1(x, tgt) : 0.f;
+
+  V16<T> xv[NVT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) {
+    const int v = threadIdx.x + j * CE_THREADS;
+    if (v < nvec) {
+      xv[j].load(x + (size_t)v * VEC);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        if (v * VEC + e >= V) xv[j].v[e] = -INFINITY;
+        mx = fmaxf(mx, xv[j].v[e]);
+      }
+    }
+  }
+  mx = block_max<CE_WAVES>(mx, red);
+  const float mx2 = mx * LOG2E;
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) {
+    const int v = threadIdx.x + j * CE_THREADS;
+    if (v < nvec) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float p = fast_exp2(xv[j].v[e] * LOG2E - mx2);
+        xv[j].v[e] = p;  // unnormalised probability (0 for padded columns)
+        se += p;
+      }
+    }
+  }
+  se = block_sum<CE_WAVES>(se, red);  // includes the barrier that publishes xt_sh
+  const float lse = mx + logf(se);
+  if (threadIdx.x == 0) losses[row] = tgt >= 0 ? lse - xt_sh : 0.f;
+  if (!dloss_p) return;
+  const float dl = tgt >= 0 ? *dloss_p : 0.f;
+  const float inv = dl / se;
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) {
+    const int v = threadIdx.x + j * CE_THREADS;
+    if (v < nvec) {
+      V16<T> o;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int col = v * VEC + e;
+        o.v[e] = xv[j].v[e] * inv - (col == tgt ? dl : 0.f);
+      }
+      o.store(x + (size_t)v * VEC);
+    }
+  }
+}
+
+template <typename T>
+static hipError_t ce_t(int rows, int V, int ld, void* logits, const int32_t* targets, const float* dloss,
+                       float* losses, hipStream_t s) {
+  constexpr int VEC = Elt<T>::VEC;
+  const int nvt = cdiv(ld / VEC, CE_THREADS);
+  T* L = reinterpret_cast<T*>(logits);
+  if (nvt <= 1) ce_kernel<T, 1><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
+  else if (nvt <= 2) ce_kernel<T, 2><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
+  else if (nvt <= 4) ce_kernel<T, 4><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
+  else if (nvt <= 8) ce_kernel<T, 8><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
+  else if (nvt <= 16) ce_kernel<T, 16><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_count_targets(const int32_t* targets, int rows, int V, int accum, float* dloss, int* nvalid,
+                                int* err, hipStream_t s) {
+  count_targets_kernel<<<1, 1024, 0, s>>>(targets, rows, V, accum, dloss, nvalid, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_cross_entropy(DType dt, int rows, int V, int ld, void* logits, const int32_t* targets,
+                                const float* dloss, float* losses, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (ld % (dt == DT_BF16 ? 8 : 4)) return hipErrorInvalidValue;
+  return dt == DT_BF16 ? ce_t<bf16>(rows, V, ld, logits, targets, dloss, losses, s)
+                       : ce_t<float>(rows, V, ld, logits, targets, dloss, losses, s);
+}
+
+// mean = sum(losses) / n_valid in double, fixed order (one block); writes float and double
+__global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict__ losses, int rows,
+                                                         const int* __restrict__ nvalid, float* out) {
+  __shared__ double sh[1024];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < rows; i += 1024) s += (double)losses[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int n = *nvalid;
+    out[0] = n > 0 ? (float)(sh[0] / n) : 0.f;
+  }
+}
+
+hipError_t launch_loss_mean(const float* losses, int rows, const int* nvalid, float* out, hipStream_t s) {
+  loss_mean_kernel<<<1, 1024, 0, s>>>(losses, rows, nvalid, out);
+  return hipGetLastError();
+}
+
+}  // namespace g2

@@ -1,0 +1,229 @@
+// Token + position encoder, forward and backward.
+//
+// The llm.c tour ("Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 代码解剖)
+// names encoder_forward first and encoder_backward among the backward layers: the forward adds
+// the token row of wte and the position row of wpe; the backward adds the output gradient of each
+// position into the wte row of its token and the wpe row of its position.
+//
+// The wte scatter is made deterministic without atomics: the (token, position) pairs are sorted
+// once (bitonic sort of unique 31-bit keys in LDS), every run of equal tokens is then summed in
+// position order. Runs are cut into fixed 32-entry chunks; a run that crosses a chunk boundary
+// leaves per-chunk pieces that its first chunk adds up in chunk order.
+#include "common.h"
+#include "kernels.h"
+
+namespace g2 {
+
+template <typename T>
+__global__ __launch_bounds__(256) void encoder_fwd_kernel(int BT, int T_, int C, int V, const int32_t* __restrict__ tok,
+                                                          const T* __restrict__ wte, const T* __restrict__ wpe,
+                                                          T* __restrict__ out, int* err) {
+  constexpr int VEC = Elt<T>::VEC;
+  const int nv = C / VEC;
+  const size_t total = (size_t)BT * nv;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    const int row = (int)(i / nv);
+    const int cv = (int)(i % nv);
+    int t = tok[row];
+    if (t < 0 || t >= V) {
+      if (cv == 0) atomicOr(err, 1);
+      t = 0;
+    }
+    V16<T> a, b;
+    a.load(wte + (size_t)t * C + cv * VEC);
+    b.load(wpe + (size_t)(row % T_) * C + cv * VEC);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) a.v[e] += b.v[e];
+    a.store(out + (size_t)row * C + cv * VEC);
+  }
+}
+
+hipError_t launch_encoder_fwd(DType dt, int B, int T, int C, int V, const int32_t* tok, const void* wte,
+                              const void* wpe, void* out, int* err, hipStream_t s) {
+  const int BT = B * T;
+  if (BT <= 0) return hipSuccess;
+  const int vec = dt == DT_BF16 ? 8 : 4;
+  const int blocks = std::min(cdiv((long)BT * (C / vec), 256), 8192);
+  if (dt == DT_BF16)
+    encoder_fwd_kernel<bf16><<<blocks, 256, 0, s>>>(BT, T, C, V, tok, reinterpret_cast<const bf16*>(wte),
+                                                   reinterpret_cast<const bf16*>(wpe), reinterpret_cast<bf16*>(out), err);
+  else
+    encoder_fwd_kernel<float><<<blocks, 256, 0, s>>>(BT, T, C, V, tok, reinterpret_cast<const float*>(wte),
+                                                    reinterpret_cast<const float*>(wpe), reinterpret_cast<float*>(out), err);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ sort of (token, position)
+constexpr int POS_BITS = 15;  // BT <= 32768
+constexpr uint32_t POS_MASK = (1u << POS_BITS) - 1u;
+__device__ __forceinline__ int key_tok(uint32_t k) { return (int)(k >> POS_BITS); }
+__device__ __forceinline__ int key_pos(uint32_t k) { return (int)(k & POS_MASK); }
+
+__global__ __launch_bounds__(1024) void encoder_sort_kernel(int BT, int n2, int V, const int32_t* __restrict__ tok,
+                                                            uint32_t* __restrict__ keys) {
+  extern __shared__ uint32_t sk[];
+  for (int i = threadIdx.x; i < n2; i += 1024) {
+    uint32_t k = 0xffffffffu;
+    if (i < BT) {
+      int t = tok[i];
+      t = (t < 0 || t >= V) ? 0 : t;  // out-of-range ids were reported by the forward
+      k = ((uint32_t)t << POS_BITS) | (uint32_t)i;
+    }
+    sk[i] = k;
+  }
+  __syncthreads();
+  const int npairs = n2 >> 1;
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int pr = threadIdx.x; pr < npairs; pr += 1024) {
+        const int i = 2 * j * (pr / j) + (pr % j);
+        const int l = i + j;
+        const uint32_t a = sk[i], b = sk[l];
+        const bool up = (i & k) == 0;
+        if ((a > b) == up) {
+          sk[i] = b;
+          sk[l] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < BT; i += 1024) keys[i] = sk[i];
+}
+
+hipError_t launch_encoder_sort(int BT, int V, const int32_t* tok, uint32_t* keys, hipStream_t s) {
+  if (BT <= 0) return hipSuccess;
+  if (BT > (1 << POS_BITS) || V > (1 << (32 - POS_BITS - 1))) return hipErrorInvalidValue;
+  int n2 = 1;
+  while (n2 < BT) n2 <<= 1;
+  n2 = std::max(n2, 2);
+  if ((size_t)n2 * 4 > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&encoder_sort_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, n2 * 4);
+    if (e != hipSuccess) return e;
+  }
+  encoder_sort_kernel<<<1, 1024, (size_t)n2 * 4, s>>>(BT, n2, V, tok, keys);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ backward
+constexpr int CH = 32;  // sorted entries per chunk
+
+template <typename T>
+__global__ __launch_bounds__(256) void wpe_bwd_kernel(int B, int T_, int maxT, int C, const T* __restrict__ dout,
+                                                      float* __restrict__ dwpe, int accumulate) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // over maxT*C; rows t >= T get no gradient
+  if (i >= maxT * C) return;
+  const int t = i / C, c = i % C;
+  float s = 0.f;
+  if (t < T_)
+    for (int b = 0; b < B; ++b) s += ld1(dout, ((size_t)b * T_ + t) * C + c);
+  dwpe[i] = accumulate ? dwpe[i] + s : s;
+}
+
+struct ChunkInfo {
+  int start, end;
+  bool head_cont, tail_cont, single;
+};
+__device__ __forceinline__ ChunkInfo chunk_info(const uint32_t* keys, int BT, int ch) {
+  ChunkInfo c;
+  c.start = ch * CH;
+  c.end = min(BT, c.start + CH);
+  c.head_cont = ch > 0 && key_tok(keys[c.start]) == key_tok(keys[c.start - 1]);
+  c.tail_cont = c.end < BT && key_tok(keys[c.end - 1]) == key_tok(keys[c.end]);
+  c.single = key_tok(keys[c.start]) == key_tok(keys[c.end - 1]);
+  return c;
+}
+
+// grid: (nchunks, cdiv(C/VEC, 64)), block 64: one 16-byte column vector per thread
+template <typename T>
+__global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32_t* __restrict__ keys,
+                                                     const T* __restrict__ dout, float* __restrict__ dwte,
+                                                     float* __restrict__ part_head, float* __restrict__ part_tail) {
+  constexpr int VEC = Elt<T>::VEC;
+  const int cv = blockIdx.y * 64 + threadIdx.x;
+  if (cv * VEC >= C) return;
+  const int ch = blockIdx.x;
+  const ChunkInfo ci = chunk_info(keys, BT, ch);
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  int cur = key_tok(keys[ci.start]);
+  bool first = true;
+  auto flush = [&](int v, bool last) {
+    float* dst;
+    bool add = false;
+    if (first && ci.head_cont) dst = part_head + (size_t)ch * C;
+    else if (last && ci.tail_cont) dst = part_tail + (size_t)ch * C;
+    else {
+      dst = dwte + (size_t)v * C;
+      add = true;
+    }
+    dst += cv * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dst[e] = add ? dst[e] + acc[e] : acc[e];
+  };
+  for (int i = ci.start; i < ci.end; ++i) {
+    const uint32_t k = keys[i];
+    const int v = key_tok(k);
+    if (v != cur) {
+      flush(cur, false);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+      cur = v;
+      first = false;
+    }
+    V16<T> d;
+    d.load(dout + (size_t)key_pos(k) * C + cv * VEC);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += d.v[e];
+  }
+  flush(cur, true);
+}
+
+// Runs that cross chunk boundaries: the chunk where the run starts adds its pieces in order.
+__global__ __launch_bounds__(256) void wte_bwd_fixup(int BT, int C, int nch, const uint32_t* __restrict__ keys,
+                                                     float* __restrict__ dwte, const float* __restrict__ part_head,
+                                                     const float* __restrict__ part_tail) {
+  const int ch = blockIdx.x;
+  const ChunkInfo ci = chunk_info(keys, BT, ch);
+  if (!ci.tail_cont || (ci.single && ci.head_cont)) return;
+  const int v = key_tok(keys[ci.end - 1]);
+  for (int c = threadIdx.x; c < C; c += 256) {
+    float s = part_tail[(size_t)ch * C + c];
+    for (int n = ch + 1; n < nch; ++n) {
+      s += part_head[(size_t)n * C + c];
+      const ChunkInfo cn = chunk_info(keys, BT, n);
+      if (!(cn.single && cn.tail_cont)) break;
+    }
+    dwte[(size_t)v * C + c] += s;
+  }
+}
+
+size_t encoder_bwd_partial_floats(int BT, int C) { return (size_t)2 * cdiv(BT, CH) * C; }
+
+hipError_t launch_encoder_bwd(DType dt, int B, int T, int maxT, int C, const uint32_t* keys, const void* dout, float* dwte,
+                              float* dwpe, int accumulate_wpe, float* partial, size_t partial_floats,
+                              hipStream_t s) {
+  const int BT = B * T;
+  if (BT <= 0) return hipSuccess;
+  const int nch = cdiv(BT, CH);
+  if (encoder_bwd_partial_floats(BT, C) > partial_floats) return hipErrorInvalidValue;
+  float* ph = partial;
+  float* pt = partial + (size_t)nch * C;
+  const int vec = dt == DT_BF16 ? 8 : 4;
+  dim3 g1(nch, cdiv(C / vec, 64));
+  if (dt == DT_BF16) {
+    auto D = reinterpret_cast<const bf16*>(dout);
+    wpe_bwd_kernel<bf16><<<cdiv((long)maxT * C, 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
+    wte_bwd_chunks<bf16><<<g1, 64, 0, s>>>(BT, C, keys, D, dwte, ph, pt);
+  } else {
+    auto D = reinterpret_cast<const float*>(dout);
+    wpe_bwd_kernel<float><<<cdiv((long)maxT * C, 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
+    wte_bwd_chunks<float><<<g1, 64, 0, s>>>(BT, C, keys, D, dwte, ph, pt);
+  }
+  wte_bwd_fixup<<<nch, 256, 0, s>>>(BT, C, nch, keys, dwte, ph, pt);
+  return hipGetLastError();
+}
+
+}  // namespace g2

@@ -1,0 +1,114 @@
+// Internal launchers of the gfx950 kernels (host-callable; enqueue on `stream`).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace g2 {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// GEMM  C[M,N] = sum_k A(m,k) * B(n,k)
+//   A(m,k) = A[m*lda + k] when a_kc (K-contiguous) else A[k*lda + m]
+//   B(n,k) = B[n*ldb + k] when b_kc (K-contiguous) else B[k*ldb + n]
+enum Epi {
+  EPI_BIAS = 0,      // C(T) = acc + bias
+  EPI_GELU = 1,      // C(T) = pre = acc + bias ; C2(T) = gelu(pre)
+  EPI_RESID = 2,     // C(T) = aux + acc + bias        (residual add)
+  EPI_GELU_BWD = 3,  // C(T) = acc * gelu'(aux)
+  EPI_F32 = 4,       // C(f32) = acc  (or += acc when accumulate)
+};
+
+struct GemmArgs {
+  int M, N, K;
+  const void* A;
+  long lda;
+  const void* B;
+  long ldb;
+  void* C;
+  long ldc;
+  const void* bias;  // [N] in the compute dtype, or null
+  const void* aux;   // residual / pre-activation input (compute dtype)
+  long ldaux;
+  void* C2;          // second output (EPI_GELU), same ldc
+  int accumulate;    // EPI_F32 only
+};
+
+// split-K: for EPI_F32 only; `scratch` must hold splits*M*N floats (nullptr => no split).
+hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& a, float* scratch,
+                       size_t scratch_floats, hipStream_t s);
+// Choose the number of K splits for an EPI_F32 GEMM (1 = none).
+int gemm_splits(int M, int N, int K, size_t scratch_floats);
+
+// db[n] (+)= sum_m dY[m*ld + n]; deterministic, two stages through `partial` (rows_split*N floats)
+hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float* db, int accumulate,
+                         float* partial, size_t partial_floats, hipStream_t s);
+
+// LayerNorm
+hipError_t launch_layernorm_fwd(DType dt, int rows, int C, const void* x, const void* w, const void* b,
+                                void* y, float* mean, float* rstd, hipStream_t s);
+// dres[row] += dx (add = 1) or = dx (add = 0); dw/db (+)= column sums (two-stage, deterministic)
+hipError_t launch_layernorm_bwd(DType dt, int rows, int C, const void* dy, const void* x, const void* w,
+                                const float* mean, const float* rstd, void* dres, int add, float* dw, float* db,
+                                int accumulate, float* partial, size_t partial_floats, hipStream_t s);
+size_t layernorm_bwd_partial_floats(int rows, int C);
+
+// Encoder
+hipError_t launch_encoder_fwd(DType dt, int B, int T, int C, int V, const int32_t* tok, const void* wte,
+                              const void* wpe, void* out, int* err, hipStream_t s);
+// Sort (token, position) keys for the deterministic embedding-gradient scatter; needs BT <= 32768.
+hipError_t launch_encoder_sort(int BT, int V, const int32_t* tok, uint32_t* keys, hipStream_t s);
+hipError_t launch_encoder_bwd(DType dt, int B, int T, int maxT, int C, const uint32_t* sorted_keys, const void* dout,
+                              float* dwte, float* dwpe, int accumulate_wpe, float* partial,
+                              size_t partial_floats, hipStream_t s);
+size_t encoder_bwd_partial_floats(int BT, int C);
+
+// Attention (causal). qkv [B,T,3C], out [B,T,C], lse [B,H,T] (natural log).
+hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const void* qkv, void* out,
+                                float* lse, hipStream_t s);
+// dqkv [B,T,3C] is fully written. `dvec` holds B*H*T floats of scratch.
+hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
+                                const void* dout, const float* lse, void* dqkv, float* dvec,
+                                hipStream_t s);
+
+// Softmax cross-entropy over the first V columns of each row (row stride ld).
+// targets < 0 are ignored. When dloss != nullptr the logits are overwritten by
+// (softmax - onehot) * (*dloss) (0 in padded columns and ignored rows).
+// losses[row] = lse - logit[target] (0 when ignored).
+hipError_t launch_count_targets(const int32_t* targets, int rows, int V, int accum, float* dloss, int* nvalid,
+                                int* err, hipStream_t s);
+hipError_t launch_cross_entropy(DType dt, int rows, int V, int ld, void* logits, const int32_t* targets,
+                                const float* dloss, float* losses, hipStream_t s);
+hipError_t launch_loss_mean(const float* losses, int rows, const int* nvalid, float* out, hipStream_t s);
+
+// Deterministic sum of squares: per-block partials (double), fixed grid.
+hipError_t launch_sumsq_partial(const float* x, size_t n, double* partial, int nparts, hipStream_t s);
+
+// Optimizer / init work items: contiguous runs of the flat parameter vector.
+struct WorkItem {
+  uint64_t off;      // first element
+  uint32_t len;      // elements (<= ITEM_LEN)
+  uint32_t kind;     // 0: 1-D, no decay, init const ; 1: 2-D, decay, init normal
+  uint64_t normal0;  // index of the first element in the normal stream (kind 1)
+  float init_val;    // constant init (kind 0)
+  float pad_;
+};
+constexpr uint32_t ITEM_LEN = 8192;
+
+struct AdamArgs {
+  float lr, b1, b2, eps, wd;
+  float bc1, bc2;    // 1/(1-b1^t), 1/(1-b2^t)
+  float clip;        // <= 0: off
+};
+// norm: partials -> norm2 (double) ; scale = clip / ||g|| when above the clip
+hipError_t launch_grad_norm_finish(const double* partial, int nparts, double* norm2, float* scale, float clip,
+                                   hipStream_t s);
+hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float* g, float* m, float* v,
+                        uint16_t* shadow, const float* scale, const double* norm2, AdamArgs a,
+                        hipStream_t s);
+hipError_t launch_init_params(const WorkItem* items, int nitems, float* p, uint64_t seed, double std_,
+                              hipStream_t s);
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
+
+}  // namespace g2

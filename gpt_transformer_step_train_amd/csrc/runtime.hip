@@ -1,0 +1,660 @@
+// Host runtime behind the C ABI of include/gpt2.h and include/gpt2_ops.h.
+//
+// Owns no device memory: the caller's workspace is carved once at gpt2_init (the GPT-2
+// reproduction post, "Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 代码, notes that
+// all GPU memory is allocated once at start-up so the footprint never changes). Enqueues the
+// forward (encoder -> L x [LN, QKV, attention, proj + residual, LN, fc + GELU, proj + residual]
+// -> final LN -> tied classifier -> fused cross-entropy) and the backward in the reverse order
+// the llm.c tour describes ("Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section
+// 代码解剖), then the single-launch AdamW update.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "../../include/gpt2_ops.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace g2;
+
+namespace {
+
+constexpr size_t NONE = ~(size_t)0;
+constexpr int NORM_PARTS = 1024;
+
+struct LayerOff {
+  size_t ln1w, ln1b, qkvw, qkvb, attprojw, attprojb, ln2w, ln2b, fcw, fcb, fcprojw, fcprojb;
+};
+struct LayerAct {
+  char *ln1, *qkv, *atty, *res1, *ln2, *fch, *fchg, *res2;
+  float *ln1_mean, *ln1_rstd, *ln2_mean, *ln2_rstd, *lse;
+};
+
+struct Model {
+  bool ready = false;
+  gpt2_config cfg{};
+  DType dt = DT_F32;
+  size_t es = 4;  // bytes per activation element
+  int L = 0, H = 0, C = 0, V = 0, Vp = 0, maxT = 0, B = 0, T = 0, BT = 0, ldl = 0;
+  size_t N = 0;
+  size_t o_wte = 0, o_wpe = 0, o_lnfw = 0, o_lnfb = NONE;
+  std::vector<LayerOff> lo;
+  std::vector<WorkItem> items_host;
+
+  // device pointers inside the workspace
+  float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
+  uint16_t* shadow = nullptr;
+  WorkItem* items = nullptr;
+  char* encoded = nullptr;
+  std::vector<LayerAct> la;
+  char* lnf = nullptr;
+  float *lnf_mean = nullptr, *lnf_rstd = nullptr;
+  char* logits = nullptr;
+  float* losses = nullptr;
+  char *dres = nullptr, *dbuf1 = nullptr, *dbuf2 = nullptr;
+  float* dvec = nullptr;
+  uint32_t* keys = nullptr;
+  float* scratch = nullptr;
+  size_t scratch_floats = 0;
+  double* norm_partial = nullptr;
+  double* norm2 = nullptr;
+  float* clip_scale = nullptr;
+  float* loss_dev = nullptr;
+  float* dloss_dev = nullptr;
+  int* nvalid_dev = nullptr;
+  int* err_dev = nullptr;
+
+  // host state
+  float* pinned = nullptr;  // [0] loss, [1] error word (as int)
+  int micro = 0;            // backward passes since the last update
+  bool fwd_targets = false; // last forward had targets and its backward has not run yet
+  bool fwd_logits = false;  // last forward had no targets: logits are readable
+  hipStream_t stream = nullptr;
+};
+
+Model g;
+int g_status = GPT2_OK;
+std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  g_status = code;
+  return code;
+}
+int ok() {
+  g_status = GPT2_OK;
+  return GPT2_OK;
+}
+#define HIPCHK(x)                                                                      \
+  do {                                                                                 \
+    hipError_t e_ = (x);                                                               \
+    if (e_ != hipSuccess) return fail(GPT2_EHIP, "%s: %s", #x, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------------ configuration + layout
+const char* check_config(const gpt2_config* c) {
+  if (!c) return "null config";
+  if (c->n_layer < 1 || c->n_head < 1 || c->n_embd < 8) return "n_layer, n_head >= 1 and n_embd >= 8 required";
+  if (c->n_embd % c->n_head) return "n_embd must be a multiple of n_head";
+  if (c->n_embd % 8) return "n_embd must be a multiple of 8";
+  if (c->vocab < 1 || c->padded_vocab < c->vocab || c->padded_vocab > 65536) return "need 1 <= vocab <= padded_vocab <= 65536";
+  if (c->max_seq < 1 || c->seq < 1 || c->seq > c->max_seq) return "need 1 <= seq <= max_seq";
+  if (c->batch < 1 || (long)c->batch * c->seq > 32768) return "need batch >= 1 and batch*seq <= 32768";
+  if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16) return "precision must be GPT2_FP32 or GPT2_BF16";
+  const int hs = c->n_embd / c->n_head;
+  if (c->precision == GPT2_BF16 && hs != 64) return "GPT2_BF16 needs head size 64";
+  if (c->precision == GPT2_FP32 && hs != 4 && hs != 8 && hs != 16 && hs != 32 && hs != 64)
+    return "GPT2_FP32 needs head size in {4, 8, 16, 32, 64}";
+  if (c->n_embd > 2048) return "n_embd must be <= 2048";
+  if (c->grad_accum < 1) return "grad_accum must be >= 1";
+  if (c->linear_bias != 0 && c->linear_bias != 1) return "linear_bias must be 0 or 1";
+  if (c->ln_bias != 0 && c->ln_bias != 1) return "ln_bias must be 0 or 1";
+  return nullptr;
+}
+
+// Walk the layout; returns the number of parameters. Fills offsets when m != nullptr.
+size_t layout(const gpt2_config* c, Model* m) {
+  const size_t C = c->n_embd;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off += n;
+    return o;
+  };
+  size_t wte = take((size_t)c->padded_vocab * C), wpe = take((size_t)c->max_seq * C);
+  std::vector<LayerOff> lo(c->n_layer);
+  for (int l = 0; l < c->n_layer; ++l) {
+    LayerOff& L = lo[l];
+    L.ln1w = take(C);
+    L.ln1b = c->ln_bias ? take(C) : NONE;
+    L.qkvw = take(3 * C * C);
+    L.qkvb = c->linear_bias ? take(3 * C) : NONE;
+    L.attprojw = take(C * C);
+    L.attprojb = c->linear_bias ? take(C) : NONE;
+    L.ln2w = take(C);
+    L.ln2b = c->ln_bias ? take(C) : NONE;
+    L.fcw = take(4 * C * C);
+    L.fcb = c->linear_bias ? take(4 * C) : NONE;
+    L.fcprojw = take(4 * C * C);
+    L.fcprojb = c->linear_bias ? take(C) : NONE;
+  }
+  size_t lnfw = take(C), lnfb = c->ln_bias ? take(C) : NONE;
+  if (m) {
+    m->o_wte = wte;
+    m->o_wpe = wpe;
+    m->o_lnfw = lnfw;
+    m->o_lnfb = lnfb;
+    m->lo = lo;
+  }
+  return off;
+}
+
+// Work items: tensors cut into runs of <= ITEM_LEN elements; 2-D tensors draw normals.
+std::vector<WorkItem> make_items(const gpt2_config* c) {
+  const size_t C = c->n_embd;
+  std::vector<std::pair<size_t, int>> tensors;  // (size, is2d) in layout order
+  tensors.push_back({(size_t)c->padded_vocab * C, 1});
+  tensors.push_back({(size_t)c->max_seq * C, 1});
+  for (int l = 0; l < c->n_layer; ++l) {
+    tensors.push_back({C, 0});
+    if (c->ln_bias) tensors.push_back({C, 2});
+    tensors.push_back({3 * C * C, 1});
+    if (c->linear_bias) tensors.push_back({3 * C, 2});
+    tensors.push_back({C * C, 1});
+    if (c->linear_bias) tensors.push_back({C, 2});
+    tensors.push_back({C, 0});
+    if (c->ln_bias) tensors.push_back({C, 2});
+    tensors.push_back({4 * C * C, 1});
+    if (c->linear_bias) tensors.push_back({4 * C, 2});
+    tensors.push_back({4 * C * C, 1});
+    if (c->linear_bias) tensors.push_back({C, 2});
+  }
+  tensors.push_back({C, 0});
+  if (c->ln_bias) tensors.push_back({C, 2});
+  std::vector<WorkItem> items;
+  size_t off = 0, normal = 0;
+  for (auto& t : tensors) {
+    for (size_t s = 0; s < t.first; s += ITEM_LEN) {
+      WorkItem it{};
+      it.off = off + s;
+      it.len = (uint32_t)std::min<size_t>(ITEM_LEN, t.first - s);
+      it.kind = t.second == 1 ? 1u : 0u;
+      it.normal0 = normal + s;
+      it.init_val = t.second == 0 ? 1.0f : 0.0f;  // LN weights 1, biases 0
+      items.push_back(it);
+    }
+    off += t.first;
+    if (t.second == 1) normal += t.first;
+  }
+  return items;
+}
+
+// Carve the arena. With base == nullptr only the size is computed.
+size_t plan(const gpt2_config* c, Model* m, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    off = round_up(off, 256);
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  const size_t N = layout(c, nullptr);
+  const size_t es = c->precision == GPT2_BF16 ? 2 : 4;
+  const size_t B = c->batch, T = c->seq, BT = B * T, C = c->n_embd, H = c->n_head, L = c->n_layer;
+  const size_t ldl = round_up(c->padded_vocab, 8);
+  const size_t nitems = make_items(c).size();
+
+  Model tmp;
+  Model* M = m ? m : &tmp;
+  M->params = (float*)take(N * 4);
+  M->grads = (float*)take(N * 4);
+  M->m = (float*)take(N * 4);
+  M->v = (float*)take(N * 4);
+  M->shadow = c->precision == GPT2_BF16 ? (uint16_t*)take(N * 2) : nullptr;
+  M->items = (WorkItem*)take(nitems * sizeof(WorkItem));
+  M->encoded = take(BT * C * es);
+  M->la.resize(L);
+  for (size_t l = 0; l < L; ++l) {
+    LayerAct& a = M->la[l];
+    a.ln1 = take(BT * C * es);
+    a.ln1_mean = (float*)take(BT * 4);
+    a.ln1_rstd = (float*)take(BT * 4);
+    a.qkv = take(BT * 3 * C * es);
+    a.atty = take(BT * C * es);
+    a.lse = (float*)take(B * H * T * 4);
+    a.res1 = take(BT * C * es);
+    a.ln2 = take(BT * C * es);
+    a.ln2_mean = (float*)take(BT * 4);
+    a.ln2_rstd = (float*)take(BT * 4);
+    a.fch = take(BT * 4 * C * es);
+    a.fchg = take(BT * 4 * C * es);
+    a.res2 = take(BT * C * es);
+  }
+  M->lnf = take(BT * C * es);
+  M->lnf_mean = (float*)take(BT * 4);
+  M->lnf_rstd = (float*)take(BT * 4);
+  M->logits = take(BT * ldl * es);
+  M->losses = (float*)take(BT * 4);
+  M->dres = take(BT * C * es);
+  M->dbuf1 = take(BT * 4 * C * es);
+  M->dbuf2 = take(BT * C * es);
+  M->dvec = (float*)take(B * H * T * 4);
+  M->keys = (uint32_t*)take(BT * 4);
+  size_t sf = std::max<size_t>(8 * 4 * C * C, (size_t)ldl * C * 2);
+  sf = std::max(sf, layernorm_bwd_partial_floats((int)BT, (int)C));
+  sf = std::max(sf, encoder_bwd_partial_floats((int)BT, (int)C));
+  sf = std::max<size_t>(sf, (size_t)256 * 4 * C);  // column-sum partials
+  M->scratch_floats = sf;
+  M->scratch = (float*)take(sf * 4);
+  M->norm_partial = (double*)take(NORM_PARTS * 8);
+  M->norm2 = (double*)take(8);
+  M->clip_scale = (float*)take(4);
+  M->loss_dev = (float*)take(4);
+  M->dloss_dev = (float*)take(4);
+  M->nvalid_dev = (int*)take(4);
+  M->err_dev = (int*)take(4);
+  return round_up(off, 256);
+}
+
+
+// weight pointer in the compute dtype (bf16 shadow or fp32 master)
+const void* W(size_t off) {
+  if (off == NONE) return nullptr;
+  if (g.dt == DT_BF16) return g.shadow + off;
+  return g.params + off;
+}
+float* G(size_t off) { return off == NONE ? nullptr : g.grads + off; }
+
+int gemm(bool akc, bool bkc, Epi epi, int M, int N, int K, const void* A, long lda, const void* Bp, long ldb,
+         void* Cp, long ldc, const void* bias = nullptr, const void* aux = nullptr, long ldaux = 0,
+         void* C2 = nullptr, int accumulate = 0, bool split = false) {
+  GemmArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = A;
+  a.lda = lda;
+  a.B = Bp;
+  a.ldb = ldb;
+  a.C = Cp;
+  a.ldc = ldc;
+  a.bias = bias;
+  a.aux = aux;
+  a.ldaux = ldaux;
+  a.C2 = C2;
+  a.accumulate = accumulate;
+  HIPCHK(launch_gemm(g.dt, akc, bkc, epi, a, split ? g.scratch : nullptr, split ? g.scratch_floats : 0, g.stream));
+  return GPT2_OK;
+}
+
+#define RUN(x)                   \
+  do {                           \
+    int r_ = (x);                \
+    if (r_ != GPT2_OK) return r_; \
+  } while (0)
+
+__global__ void set_scalars_kernel(int* err) { *err = 0; }
+
+int forward_impl(const int32_t* tokens, const int32_t* targets) {
+  const int BT = g.BT, C = g.C, L = g.L;
+  const size_t es = g.es;
+  hipStream_t s = g.stream;
+  set_scalars_kernel<<<1, 1, 0, s>>>(g.err_dev);
+  HIPCHK(launch_encoder_fwd(g.dt, g.B, g.T, C, g.V, tokens, W(g.o_wte), W(g.o_wpe), g.encoded, g.err_dev, s));
+  if (targets) HIPCHK(launch_encoder_sort(BT, g.V, tokens, g.keys, s));
+  const char* x = g.encoded;
+  for (int l = 0; l < L; ++l) {
+    const LayerOff& o = g.lo[l];
+    LayerAct& a = g.la[l];
+    HIPCHK(launch_layernorm_fwd(g.dt, BT, C, x, W(o.ln1w), W(o.ln1b), a.ln1, a.ln1_mean, a.ln1_rstd, s));
+    RUN(gemm(true, true, EPI_BIAS, BT, 3 * C, C, a.ln1, C, W(o.qkvw), C, a.qkv, 3 * C, W(o.qkvb)));
+    HIPCHK(launch_attention_fwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, a.lse, s));
+    RUN(gemm(true, true, EPI_RESID, BT, C, C, a.atty, C, W(o.attprojw), C, a.res1, C, W(o.attprojb), x, C));
+    HIPCHK(launch_layernorm_fwd(g.dt, BT, C, a.res1, W(o.ln2w), W(o.ln2b), a.ln2, a.ln2_mean, a.ln2_rstd, s));
+    RUN(gemm(true, true, EPI_GELU, BT, 4 * C, C, a.ln2, C, W(o.fcw), C, a.fch, 4 * C, W(o.fcb), nullptr, 0, a.fchg));
+    RUN(gemm(true, true, EPI_RESID, BT, C, 4 * C, a.fchg, 4 * C, W(o.fcprojw), 4 * C, a.res2, C, W(o.fcprojb),
+             a.res1, C));
+    x = a.res2;
+  }
+  HIPCHK(launch_layernorm_fwd(g.dt, BT, C, x, W(g.o_lnfw), W(g.o_lnfb), g.lnf, g.lnf_mean, g.lnf_rstd, s));
+  RUN(gemm(true, true, EPI_BIAS, BT, g.Vp, C, g.lnf, C, W(g.o_wte), C, g.logits, g.ldl));
+  if (targets) {
+    HIPCHK(launch_count_targets(targets, BT, g.V, g.cfg.grad_accum, g.dloss_dev, g.nvalid_dev, g.err_dev, s));
+    HIPCHK(launch_cross_entropy(g.dt, BT, g.V, g.ldl, g.logits, targets, g.dloss_dev, g.losses, s));
+    HIPCHK(launch_loss_mean(g.losses, BT, g.nvalid_dev, g.loss_dev, s));
+    HIPCHK(hipMemcpyAsync(g.pinned, g.loss_dev, 4, hipMemcpyDeviceToHost, s));
+  }
+  HIPCHK(hipMemcpyAsync(g.pinned + 1, g.err_dev, 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  (void)es;
+  return GPT2_OK;
+}
+
+int backward_impl() {
+  const int BT = g.BT, C = g.C, L = g.L;
+  const int acc = g.micro > 0 ? 1 : 0;
+  const bool lb = g.cfg.linear_bias != 0;
+  hipStream_t s = g.stream;
+  float* sc = g.scratch;
+  const size_t sf = g.scratch_floats;
+  // classifier (tied wte): dz = dlogits wte ; dwte (+)= dlogits^T z
+  RUN(gemm(true, false, EPI_BIAS, BT, C, g.Vp, g.logits, g.ldl, W(g.o_wte), C, g.dbuf2, C));
+  RUN(gemm(false, false, EPI_F32, g.Vp, C, BT, g.logits, g.ldl, g.lnf, C, G(g.o_wte), C, nullptr, nullptr, 0,
+           nullptr, acc, true));
+  const char* xlast = L > 0 ? g.la[L - 1].res2 : g.encoded;
+  HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xlast, W(g.o_lnfw), g.lnf_mean, g.lnf_rstd, g.dres, 0,
+                              G(g.o_lnfw), G(g.o_lnfb), acc, sc, sf, s));
+  for (int l = L - 1; l >= 0; --l) {
+    const LayerOff& o = g.lo[l];
+    LayerAct& a = g.la[l];
+    const char* xin = l > 0 ? g.la[l - 1].res2 : g.encoded;
+    // fcproj: res2 = res1 + gelu(fch) Wfcproj^T + b
+    RUN(gemm(true, false, EPI_GELU_BWD, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr,
+             a.fch, 4 * C));
+    RUN(gemm(false, false, EPI_F32, C, 4 * C, BT, g.dres, C, a.fchg, 4 * C, G(o.fcprojw), 4 * C, nullptr, nullptr,
+             0, nullptr, acc, true));
+    if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.fcprojb), acc, sc, sf, s));
+    // fc: fch = ln2 Wfc^T + b
+    RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
+    RUN(gemm(false, false, EPI_F32, 4 * C, C, BT, g.dbuf1, 4 * C, a.ln2, C, G(o.fcw), C, nullptr, nullptr, 0,
+             nullptr, acc, true));
+    if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 4 * C, BT, 4 * C, G(o.fcb), acc, sc, sf, s));
+    HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, a.res1, W(o.ln2w), a.ln2_mean, a.ln2_rstd, g.dres, 1,
+                                G(o.ln2w), G(o.ln2b), acc, sc, sf, s));
+    // attproj: res1 = xin + atty Wproj^T + b
+    RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
+    RUN(gemm(false, false, EPI_F32, C, C, BT, g.dres, C, a.atty, C, G(o.attprojw), C, nullptr, nullptr, 0, nullptr,
+             acc, true));
+    if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.attprojb), acc, sc, sf, s));
+    HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec, s));
+    // qkv = ln1 Wqkv^T + b
+    RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
+    RUN(gemm(false, false, EPI_F32, 3 * C, C, BT, g.dbuf1, 3 * C, a.ln1, C, G(o.qkvw), C, nullptr, nullptr, 0,
+             nullptr, acc, true));
+    if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
+    HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, g.dres, 1, G(o.ln1w),
+                                G(o.ln1b), acc, sc, sf, s));
+  }
+  HIPCHK(launch_encoder_bwd(g.dt, g.B, g.T, g.maxT, C, g.keys, g.dres, G(g.o_wte), G(g.o_wpe), acc, sc, sf, s));
+  return GPT2_OK;
+}
+
+int check_ready() {
+  if (!g.ready) return fail(GPT2_ESTATE, "gpt2_init has not succeeded");
+  return GPT2_OK;
+}
+
+}  // namespace
+
+// ===================================================================================== C ABI
+extern "C" {
+
+uint64_t gpt2_workspace_bytes(const gpt2_config* cfg) {
+  if (const char* e = check_config(cfg)) {
+    fail(GPT2_EINVAL, "%s", e);
+    return 0;
+  }
+  ok();
+  return plan(cfg, nullptr, nullptr);
+}
+
+void gpt2_free(void) {
+  if (g.pinned) (void)hipHostFree(g.pinned);
+  g = Model();
+}
+
+int gpt2_init(const gpt2_config* cfg, uint64_t seed) {
+  gpt2_free();
+  if (const char* e = check_config(cfg)) return fail(GPT2_EINVAL, "%s", e);
+  const size_t need = plan(cfg, nullptr, nullptr);
+  if (!cfg->workspace || cfg->workspace_bytes < need)
+    return fail(GPT2_ENOMEM, "workspace of %llu bytes < %llu needed", (unsigned long long)cfg->workspace_bytes,
+                (unsigned long long)need);
+  if (reinterpret_cast<uintptr_t>(cfg->workspace) % 256) return fail(GPT2_EINVAL, "workspace must be 256-byte aligned");
+  g.cfg = *cfg;
+  g.dt = cfg->precision == GPT2_BF16 ? DT_BF16 : DT_F32;
+  g.es = g.dt == DT_BF16 ? 2 : 4;
+  g.L = cfg->n_layer;
+  g.H = cfg->n_head;
+  g.C = cfg->n_embd;
+  g.V = cfg->vocab;
+  g.Vp = cfg->padded_vocab;
+  g.maxT = cfg->max_seq;
+  g.B = cfg->batch;
+  g.T = cfg->seq;
+  g.BT = g.B * g.T;
+  g.ldl = (int)round_up(g.Vp, 8);
+  g.N = layout(cfg, &g);
+  g.items_host = make_items(cfg);
+  plan(cfg, &g, reinterpret_cast<char*>(cfg->workspace));
+  g.stream = reinterpret_cast<hipStream_t>(cfg->stream);
+  HIPCHK(hipHostMalloc((void**)&g.pinned, 16, hipHostMallocDefault));
+  HIPCHK(hipMemcpyAsync(g.items, g.items_host.data(), g.items_host.size() * sizeof(WorkItem), hipMemcpyHostToDevice,
+                        g.stream));
+  HIPCHK(launch_init_params(g.items, (int)g.items_host.size(), g.params, seed, 0.02, g.stream));
+  HIPCHK(launch_fill_f32(g.m, g.N, 0.f, g.stream));
+  HIPCHK(launch_fill_f32(g.v, g.N, 0.f, g.stream));
+  HIPCHK(launch_fill_f32(g.grads, g.N, 0.f, g.stream));
+  if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
+  HIPCHK(hipStreamSynchronize(g.stream));
+  g.ready = true;
+  return ok();
+}
+
+float gpt2_forward(const int32_t* tokens, const int32_t* targets) {
+  if (check_ready() != GPT2_OK) return NAN;
+  if (!tokens) {
+    fail(GPT2_EINVAL, "tokens is NULL");
+    return NAN;
+  }
+  g.fwd_targets = false;
+  g.fwd_logits = false;
+  if (forward_impl(tokens, targets) != GPT2_OK) return NAN;
+  const int err = *reinterpret_cast<int*>(g.pinned + 1);
+  if (err) {
+    fail(GPT2_ERANGE, "%s", (err & 1) ? "token id outside [0, vocab)" : "target outside [-1, vocab)");
+    return NAN;
+  }
+  ok();
+  if (!targets) {
+    g.fwd_logits = true;
+    return NAN;
+  }
+  g.fwd_targets = true;
+  return g.pinned[0];
+}
+
+int gpt2_backward(void) {
+  RUN(check_ready());
+  if (!g.fwd_targets) return fail(GPT2_ESTATE, "gpt2_backward needs a preceding gpt2_forward with targets");
+  RUN(backward_impl());
+  g.fwd_targets = false;
+  g.micro++;
+  return ok();
+}
+
+int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t) {
+  RUN(check_ready());
+  if (t < 1) return fail(GPT2_EINVAL, "t must be >= 1");
+  if (g.micro == 0) return fail(GPT2_ESTATE, "gpt2_adamw_step needs at least one gpt2_backward since the last update");
+  hipStream_t s = g.stream;
+  HIPCHK(launch_sumsq_partial(g.grads, g.N, g.norm_partial, NORM_PARTS, s));
+  HIPCHK(launch_grad_norm_finish(g.norm_partial, NORM_PARTS, g.norm2, g.clip_scale, g.cfg.grad_clip, s));
+  AdamArgs a;
+  a.lr = lr;
+  a.b1 = b1;
+  a.b2 = b2;
+  a.eps = eps;
+  a.wd = wd;
+  a.bc1 = (float)(1.0 / (1.0 - pow((double)b1, (double)t)));
+  a.bc2 = (float)(1.0 / (1.0 - pow((double)b2, (double)t)));
+  a.clip = g.cfg.grad_clip;
+  HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale, g.norm2,
+                      a, s));
+  g.micro = 0;
+  return ok();
+}
+
+float gpt2_grad_norm(void) {
+  if (check_ready() != GPT2_OK) return NAN;
+  double n2 = 0;
+  hipError_t e = hipMemcpyAsync(&n2, g.norm2, 8, hipMemcpyDeviceToHost, g.stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(g.stream);
+  if (e != hipSuccess) {
+    fail(GPT2_EHIP, "gpt2_grad_norm: %s", hipGetErrorString(e));
+    return NAN;
+  }
+  ok();
+  return (float)sqrt(n2);
+}
+
+int gpt2_last_status(void) { return g_status; }
+const char* gpt2_last_error(void) { return g_err.c_str(); }
+uint64_t gpt2_num_params(void) { return g.ready ? g.N : 0; }
+
+static int copy_d2h(void* dst, const void* src, size_t bytes) {
+  HIPCHK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, g.stream));
+  HIPCHK(hipStreamSynchronize(g.stream));
+  return ok();
+}
+
+int gpt2_get_params(float* dst, uint64_t n) {
+  RUN(check_ready());
+  if (!dst || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
+  return copy_d2h(dst, g.params, n * 4);
+}
+
+int gpt2_set_params(const float* src, uint64_t n) {
+  RUN(check_ready());
+  if (!src || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
+  HIPCHK(hipMemcpyAsync(g.params, src, n * 4, hipMemcpyHostToDevice, g.stream));
+  if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
+  HIPCHK(hipStreamSynchronize(g.stream));
+  return ok();
+}
+
+int gpt2_get_grads(float* dst, uint64_t n) {
+  RUN(check_ready());
+  if (!dst || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
+  return copy_d2h(dst, g.grads, n * 4);
+}
+
+int gpt2_get_adam_state(float* m, float* v, uint64_t n) {
+  RUN(check_ready());
+  if (!m || !v || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
+  RUN(copy_d2h(m, g.m, n * 4));
+  return copy_d2h(v, g.v, n * 4);
+}
+
+int gpt2_get_logits(float* dst, uint64_t n) {
+  RUN(check_ready());
+  if (!g.fwd_logits) return fail(GPT2_ESTATE, "logits are kept only by a gpt2_forward with targets == NULL");
+  if (!dst || n != (uint64_t)g.BT * g.V) return fail(GPT2_EINVAL, "need n == B*T*vocab");
+  std::vector<char> raw((size_t)g.BT * g.ldl * g.es);
+  RUN(copy_d2h(raw.data(), g.logits, raw.size()));
+  for (size_t r = 0; r < (size_t)g.BT; ++r)
+    for (size_t c = 0; c < (size_t)g.V; ++c) {
+      const size_t i = r * g.ldl + c;
+      float f;
+      if (g.es == 2) {
+        const uint32_t u = (uint32_t)reinterpret_cast<const uint16_t*>(raw.data())[i] << 16;
+        memcpy(&f, &u, 4);
+      } else {
+        f = reinterpret_cast<const float*>(raw.data())[i];
+      }
+      dst[r * g.V + c] = f;
+    }
+  return ok();
+}
+
+// ===================================================================================== per-op ABI
+static DType to_dt(int dtype) { return dtype == GPT2_BF16 ? DT_BF16 : DT_F32; }
+static int op_ret(hipError_t e) {
+  if (e == hipErrorInvalidValue) return fail(GPT2_EINVAL, "unsupported shape or argument");
+  if (e != hipSuccess) return fail(GPT2_EHIP, "%s", hipGetErrorString(e));
+  return ok();
+}
+
+int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
+                int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias, const void* aux,
+                int64_t ldaux, void* C2, int accumulate, float* scratch, uint64_t scratch_floats, void* stream) {
+  if (epilogue < 0 || epilogue > 4 || M < 0 || N < 0 || K < 0) return fail(GPT2_EINVAL, "bad gemm arguments");
+  GemmArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = A;
+  a.lda = lda;
+  a.B = B;
+  a.ldb = ldb;
+  a.C = C;
+  a.ldc = ldc;
+  a.bias = bias;
+  a.aux = aux;
+  a.ldaux = ldaux;
+  a.C2 = C2;
+  a.accumulate = accumulate;
+  return op_ret(launch_gemm(to_dt(dtype), a_kcontig != 0, b_kcontig != 0, (Epi)epilogue, a, scratch, scratch_floats,
+                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,
+                             float* mean, float* rstd, void* stream) {
+  return op_ret(launch_layernorm_fwd(to_dt(dtype), rows, C, x, w, b, y, mean, rstd, reinterpret_cast<hipStream_t>(stream)));
+}
+
+uint64_t gpt2op_layernorm_backward_scratch(int rows, int C) { return layernorm_bwd_partial_floats(rows, C); }
+
+int gpt2op_layernorm_backward(int dtype, int rows, int C, const void* dy, const void* x, const void* w,
+                              const float* mean, const float* rstd, void* dres, float* dw, float* db, int accumulate,
+                              float* partial, void* stream) {
+  return op_ret(launch_layernorm_bwd(to_dt(dtype), rows, C, dy, x, w, mean, rstd, dres, 1, dw, db, accumulate, partial,
+                                     layernorm_bwd_partial_floats(rows, C), reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,
+                             void* stream) {
+  return op_ret(launch_attention_fwd(to_dt(dtype), B, T, H, hs, qkv, out, lse, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
+                              const void* dout, const float* lse, void* dqkv, float* dvec, void* stream) {
+  return op_ret(launch_attention_bwd(to_dt(dtype), B, T, H, hs, qkv, out, dout, lse, dqkv, dvec,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_cross_entropy(int dtype, int rows, int V, int ld, void* logits, const int32_t* targets, const float* dloss,
+                         float* losses, void* stream) {
+  return op_ret(launch_cross_entropy(to_dt(dtype), rows, V, ld, logits, targets, dloss, losses,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t* tok, const void* wte, const void* wpe,
+                           void* out, int* err, void* stream) {
+  return op_ret(launch_encoder_fwd(to_dt(dtype), B, T, C, V, tok, wte, wpe, out, err, reinterpret_cast<hipStream_t>(stream)));
+}
+
+uint64_t gpt2op_encoder_backward_scratch(int BT, int C) { return encoder_bwd_partial_floats(BT, C); }
+
+int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok, const void* dout,
+                            float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys, float* partial, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_encoder_sort(B * T, V, tok, keys, s);
+  if (e != hipSuccess) return op_ret(e);
+  return op_ret(launch_encoder_bwd(to_dt(dtype), B, T, max_seq, C, keys, dout, dwte, dwpe, accumulate_wpe, partial,
+                                   encoder_bwd_partial_floats(B * T, C), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Global gradient norm + clip scale, the single-launch AdamW update (which also refreshes the
+// bf16 parameter shadow), and the seeded parameter initialisation.
+//
+// Pages: the llm.c tour ("Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 性能对比)
+// contrasts one update kernel for all parameters with an optimizer that launches several; the
+// GPT-2 reproduction post ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 训练) shows
+// AdamW state m, v and an fp32 master copy next to bf16 parameters, and (section 参数指南, -c)
+// weight decay on 2-D tensors only.
+//
+// AdamW, decoupled decay on the pre-update value:
+//   g = s * grad;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2
+//   p = p - lr * ( (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd_i * p ),  wd_i = wd on 2-D tensors
+// s = clip / ||g|| when clipping is on and ||g|| > clip, else 1. If ||g|| is not finite the
+// update is skipped (p, m, v unchanged).
+// The parameter vector is cut into work items (<= 8192 elements, never straddling a tensor), so one
+// launch covers every tensor and each block knows its tensor's decay flag.
+#include "common.h"
+#include "kernels.h"
+
+namespace g2 {
+
+// ---------------------------------------------------------------- sum of squares (double)
+__global__ __launch_bounds__(256) void sumsq_partial_kernel(const float* __restrict__ x, size_t n,
+                                                            double* __restrict__ partial) {
+  __shared__ double sh[256];
+  double s = 0.0;
+  const size_t n4 = n / 4;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += stride) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(x)[i];
+    const double a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    s += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
+  }
+  for (size_t i = n4 * 4 + blockIdx.x * 256ull + threadIdx.x; i < n; i += stride) s += (double)x[i] * (double)x[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = sh[0];
+}
+
+hipError_t launch_sumsq_partial(const float* x, size_t n, double* partial, int nparts, hipStream_t s) {
+  sumsq_partial_kernel<<<nparts, 256, 0, s>>>(x, n, partial);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void norm_finish_kernel(const double* __restrict__ partial, int nparts,
+                                                          double* norm2, float* scale, float clip) {
+  __shared__ double sh[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += 256) s += partial[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double n2 = sh[0];
+    const double nrm = sqrt(n2);
+    *norm2 = n2;
+    *scale = (clip > 0.f && nrm > (double)clip) ? (float)((double)clip / nrm) : 1.0f;
+  }
+}
+
+hipError_t launch_grad_norm_finish(const double* partial, int nparts, double* norm2, float* scale, float clip,
+                                   hipStream_t s) {
+  norm_finish_kernel<<<1, 256, 0, s>>>(partial, nparts, norm2, scale, clip);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- AdamW
+constexpr int ADAM_T = 256;
+
+__global__ __launch_bounds__(ADAM_T) void adamw_kernel(const WorkItem* __restrict__ items, float* __restrict__ p,
+                                                       const float* __restrict__ g, float* __restrict__ m,
+                                                       float* __restrict__ v, uint16_t* __restrict__ shadow,
+                                                       const float* __restrict__ scale_p,
+                                                       const double* __restrict__ norm2_p, AdamArgs a) {
+  const double n2 = *norm2_p;
+  if (!(n2 <= 1.0e300)) return;  // non-finite norm: skip the update (NaN fails the compare)
+  const WorkItem it = items[blockIdx.x];
+  const float sc = *scale_p;
+  const float wd = it.kind == 1 ? a.wd : 0.f;
+  const size_t base = it.off;
+  for (int j = threadIdx.x * 4; j < (int)it.len; j += ADAM_T * 4) {
+    const size_t i = base + j;
+    if (j + 4 <= (int)it.len) {
+      f32x4 pv = *reinterpret_cast<const f32x4*>(p + i);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + i);
+      f32x4 mv = *reinterpret_cast<const f32x4*>(m + i);
+      f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float gg = gv[e] * sc;
+        mv[e] = a.b1 * mv[e] + (1.f - a.b1) * gg;
+        vv[e] = a.b2 * vv[e] + (1.f - a.b2) * gg * gg;
+        const float mh = mv[e] * a.bc1;
+        const float vh = vv[e] * a.bc2;
+        pv[e] = pv[e] - a.lr * (mh / (sqrtf(vh) + a.eps) + wd * pv[e]);
+      }
+      *reinterpret_cast<f32x4*>(p + i) = pv;
+      *reinterpret_cast<f32x4*>(m + i) = mv;
+      *reinterpret_cast<f32x4*>(v + i) = vv;
+      if (shadow) {
+        u32x2 sv = {pack2bf(pv[0], pv[1]), pack2bf(pv[2], pv[3])};
+        *reinterpret_cast<u32x2*>(shadow + i) = sv;
+      }
+    } else {
+      for (int e = 0; j + e < (int)it.len; ++e) {
+        const size_t k = i + e;
+        const float gg = g[k] * sc;
+        const float mm = a.b1 * m[k] + (1.f - a.b1) * gg;
+        const float vv2 = a.b2 * v[k] + (1.f - a.b2) * gg * gg;
+        m[k] = mm;
+        v[k] = vv2;
+        const float pp = p[k] - a.lr * ((mm * a.bc1) / (sqrtf(vv2 * a.bc2) + a.eps) + wd * p[k]);
+        p[k] = pp;
+        if (shadow) shadow[k] = f2bf(pp);
+      }
+    }
+  }
+}
+
+hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float* g, float* m, float* v,
+                        uint16_t* shadow, const float* scale, const double* norm2, AdamArgs a, hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  adamw_kernel<<<nitems, ADAM_T, 0, s>>>(items, p, g, m, v, shadow, scale, norm2, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- init
+// SplitMix64 (Steele, Lea & Flood 2014): output n of the stream seeded with s is
+// mix(s + (n+1) * 0x9E3779B97F4A7C15). Uniform in (0,1): ((x >> 11) + 0.5) * 2^-53.
+// Box-Muller (1958) on outputs (2p, 2p+1): normals 2p = r cos(2 pi u2), 2p+1 = r sin(2 pi u2),
+// r = sqrt(-2 ln u1), in double; parameter = float(std * z).
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ double u01(uint64_t x) { return ((double)(x >> 11) + 0.5) * 0x1.0p-53; }
+
+__global__ __launch_bounds__(256) void init_kernel(const WorkItem* __restrict__ items, float* __restrict__ p,
+                                                   uint64_t seed, double std_) {
+  const WorkItem it = items[blockIdx.x];
+  for (int j = threadIdx.x; j < (int)it.len; j += 256) {
+    float val;
+    if (it.kind == 1) {
+      const uint64_t idx = it.normal0 + j;
+      const uint64_t pr = idx >> 1;
+      const double u1 = u01(splitmix64(seed, 2 * pr));
+      const double u2 = u01(splitmix64(seed, 2 * pr + 1));
+      const double r = sqrt(-2.0 * log(u1));
+      const double ang = (2.0 * M_PI) * u2;
+      const double z = (idx & 1) ? r * sin(ang) : r * cos(ang);
+      val = (float)(std_ * z);
+    } else {
+      val = it.init_val;
+    }
+    p[it.off + j] = val;
+  }
+}
+
+hipError_t launch_init_params(const WorkItem* items, int nitems, float* p, uint64_t seed, double std_,
+                              hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  init_kernel<<<nitems, 256, 0, s>>>(items, p, seed, std_);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                      size_t n) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = f2bf(src[i]);
+}
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  to_bf16_kernel<<<(int)std::min<size_t>(8192, (n + 255) / 256), 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, size_t n, float v) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
+}
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
+  if (!n) return hipSuccess;
+  fill_kernel<<<(int)std::min<size_t>(8192, (n + 255) / 256), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace g2

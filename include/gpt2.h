@@ -1,0 +1,108 @@
+/*
+ * gpt2.h -- C ABI of the GPT-2 training-step library for AMD MI355X (gfx950).
+ *
+ * One training step of a decoder-only GPT-2 on one GPU: forward, backward, AdamW update.
+ * The model and what each call computes follow the pages on llm.c:
+ *   - layer order (encoder, LayerNorm, QKV matmul, attention, ..., classifier) and a hand-ordered
+ *     backward starting from the logits: "Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现",
+ *     section 代码解剖 (code walk-through);
+ *   - attention softmax(Q K^T / sqrt(d_k)) V: the LLM primer page ("从Andrej Karpathy
+ *     《深入了解ChatGPT之类的大语言模型》入门LLMs"), attention formula; causal for GPT-2;
+ *   - a model built from scratch at a given depth, memory allocated once at start-up, bitwise
+ *     determinism, gradient accumulation to a total batch, AdamW with weight decay on 2-D tensors,
+ *     fp32 master weights with bf16 compute: "Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672",
+ *     sections 训练 (training), 参数指南 (flags -d -c -e -y) and 代码 (code);
+ *   - vocabulary padded (50257 -> 50304) for efficiency only: same post, section PyTorch 对比.
+ *
+ * Conventions
+ *   - One model per process; the library is not thread-safe.
+ *   - Device pointers are HIP device memory owned by the caller (e.g. torch tensors). The library
+ *     never allocates device memory: everything it needs lives in the caller's workspace, carved
+ *     once by gpt2_init. Host pointers are owned by the caller and only read/written inside a call.
+ *   - All work is enqueued on cfg.stream (0 = the null stream).
+ *   - Status codes: GPT2_OK (0) or a negative GPT2_E*; gpt2_last_error() describes the last one.
+ *
+ * Parameter layout (flat, float32 master, in this order; weights are [out, in], y = x W^T):
+ *   wte [Vp, C], wpe [max_seq, C], then per layer l = 0..L-1:
+ *   ln1w [C], ln1b [C], qkvw [3C, C], qkvb [3C], attprojw [C, C], attprojb [C], ln2w [C], ln2b [C],
+ *   fcw [4C, C], fcb [4C], fcprojw [C, 4C], fcprojb [C]; then lnfw [C], lnfb [C].
+ *   Linear biases are absent when linear_bias == 0, LayerNorm biases when ln_bias == 0.
+ *   qkvw rows: Q (head h at rows h*hs..), then K, then V. wte is also the classifier (tied).
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPT2_OK 0
+#define GPT2_EINVAL (-1)     /* bad configuration or argument */
+#define GPT2_ENOMEM (-2)     /* workspace smaller than gpt2_workspace_bytes() */
+#define GPT2_EHIP (-3)       /* HIP runtime error */
+#define GPT2_ESTATE (-4)     /* call out of order (e.g. backward without a forward with targets) */
+#define GPT2_ERANGE (-5)     /* token not in [0, V) or target not in [-1, V) */
+#define GPT2_ENONFINITE (-6) /* gradient norm not finite: the update was skipped */
+
+#define GPT2_FP32 0 /* fp32 everywhere */
+#define GPT2_BF16 1 /* bf16 activations and matmul inputs, fp32 accumulation, fp32 master/grads/m/v */
+
+typedef struct {
+  int32_t n_layer, n_head, n_embd; /* L, H, C; C % H == 0, C % 8 == 0 */
+  int32_t vocab, padded_vocab;     /* V (softmax width), Vp >= V rows of wte; Vp <= 65536 */
+  int32_t max_seq;                 /* rows of wpe */
+  int32_t batch, seq;              /* micro-batch B x T, T <= max_seq, B*T <= 32768 */
+  int32_t precision;               /* GPT2_FP32 or GPT2_BF16 (bf16 needs C / H == 64) */
+  int32_t linear_bias, ln_bias;    /* 1/1 for GPT-2; 0/1 for the BabyGPT toy */
+  int32_t grad_accum;              /* micro-steps per update, >= 1 */
+  float grad_clip;                 /* global-norm clip; <= 0 disables */
+  void* stream;                    /* hipStream_t */
+  void* workspace;                 /* device memory, >= gpt2_workspace_bytes(cfg), 256-byte aligned */
+  uint64_t workspace_bytes;
+} gpt2_config;
+
+/* Bytes of device workspace the configuration needs (0 if the configuration is invalid). */
+uint64_t gpt2_workspace_bytes(const gpt2_config* cfg);
+
+/* Validate cfg, carve the workspace, initialise the parameters, zero m and v.
+ * Init: every 2-D tensor in layout order draws N(0, 0.02^2) from one stream (SplitMix64 seeded
+ * with `seed`, Box-Muller in double, rounded to fp32); biases 0; LayerNorm weights 1.
+ * Synchronous. Replaces any previous model. */
+int gpt2_init(const gpt2_config* cfg, uint64_t seed);
+
+/* Forward pass on device int32 tokens [B*T] (row-major [B][T]) and targets [B*T].
+ * targets == NULL: logits only (kept for gpt2_get_logits), returns NaN with status OK.
+ * target < 0 is ignored; the loss is the mean of -log softmax(logits)[target] over valid targets
+ * (0 when there is none). Synchronous: returns the loss, or NaN on error (see gpt2_last_status). */
+float gpt2_forward(const int32_t* tokens, const int32_t* targets);
+
+/* Backward pass of the last forward (which must have had targets). The first backward after
+ * gpt2_init or an update overwrites the gradients, later ones add (gradient accumulation; each
+ * micro-step's loss is scaled by 1 / grad_accum). Asynchronous. */
+int gpt2_backward(void);
+
+/* AdamW update with t >= 1 (bias correction), decoupled weight decay `wd` on 2-D tensors only,
+ * after scaling the gradients by min(1, grad_clip / ||g||) when grad_clip > 0.
+ * In GPT2_BF16 mode also rewrites the bf16 parameter copy. If ||g|| is not finite the update is
+ * skipped on the device; gpt2_grad_norm() then returns a non-finite value. Asynchronous. */
+int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t);
+
+/* Diagnostics and parity (synchronous; host buffers owned by the caller). */
+float gpt2_grad_norm(void);     /* pre-clip global L2 norm of the last update's gradients */
+int gpt2_last_status(void);     /* status of the most recent call */
+const char* gpt2_last_error(void);
+uint64_t gpt2_num_params(void);
+int gpt2_get_params(float* dst, uint64_t n);      /* fp32 master, layout order */
+int gpt2_set_params(const float* src, uint64_t n); /* also refreshes the bf16 copy */
+int gpt2_get_grads(float* dst, uint64_t n);
+int gpt2_get_adam_state(float* m, float* v, uint64_t n);
+/* Logits of the last forward, [B*T, V] as float (real vocabulary only). Valid until backward. */
+int gpt2_get_logits(float* dst, uint64_t n);
+void gpt2_free(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_H */

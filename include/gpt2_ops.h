@@ -1,0 +1,78 @@
+/*
+ * gpt2_ops.h -- per-kernel entry points of the GPT-2 training-step library.
+ *
+ * Each call enqueues one step of the training step on raw device pointers (caller-owned HIP
+ * device memory) so that it can be checked on its own against the CPU oracle. `dtype` is
+ * GPT2_FP32 (float buffers) or GPT2_BF16 (bf16 buffers, 16-bit storage); fp32 statistics and
+ * gradients of parameters are always float. `stream` is a hipStream_t. Every call returns
+ * GPT2_OK or GPT2_EINVAL (unsupported shape or argument) / GPT2_EHIP (launch failure).
+ * Row-major layouts throughout; all leading dimensions and tensor widths must be multiples of
+ * 8 elements (16 bytes) and every pointer 16-byte aligned.
+ */
+#ifndef GPT2_OPS_H
+#define GPT2_OPS_H
+
+#include <stdint.h>
+
+#include "gpt2.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Epilogues of gpt2op_gemm */
+#define GPT2_EPI_BIAS 0     /* C = acc + bias                        (C in dtype)       */
+#define GPT2_EPI_GELU 1     /* C = acc + bias ; C2 = gelu_tanh(C)    (forward MLP)      */
+#define GPT2_EPI_RESID 2    /* C = aux + acc + bias                  (residual add)     */
+#define GPT2_EPI_GELU_BWD 3 /* C = acc * gelu_tanh'(aux)             (MLP backward)     */
+#define GPT2_EPI_F32 4      /* C(float) = acc, or += acc when accumulate (weight grads)  */
+
+/* C[M,N] = sum_k A(m,k) B(n,k) then the epilogue.
+ * A(m,k) = A[m*lda + k] if a_kcontig else A[k*lda + m]; B(n,k) = B[n*ldb + k] if b_kcontig
+ * else B[k*ldb + n]. bias [N] (dtype) may be NULL. aux has leading dimension ldaux.
+ * scratch (float, scratch_floats) enables deterministic split-K for GPT2_EPI_F32; may be NULL.
+ * Linear layer forward is (a_kcontig=1, b_kcontig=1), input-gradient (1, 0), weight-gradient (0, 0). */
+int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
+                int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias, const void* aux,
+                int64_t ldaux, void* C2, int accumulate, float* scratch, uint64_t scratch_floats, void* stream);
+
+/* LayerNorm over rows of width C (eps 1e-5, biased variance): y, mean[rows], rstd[rows]. b may be NULL. */
+int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,
+                             float* mean, float* rstd, void* stream);
+/* dres += dx; dw, db (float [C]) = or += column sums (accumulate). db may be NULL.
+ * partial: float scratch of gpt2op_layernorm_backward_scratch(rows, C) elements. */
+int gpt2op_layernorm_backward(int dtype, int rows, int C, const void* dy, const void* x, const void* w,
+                              const float* mean, const float* rstd, void* dres, float* dw, float* db,
+                              int accumulate, float* partial, void* stream);
+uint64_t gpt2op_layernorm_backward_scratch(int rows, int C);
+
+/* Causal attention of qkv [B,T,3C] (Q|K|V, head h at columns h*hs of each third) into
+ * out [B,T,C] and lse [B,H,T] (natural log of the softmax denominators). bf16 requires hs == 64;
+ * fp32 supports hs in {4, 8, 16, 32, 64}. */
+int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,
+                             void* stream);
+/* dqkv [B,T,3C] (fully written) from qkv, out, dout, lse; dvec: float scratch [B*H*T]. */
+int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
+                              const void* dout, const float* lse, void* dqkv, float* dvec, void* stream);
+
+/* Softmax cross-entropy over the first V of ld columns of each row. losses[rows] (float).
+ * When dloss != NULL (device float scalar), logits are overwritten by (softmax - onehot)*dloss,
+ * with 0 in padded columns and on rows whose target is < 0. */
+int gpt2op_cross_entropy(int dtype, int rows, int V, int ld, void* logits, const int32_t* targets,
+                         const float* dloss, float* losses, void* stream);
+
+/* out[b,t,:] = wte[tok[b,t],:] + wpe[t,:]; err (device int) gets bit 0 set on an id outside [0, V). */
+int gpt2op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t* tok, const void* wte,
+                           const void* wpe, void* out, int* err, void* stream);
+/* dwte[tok[p]] += dout[p] for every position p (deterministic order); dwpe[t] = or += sum_b dout[b,t]
+ * (rows t >= T of the max_seq rows are set to 0 / left). keys: uint32 scratch [B*T];
+ * partial: float scratch of gpt2op_encoder_backward_scratch(B*T, C) elements. */
+int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok,
+                            const void* dout, float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys,
+                            float* partial, void* stream);
+uint64_t gpt2op_encoder_backward_scratch(int BT, int C);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_OPS_H */

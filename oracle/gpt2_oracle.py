@@ -47,7 +47,7 @@ __all__ = [
     "attention_forward", "attention_backward", "cross_entropy_forward_backward",
     "encoder_forward", "encoder_backward",
     "forward_backward", "forward_logits", "next_token_probs",
-    "grad_norm", "clip_scale", "adamw_update", "train",
+    "grad_norm", "clip_scale", "adamw_update", "train", "matmul_nt",
     "CFG_TOY", "CFG_124M", "CFG_350M", "CFG_1558M",
 ]
 
@@ -147,12 +147,12 @@ def layernorm_backward(dy, xhat, rstd, w):
 
 def gelu(f):
     """GELU, tanh form: 0.5 f (1 + tanh(sqrt(2/pi) (f + 0.044715 f^3)))."""
-    return 0.5 * f * (1.0 + np.tanh(GELU_K * (f + GELU_C * f ** 3)))
+    return 0.5 * f * (1.0 + np.tanh(GELU_K * (f + GELU_C * f * f * f)))
 
 
 def gelu_grad(f):
     """d gelu / d f for the tanh form."""
-    t = np.tanh(GELU_K * (f + GELU_C * f ** 3))
+    t = np.tanh(GELU_K * (f + GELU_C * f * f * f))
     return 0.5 * (1.0 + t) + 0.5 * f * (1.0 - t * t) * GELU_K * (1.0 + 3.0 * GELU_C * f * f)
 
 
@@ -414,3 +414,8 @@ def train(cfg: Config, params, batches, lr, b1, b2, eps, wd, clip=0.0, grad_accu
         losses.append(lsum / grad_accum)
         norms.append(nrm)
     return p, m, v, losses, norms
+
+
+def matmul_nt(a, b):
+    """a @ b^T in float64: the product every Linear layer (y = x W^T) and its gradients use."""
+    return np.asarray(a, np.float64) @ np.asarray(b, np.float64).T

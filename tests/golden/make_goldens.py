@@ -1,0 +1,94 @@
+"""Write the oracle's expected values for the full-size parity tests.
+
+Calls only oracle/ (and the seeded input generators). Run from the repository root:
+    python tests/golden/make_goldens.py cfg2     # GPT-2 124M fp32, B=4: one step   (~2 min)
+    python tests/golden/make_goldens.py cfg3     # GPT-2 124M, B=16: 10 updates     (~45 min)
+
+cfg2 -> tests/golden/gpt2_124m_fp32_b4_step1.npz: the loss, the pre-clip gradient norm, and
+        for every tensor its max |g| plus g, and theta/m/v after one AdamW update, at 64
+        seeded sample positions (the full vectors are 124M elements).
+cfg3 -> tests/golden/gpt2_124m_b16_10steps.json: the per-update mean losses and norms of
+        10 updates with lr 6e-4, betas (0.9, 0.95), eps 1e-8, wd 0.1, clip 1.0.
+Inputs: parameters from the seed-1337 normal(0, 0.02) init, Zipf(1.1) token stream of seed 42
+(micro-step s uses stream positions s*(B*T+1) ...).
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle as O  # noqa: E402
+from gpt_transformer_step_train_amd import synth  # noqa: E402
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+N_SAMPLES = 64
+
+
+def sample_positions(cfg, seed=2024):
+    """Per tensor: 64 seeded flat positions (sorted), as absolute indices into the flat vector."""
+    rng = np.random.default_rng(seed)
+    out, off = [], 0
+    for _, shape in O.param_layout(cfg):
+        n = int(np.prod(shape))
+        k = min(n, N_SAMPLES)
+        out.append(off + np.sort(rng.choice(n, k, replace=False)))
+        off += n
+    return out
+
+
+def init(cfg):
+    return synth.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq,
+                             cfg.linear_bias, cfg.ln_bias).astype(np.float64)
+
+
+def make_cfg2():
+    cfg, B, T = O.CFG_124M, 4, 1024
+    p0 = init(cfg)
+    tok, tgt = synth.zipf_batch(cfg.vocab, B, T, 0)
+    t0 = time.time()
+    loss, g = O.forward_backward(cfg, p0, tok, tgt)
+    lr, b1, b2, eps, wd = 3e-4, 0.9, 0.999, 1e-8, 0.0
+    p1, m1, v1, norm = O.adamw_update(cfg, p0, g, 0 * p0, 0 * p0, lr, b1, b2, eps, wd, 1, 0.0)
+    print(f"cfg2: loss {loss:.8f} norm {norm:.6f} ({time.time() - t0:.1f} s)")
+    pos = sample_positions(cfg)
+    offs = np.cumsum([0] + [int(np.prod(s)) for _, s in O.param_layout(cfg)])
+    gmax = np.array([np.abs(g[offs[i]:offs[i + 1]]).max() for i in range(len(pos))])
+    flat_pos = np.concatenate(pos)
+    np.savez_compressed(os.path.join(HERE, "gpt2_124m_fp32_b4_step1.npz"),
+                        loss=loss, norm=norm, gmax=gmax, positions=flat_pos,
+                        counts=np.array([len(p) for p in pos]),
+                        g=g[flat_pos], p1=p1[flat_pos], m1=m1[flat_pos], v1=v1[flat_pos],
+                        hyper=np.array([lr, b1, b2, eps, wd]))
+
+
+def make_cfg3():
+    cfg, B, T, steps = O.CFG_124M, 16, 1024, 10
+    p = init(cfg)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    lr, b1, b2, eps, wd, clip = 6e-4, 0.9, 0.95, 1e-8, 0.1, 1.0
+    losses, norms = [], []
+    for s in range(steps):
+        t0 = time.time()
+        tok, tgt = synth.zipf_batch(cfg.vocab, B, T, s)
+        loss, g = O.forward_backward(cfg, p, tok, tgt)
+        p, m, v, norm = O.adamw_update(cfg, p, g, m, v, lr, b1, b2, eps, wd, s + 1, clip)
+        losses.append(loss)
+        norms.append(norm)
+        print(f"cfg3 step {s + 1}: loss {loss:.6f} norm {norm:.4f} ({time.time() - t0:.0f} s)",
+              flush=True)
+        with open(os.path.join(HERE, "gpt2_124m_b16_10steps.json"), "w") as f:
+            json.dump({"config": "GPT-2 124M, B=16, T=1024, Zipf(1.1) seed 42, init seed 1337",
+                       "hyper": dict(lr=lr, b1=b1, b2=b2, eps=eps, wd=wd, clip=clip),
+                       "losses": losses, "norms": norms, "complete": len(losses) == steps},
+                      f, indent=1)
+
+
+if __name__ == "__main__":
+    for what in sys.argv[1:]:
+        {"cfg2": make_cfg2, "cfg3": make_cfg3}[what]()

@@ -1,0 +1,313 @@
+"""Per-kernel parity: each HIP kernel (through include/gpt2_ops.h) against the CPU oracle's function
+for the same step, on the same seeded inputs, element by element.
+
+Tolerances (max-norm relative to the reference unless stated):
+  fp32 kernels: 2e-5 (accumulation order only);
+  bf16 outputs: 8e-3 (one bf16 rounding of the result is 2^-9 relative, plus bf16 inputs);
+  bf16 attention gradients: 2e-2 (probabilities are rounded to bf16 before the second MFMA).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpt_transformer_step_train_amd import binding as bd
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib(gpu_lib):
+    return gpu_lib
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+TD = {bd.GPT2_FP32: torch.float32, bd.GPT2_BF16: torch.bfloat16}
+
+
+def dev(x, dt):
+    return torch.tensor(np.asarray(x, np.float32)).to("cuda").to(TD[dt]).contiguous()
+
+
+def h64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel(a, ref):
+    return float(np.abs(a - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def tol(dt, f32=2e-5, b16=8e-3):
+    return f32 if dt == bd.GPT2_FP32 else b16
+
+
+DTS = [bd.GPT2_FP32, bd.GPT2_BF16]
+
+
+# ---------------------------------------------------------------------------- GEMM
+
+GEMM_SHAPES = [(200, 136, 72), (256, 384, 256), (36, 16, 2), (130, 264, 520)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("akc,bkc", [(1, 1), (1, 0), (0, 0), (0, 1)])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm_layouts_bias(dt, akc, bkc, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N + K)
+    vec = 8
+    A = rng.normal(0, 1, (M, K))
+    Bm = rng.normal(0, 1, (N, K))
+    bias = rng.normal(0, 1, N)
+    lda = -(-K // vec) * vec if akc else -(-M // vec) * vec
+    ldb = -(-K // vec) * vec if bkc else -(-N // vec) * vec
+    As = np.zeros((M, lda)) if akc else np.zeros((K, lda))
+    if akc:
+        As[:, :K] = A
+    else:
+        As[:, :M] = A.T
+    Bs = np.zeros((N, ldb)) if bkc else np.zeros((K, ldb))
+    if bkc:
+        Bs[:, :K] = Bm
+    else:
+        Bs[:, :N] = Bm.T
+    Ad, Bd, bd_ = dev(As, dt), dev(Bs, dt), dev(bias, dt)
+    ldc = -(-N // vec) * vec
+    Cd = torch.zeros((M, ldc), dtype=TD[dt], device="cuda")
+    rc = bd.load().gpt2op_gemm(dt, akc, bkc, bd.EPI_BIAS, M, N, K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb,
+                               Cd.data_ptr(), ldc, bd_.data_ptr(), None, 0, None, 0, None, 0, stream())
+    assert rc == 0, bd.last_error()
+    torch.cuda.synchronize()
+    a64 = h64(Ad)[:, :K] if akc else h64(Ad)[:, :M].T
+    b64 = h64(Bd)[:, :K] if bkc else h64(Bd)[:, :N].T
+    ref = O.matmul_nt(a64, b64) + h64(bd_)
+    assert rel(h64(Cd)[:, :N], ref) <= tol(dt)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_gemm_gelu_resid_and_gelu_backward_epilogues(dt):
+    M, N, K = 160, 200, 96
+    rng = np.random.default_rng(3)
+    A, W, b = rng.normal(0, 1, (M, K)), rng.normal(0, 0.2, (N, K)), rng.normal(0, 0.5, N)
+    aux = rng.normal(0, 1, (M, N))
+    Ad, Wd, bd_, auxd = dev(A, dt), dev(W, dt), dev(b, dt), dev(aux, dt)
+    lib = bd.load()
+    pre = torch.zeros((M, N), dtype=TD[dt], device="cuda")
+    g = torch.zeros_like(pre)
+    rc = lib.gpt2op_gemm(dt, 1, 1, bd.EPI_GELU, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, pre.data_ptr(), N,
+                         bd_.data_ptr(), None, 0, g.data_ptr(), 0, None, 0, stream())
+    assert rc == 0
+    res = torch.zeros_like(pre)
+    rc = lib.gpt2op_gemm(dt, 1, 1, bd.EPI_RESID, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, res.data_ptr(), N,
+                         bd_.data_ptr(), auxd.data_ptr(), N, None, 0, None, 0, stream())
+    assert rc == 0
+    gb = torch.zeros_like(pre)
+    rc = lib.gpt2op_gemm(dt, 1, 1, bd.EPI_GELU_BWD, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, gb.data_ptr(), N,
+                         None, auxd.data_ptr(), N, None, 0, None, 0, stream())
+    assert rc == 0
+    torch.cuda.synchronize()
+    acc = O.matmul_nt(h64(Ad), h64(Wd))
+    pre_ref = acc + h64(bd_)
+    assert rel(h64(pre), pre_ref) <= tol(dt)
+    assert rel(h64(g), O.gelu(pre_ref)) <= tol(dt, 5e-5)
+    assert rel(h64(res), h64(auxd) + pre_ref) <= tol(dt)
+    assert rel(h64(gb), acc * O.gelu_grad(h64(auxd))) <= tol(dt, 5e-5)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("M,N,K", [(128, 136, 4096), (96, 64, 520), (768, 256, 2048)])
+def test_gemm_f32_weight_gradient_split_k_accumulate(dt, M, N, K):
+    # dW[M,N] (+)= dY^T X with both operands row-contiguous (K = rows of the batch)
+    rng = np.random.default_rng(M + N + K)
+    dY, X = rng.normal(0, 1, (K, M)), rng.normal(0, 1, (K, N))
+    dYd, Xd = dev(dY, dt), dev(X, dt)
+    C0 = rng.normal(0, 1, (M, N)).astype(np.float32)
+    lib = bd.load()
+    scratch = torch.empty(16 * M * N, dtype=torch.float32, device="cuda")
+    ref = O.matmul_nt(h64(dYd).T, h64(Xd).T)
+    for accumulate in (0, 1):
+        Cd = torch.tensor(C0, device="cuda")
+        rc = lib.gpt2op_gemm(dt, 0, 0, bd.EPI_F32, M, N, K, dYd.data_ptr(), M, Xd.data_ptr(), N, Cd.data_ptr(), N,
+                             None, None, 0, None, accumulate, scratch.data_ptr(), scratch.numel(), stream())
+        assert rc == 0
+        torch.cuda.synchronize()
+        want = ref + (C0 if accumulate else 0)
+        assert rel(Cd.cpu().numpy().astype(np.float64), want) <= 2e-5
+    # split-K partials are summed in a fixed order: bitwise reproducible
+    outs = []
+    for _ in range(2):
+        Cd = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+        lib.gpt2op_gemm(dt, 0, 0, bd.EPI_F32, M, N, K, dYd.data_ptr(), M, Xd.data_ptr(), N, Cd.data_ptr(), N,
+                        None, None, 0, None, 0, scratch.data_ptr(), scratch.numel(), stream())
+        torch.cuda.synchronize()
+        outs.append(Cd.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------------------- LayerNorm
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("rows,C,has_b", [(37, 16, True), (300, 768, True), (65, 200, False), (1030, 1600, True)])
+def test_layernorm_forward_backward(dt, rows, C, has_b):
+    if dt == bd.GPT2_BF16 and C % 8:
+        pytest.skip("bf16 needs C % 8 == 0")
+    rng = np.random.default_rng(rows + C)
+    x = rng.normal(0.5, 2.0, (rows, C))
+    w = 1.0 + rng.normal(0, 0.2, C)
+    b = rng.normal(0, 0.2, C)
+    dy = rng.normal(0, 1, (rows, C))
+    dres0 = rng.normal(0, 1, (rows, C))
+    xd, wd, bdv, dyd, dres = dev(x, dt), dev(w, dt), dev(b, dt), dev(dy, dt), dev(dres0, dt)
+    y = torch.empty_like(xd)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+    lib = bd.load()
+    rc = lib.gpt2op_layernorm_forward(dt, rows, C, xd.data_ptr(), wd.data_ptr(), bdv.data_ptr() if has_b else None,
+                                      y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), stream())
+    assert rc == 0
+    dw = torch.full((C,), 0.25, dtype=torch.float32, device="cuda")
+    db = torch.full((C,), -0.5, dtype=torch.float32, device="cuda")
+    part = torch.empty(lib.gpt2op_layernorm_backward_scratch(rows, C), dtype=torch.float32, device="cuda")
+    dres_before = h64(dres)
+    rc = lib.gpt2op_layernorm_backward(dt, rows, C, dyd.data_ptr(), xd.data_ptr(), wd.data_ptr(), mean.data_ptr(),
+                                       rstd.data_ptr(), dres.data_ptr(), dw.data_ptr(), db.data_ptr(), 1,
+                                       part.data_ptr(), stream())
+    assert rc == 0
+    torch.cuda.synchronize()
+    x64, w64, b64 = h64(xd), h64(wd), h64(bdv) if has_b else None
+    yref, (mu, rs, xhat) = O.layernorm_forward(x64, w64, b64)
+    assert rel(h64(y), yref) <= tol(dt)
+    np.testing.assert_allclose(mean.cpu().numpy(), mu, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(rstd.cpu().numpy(), rs, rtol=1e-5)
+    dx, dwr, dbr = O.layernorm_backward(h64(dyd), xhat, rs, w64)
+    got = h64(dres) - dres_before if dt == bd.GPT2_FP32 else h64(dres)
+    want = dx if dt == bd.GPT2_FP32 else dres_before + dx
+    assert rel(got, want) <= tol(dt, 5e-5)
+    assert rel(dw.cpu().numpy(), dwr + 0.25) <= 5e-5
+    assert rel(db.cpu().numpy(), dbr - 0.5) <= 5e-5
+
+
+# ---------------------------------------------------------------------------- attention
+
+ATT_CASES = [(bd.GPT2_FP32, 2, 3, 4, 4), (bd.GPT2_FP32, 1, 130, 2, 64), (bd.GPT2_BF16, 2, 256, 2, 64),
+             (bd.GPT2_BF16, 1, 200, 3, 64), (bd.GPT2_BF16, 1, 1024, 1, 64), (bd.GPT2_BF16, 1, 33, 1, 64)]
+
+
+@pytest.mark.parametrize("dt,B,T,H,hs", ATT_CASES)
+def test_attention_forward_backward(dt, B, T, H, hs):
+    C = H * hs
+    rng = np.random.default_rng(T + H)
+    qkv = rng.normal(0, 1, (B, T, 3 * C))
+    dout = rng.normal(0, 1, (B, T, C))
+    qd, dod = dev(qkv, dt), dev(dout, dt)
+    out = torch.empty((B, T, C), dtype=TD[dt], device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    lib = bd.load()
+    assert lib.gpt2op_attention_forward(dt, B, T, H, hs, qd.data_ptr(), out.data_ptr(), lse.data_ptr(), stream()) == 0
+    dq = torch.full((B, T, 3 * C), float("nan"), dtype=TD[dt], device="cuda")
+    dvec = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    assert lib.gpt2op_attention_backward(dt, B, T, H, hs, qd.data_ptr(), out.data_ptr(), dod.data_ptr(),
+                                         lse.data_ptr(), dq.data_ptr(), dvec.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    q64, o_gpu, do64 = h64(qd), h64(out), h64(dod)
+    for b in range(B):
+        o_ref, probs, lse_ref = O.attention_forward(q64[b], H)
+        assert rel(o_gpu[b], o_ref) <= tol(dt, 2e-5, 1e-2)
+        np.testing.assert_allclose(lse.cpu().numpy()[b], lse_ref, atol=1e-4 if dt == bd.GPT2_FP32 else 2e-2)
+        # gradient with the GPU's own output as O (D = rowsum(dO * O) uses it); reference uses oracle probs
+        dq_ref = O.attention_backward(do64[b], q64[b], probs, H)
+        assert rel(h64(dq)[b], dq_ref) <= tol(dt, 5e-5, 2e-2)
+
+
+def test_attention_rejects_unsupported_head_size():
+    lib = bd.load()
+    x = torch.zeros(8, device="cuda")
+    assert lib.gpt2op_attention_forward(bd.GPT2_BF16, 1, 4, 1, 32, x.data_ptr(), x.data_ptr(), x.data_ptr(),
+                                        stream()) == bd.GPT2_EINVAL
+
+
+# ---------------------------------------------------------------------------- cross-entropy
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("rows,V,ld", [(37, 1000, 1008), (8, 50257, 50304), (36, 2, 8)])
+def test_cross_entropy(dt, rows, V, ld):
+    rng = np.random.default_rng(rows + V)
+    logits = np.zeros((rows, ld))
+    logits[:, :V] = rng.normal(0, 2, (rows, V))
+    logits[:, V:] = 77.0  # padded columns must not matter
+    tgt = rng.integers(0, V, rows).astype(np.int32)
+    tgt[::5] = -1
+    n_valid = int((tgt >= 0).sum())
+    ld_ = dev(logits, dt)
+    x64 = h64(ld_)[:, :V]
+    td = torch.tensor(tgt, device="cuda")
+    dloss = torch.tensor([1.0 / n_valid], dtype=torch.float32, device="cuda")
+    losses = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rc = bd.load().gpt2op_cross_entropy(dt, rows, V, ld, ld_.data_ptr(), td.data_ptr(), dloss.data_ptr(),
+                                        losses.data_ptr(), stream())
+    assert rc == 0
+    torch.cuda.synchronize()
+    l_ref, d_ref = O.cross_entropy_forward_backward(x64, tgt, 1.0 / n_valid)
+    np.testing.assert_allclose(losses.cpu().numpy(), l_ref, rtol=1e-5, atol=1e-5)
+    d = h64(ld_)
+    assert rel(d[:, :V], d_ref) <= tol(dt, 1e-5, 8e-3)
+    assert np.all(d[:, V:] == 0.0)
+
+
+# ---------------------------------------------------------------------------- encoder
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("B,T,maxT,C,V,p0", [(4, 64, 80, 128, 500, 0.14), (4, 256, 256, 64, 300, 0.5),
+                                            (12, 3, 3, 16, 2, 0.5)])
+def test_encoder_forward_backward_deterministic(dt, B, T, maxT, C, V, p0):
+    rng = np.random.default_rng(B * T + V)
+    tok = rng.integers(0, V, (B, T)).astype(np.int32)
+    tok[rng.random((B, T)) < p0] = 0  # long runs of one id, crossing many 32-entry chunks
+    wte, wpe = rng.normal(0, 1, (V, C)), rng.normal(0, 1, (maxT, C))
+    dout = rng.normal(0, 1, (B, T, C))
+    lib = bd.load()
+    wted, wped, dod = dev(wte, dt), dev(wpe, dt), dev(dout, dt)
+    tokd = torch.tensor(tok, device="cuda")
+    out = torch.empty((B, T, C), dtype=TD[dt], device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert lib.gpt2op_encoder_forward(dt, B, T, C, V, tokd.data_ptr(), wted.data_ptr(), wped.data_ptr(),
+                                      out.data_ptr(), err.data_ptr(), stream()) == 0
+    keys = torch.empty(B * T, dtype=torch.int32, device="cuda")
+    part = torch.empty(lib.gpt2op_encoder_backward_scratch(B * T, C), dtype=torch.float32, device="cuda")
+    results = []
+    dwte0 = rng.normal(0, 1, (V, C)).astype(np.float32)
+    for _ in range(2):
+        dwte = torch.tensor(dwte0, device="cuda")
+        dwpe = torch.full((maxT, C), 3.0, dtype=torch.float32, device="cuda")
+        assert lib.gpt2op_encoder_backward(dt, B, T, maxT, C, V, tokd.data_ptr(), dod.data_ptr(), dwte.data_ptr(),
+                                           dwpe.data_ptr(), 0, keys.data_ptr(), part.data_ptr(), stream()) == 0
+        torch.cuda.synchronize()
+        results.append((dwte.cpu().numpy(), dwpe.cpu().numpy()))
+    assert err.item() == 0
+    ref_out = np.stack([O.encoder_forward(h64(wted), h64(wped), tok[b]) for b in range(B)])
+    assert rel(h64(out), ref_out) <= tol(dt)
+    dwte_ref = dwte0.astype(np.float64).copy()
+    dwpe_ref = np.zeros((maxT, C))
+    for b in range(B):
+        O.encoder_backward(dwte_ref, dwpe_ref, h64(dod)[b], tok[b])
+    assert rel(results[0][0].astype(np.float64), dwte_ref) <= 2e-5
+    assert rel(results[0][1].astype(np.float64), dwpe_ref) <= 2e-5
+    assert np.array_equal(results[0][0], results[1][0]) and np.array_equal(results[0][1], results[1][1])
+
+
+def test_encoder_flags_out_of_range_token():
+    lib = bd.load()
+    B, T, C, V = 1, 4, 16, 10
+    tok = torch.tensor([[1, 2, 10, 3]], dtype=torch.int32, device="cuda")
+    w = torch.zeros((V, C), device="cuda")
+    p = torch.zeros((T, C), device="cuda")
+    out = torch.empty((B, T, C), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert lib.gpt2op_encoder_forward(bd.GPT2_FP32, B, T, C, V, tok.data_ptr(), w.data_ptr(), p.data_ptr(),
+                                      out.data_ptr(), err.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    assert err.item() & 1
