@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Throughput of the GPT-2 training step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-350m|gpt2-1558m]
+
+A step is one full training step through the C ABI: forward + backward (times grad_accum
+micro-batches) + the AdamW update, on synthetic Zipf(1.1) token batches that are already resident
+in HBM. The default workload is GPT-2 124M, B=16, T=1024, bf16 mixed precision (fp32 master
+weights, grads and AdamW state), AdamW lr 6e-4, betas (0.9, 0.95), wd 0.1, clip 1.0.
+
+Prints one JSON line: tokens/s, ms/step and model-FLOPs utilisation (6N + 6LCT FLOPs per token,
+the formula that reproduces the MFU column of the llm.c GPT-2 reproduction post), the roofline of
+the kernel class that takes the most time (timed with HIP events on the library's stream over the
+timed steps) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s (published)
+PEAK_HBM = 8.0e12       # MI355X HBM3E, bytes/s (published)
+METRIC = "training tokens/sec + bf16 MFU, GPT-2 124M B=16 T=1024 on 1 MI355X"
+
+WORKLOADS = {
+    "gpt2-124m": dict(L=12, H=12, C=768, V=50257, Vp=50304, T=1024, B=16, accum=1),
+    "gpt2-350m": dict(L=24, H=16, C=1024, V=50257, Vp=50304, T=1024, B=16, accum=1),
+    "gpt2-1558m": dict(L=48, H=25, C=1600, V=50257, Vp=50304, T=1024, B=16, accum=64),
+}
+HP = dict(lr=6e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
+
+
+def num_params(w):
+    C = w["C"]
+    return w["Vp"] * C + w["T"] * C + w["L"] * (12 * C * C + 13 * C) + 2 * C
+
+
+def class_work(name, w):
+    """(bound, algorithmic flops or bytes per launch) of one launch of a kernel class."""
+    B, T, C, H, Vp, L = w["B"], w["T"], w["C"], w["H"], w["Vp"], w["L"]
+    BT, hs = B * T, C // H
+    gemm = {"gemm_qkv": (BT, 3 * C, C), "gemm_attproj": (BT, C, C), "gemm_fc": (BT, 4 * C, C),
+            "gemm_fcproj": (BT, C, 4 * C), "gemm_classifier": (BT, Vp, C), "gemm_classifier_dx": (BT, C, Vp),
+            "gemm_classifier_dw": (Vp, C, BT), "gemm_fcproj_dx": (BT, 4 * C, C), "gemm_fcproj_dw": (C, 4 * C, BT),
+            "gemm_fc_dx": (BT, C, 4 * C), "gemm_fc_dw": (4 * C, C, BT), "gemm_attproj_dx": (BT, C, C),
+            "gemm_attproj_dw": (C, C, BT), "gemm_qkv_dx": (BT, C, 3 * C), "gemm_qkv_dw": (3 * C, C, BT)}
+    if name in gemm:
+        M, N, K = gemm[name]
+        return "mfma", 2.0 * M * N * K
+    if name == "attention_fwd":      # QK^T and PV over the causal half
+        return "mfma", 2.0 * B * H * T * T * hs
+    if name == "attention_bwd":      # dV, dP, dQ, dK (recompute not credited)
+        return "mfma", 4.0 * B * H * T * T * hs
+    e = 2  # bf16 activations
+    N = num_params(w)
+    bytes_ = {
+        "encoder_fwd": BT * C * e * 2 + T * C * e + BT * 4,          # gather rows + wpe + write
+        "layernorm_fwd": BT * C * e * 2 + BT * 8 + 2 * C * e,
+        "cross_entropy": BT * Vp * e * 2 + BT * 8,                   # read logits, write dlogits in place
+        "layernorm_bwd": BT * C * e * 4 + BT * 8 + 2 * C * 4,         # dy, x, dres read+write
+        "bias_grad": BT * C * e,                                      # average row width ~C
+        "encoder_bwd": BT * C * e + BT * C * 4 + T * C * 4,
+        "grad_norm": N * 4,
+        "adamw": N * (4 * 3 * 2 + 4 + 2),                             # p, m, v rw + g read + bf16 write
+    }
+    return "hbm", float(bytes_.get(name, 0))
+
+
+def cpu_baseline(w, seconds_hint=""):
+    """The oracle (plain fp64 numpy, test infrastructure) on one sequence of the same workload."""
+    import numpy as np
+    import oracle as O
+    from gpt_transformer_step_train_amd import synth
+    cfg = O.Config(w["L"], w["H"], w["C"], w["V"], w["Vp"], w["T"])
+    p = synth.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq)
+    tok, tgt = synth.zipf_batch(w["V"], 1, w["T"], 0)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    O.forward_backward(cfg, p, tok, tgt)
+    dt = time.perf_counter() - t0
+    return {"value": round(w["T"] / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"forward+backward of 1 of the {w['B']} sequences (T={w['T']}) of one micro-batch, "
+                      f"fp64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-table", action="store_true", help="print the per-class kernel times to stderr")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (the training step here has no multi-GPU path); got --gpus "
+              f"{args.gpus}, WORLD_SIZE {world}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from gpt_transformer_step_train_amd import binding as bd
+    from gpt_transformer_step_train_amd import synth
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    m = bd.Model(w["L"], w["H"], w["C"], w["V"], w["Vp"], w["T"], w["B"], w["T"], bd.GPT2_BF16,
+                 grad_accum=w["accum"], grad_clip=1.0, seed=synth.PARAM_SEED)
+    n_micro = (args.warmup + args.steps + 1) * w["accum"]
+    n_distinct = min(n_micro, 8)           # batches are reused cyclically beyond 8 micro-steps
+    batches = []
+    for s in range(n_distinct):
+        tok, tgt = synth.zipf_batch(w["V"], w["B"], w["T"], s)
+        batches.append((torch.tensor(tok.reshape(-1), device="cuda"), torch.tensor(tgt.reshape(-1), device="cuda")))
+    torch.cuda.synchronize()
+
+    state = {"t": 0, "micro": 0}
+    losses = []
+
+    def step():
+        for _ in range(w["accum"]):
+            tok, tgt = batches[state["micro"] % n_distinct]
+            state["micro"] += 1
+            losses.append(m.forward(tok, tgt))
+            m.backward()
+        state["t"] += 1
+        m.step(HP["lr"], HP["b1"], HP["b2"], HP["eps"], HP["wd"], state["t"])
+
+    for _ in range(args.warmup):
+        step()
+    # one profiled step (outside the timed region) picks the class that takes the most time
+    ncls = len(bd.KERNEL_CLASSES)
+    ms = np.zeros(ncls, np.float32)
+    cnt = np.zeros(ncls, np.int32)
+    bd.check(bd.gpt2_profile_enable((1 << ncls) - 1), "profile")
+    step()
+    bd.check(bd.gpt2_profile_read(ms, cnt), "profile")
+    dom = int(np.argmax(ms))
+    if args.kernel_table:
+        for i in np.argsort(-ms):
+            if cnt[i]:
+                print(f"  {bd.KERNEL_CLASSES[i]:20s} {ms[i]:8.3f} ms  x{cnt[i]:3d}  avg {ms[i] / cnt[i] * 1e3:8.1f} us",
+                      file=sys.stderr)
+
+    # timed region: only the dominant class carries events
+    bd.check(bd.gpt2_profile_enable(1 << dom), "profile")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    bd.check(bd.gpt2_profile_read(ms, cnt), "profile")
+    bd.gpt2_profile_enable(0)
+
+    sec = (t1 - t0) / args.steps
+    tokens_per_step = w["B"] * w["T"] * w["accum"]
+    tps = tokens_per_step / sec
+    flops_tok = 6 * num_params(w) + 6 * w["L"] * w["C"] * w["T"]
+    mfu = tps * flops_tok / PEAK_BF16
+    name = bd.KERNEL_CLASSES[dom]
+    bound, work = class_work(name, w)
+    avg_s = ms[dom] / 1e3 / max(cnt[dom], 1)
+    achieved = work / avg_s
+    peak = PEAK_BF16 if bound == "mfma" else PEAK_HBM
+    unit = "TFLOP/s" if bound == "mfma" else "GB/s"
+    scale = 1e12 if bound == "mfma" else 1e9
+    roof = {"bound": bound, "kernel": name, "launches_per_step": int(cnt[dom] // args.steps),
+            "avg_launch_us": round(avg_s * 1e6, 2), "achieved": round(achieved / scale, 2),
+            "peak": peak / scale, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload} train step, B={w['B']} T={w['T']} grad_accum={w['accum']}, "
+                               f"bf16 mixed (fp32 master/grads/AdamW), Zipf(1.1) tokens",
+                   "global_batch": w["B"] * w["accum"], "seq_len": w["T"], "parallelism": "single GPU"},
+        "mfu": round(mfu, 4),
+        "flops_per_token": flops_tok,
+        "final_loss": round(float(losses[-1]), 5),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

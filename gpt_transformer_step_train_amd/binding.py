@@ -20,7 +20,8 @@ EPI_BIAS, EPI_GELU, EPI_RESID, EPI_GELU_BWD, EPI_F32 = 0, 1, 2, 3, 4
 EXPORTS = [
     "gpt2_workspace_bytes", "gpt2_init", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_grad_norm",
     "gpt2_last_status", "gpt2_last_error", "gpt2_num_params", "gpt2_get_params", "gpt2_set_params",
-    "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_logits", "gpt2_free",
+    "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_logits", "gpt2_free", "gpt2_profile_enable",
+    "gpt2_profile_read",
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch",
@@ -65,6 +66,8 @@ def load(path=LIB_PATH):
         "gpt2_get_adam_state": (ctypes.c_int, [_vp, _vp, _u64]),
         "gpt2_get_logits": (ctypes.c_int, [_vp, _u64]),
         "gpt2_free": (None, []),
+        "gpt2_profile_enable": (ctypes.c_int, [ctypes.c_uint32]),
+        "gpt2_profile_read": (ctypes.c_int, [_vp, _vp, _i32]),
         "gpt2op_gemm": (ctypes.c_int, [ctypes.c_int] * 7 + [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp,
                                                             ctypes.c_int, _vp, _u64, _vp]),
         "gpt2op_layernorm_forward": (ctypes.c_int, [ctypes.c_int] * 3 + [_vp] * 7),
@@ -177,6 +180,21 @@ def gpt2_get_logits(dst):
 
 def gpt2_free():
     load().gpt2_free()
+
+
+KERNEL_CLASSES = ["encoder_fwd", "layernorm_fwd", "gemm_qkv", "attention_fwd", "gemm_attproj", "gemm_fc",
+                  "gemm_fcproj", "gemm_classifier", "cross_entropy", "gemm_classifier_dx", "gemm_classifier_dw",
+                  "layernorm_bwd", "gemm_fcproj_dx", "gemm_fcproj_dw", "bias_grad", "gemm_fc_dx", "gemm_fc_dw",
+                  "gemm_attproj_dx", "gemm_attproj_dw", "attention_bwd", "gemm_qkv_dx", "gemm_qkv_dw",
+                  "encoder_bwd", "grad_norm", "adamw"]
+
+
+def gpt2_profile_enable(mask):
+    return load().gpt2_profile_enable(mask)
+
+
+def gpt2_profile_read(ms, launches):
+    return load().gpt2_profile_read(_ptr(ms), _ptr(launches), ms.size)
 
 
 # ---------------------------------------------------------------- convenience

@@ -16,13 +16,14 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-OBJDIR = os.path.join(PKG, "_build")
-LIB = os.path.join(PKG, "libgpt2.so")
+OBJDIR = os.environ.get("GPT2_OBJ_DIR", os.path.join(PKG, "_build"))
+LIB = os.environ.get("GPT2_LIB_OUT", os.path.join(PKG, "libgpt2.so"))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wno-unused-command-line-argument"]
+FLAGS += os.environ.get("GPT2_EXTRA_FLAGS", "").split()
 
 
 def _headers():

@@ -80,23 +80,26 @@ __global__ __launch_bounds__(AT) void attn_fwd_f32(int T, int H, const float* __
   }
 }
 
-// D[b,h,t] = sum_d dO * O  (fp32 or bf16 inputs)
-template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_dvec(int BT, int T_, int H, int hs, const T* __restrict__ out,
+// D[b,h,t] = sum_d dO * O  (fp32 or bf16 inputs); one thread per (row, head), HS unrolled
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dvec(int BT, int T_, int H, const T* __restrict__ out,
                                                      const T* __restrict__ dout, float* __restrict__ dvec) {
+  constexpr int VEC = Elt<T>::VEC;
   const int i = blockIdx.x * 256 + threadIdx.x;  // over B*T*H
   if (i >= BT * H) return;
   const int row = i / H, h = i % H;
-  const int C = H * hs;
-  const size_t o = (size_t)row * C + h * hs;
-  float s = 0.f;
-  for (int d = 0; d < hs; d += Elt<T>::VEC) {
-    V16<T> a, c;
-    a.load(out + o + d);
-    c.load(dout + o + d);
+  const size_t o = (size_t)row * H * HS + h * HS;
+  V16<T> a[HS / VEC], c[HS / VEC];
 #pragma unroll
-    for (int e = 0; e < Elt<T>::VEC; ++e) s += a.v[e] * c.v[e];
+  for (int j = 0; j < HS / VEC; ++j) {
+    a[j].load(out + o + j * VEC);
+    c[j].load(dout + o + j * VEC);
   }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < HS / VEC; ++j)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s += a[j].v[e] * c[j].v[e];
   const int b = row / T_, t = row % T_;
   dvec[((size_t)b * H + h) * T_ + t] = s;
 }
@@ -644,8 +647,8 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
   const int BT = B * T;
   if (dt == DT_BF16) {
     if (hs != HD) return hipErrorInvalidValue;
-    attn_bwd_dvec<bf16><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, hs, reinterpret_cast<const bf16*>(out),
-                                                                reinterpret_cast<const bf16*>(dout), dvec);
+    attn_bwd_dvec<bf16, HD><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, reinterpret_cast<const bf16*>(out),
+                                                                    reinterpret_cast<const bf16*>(dout), dvec);
     dim3 grid(cdiv(T, BQ), B * H);
     auto Q = reinterpret_cast<const uint16_t*>(qkv);
     auto dO = reinterpret_cast<const uint16_t*>(dout);
@@ -654,8 +657,19 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
     attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
     return hipGetLastError();
   }
-  attn_bwd_dvec<float><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, hs, reinterpret_cast<const float*>(out),
-                                                              reinterpret_cast<const float*>(dout), dvec);
+  {
+    auto O_ = reinterpret_cast<const float*>(out);
+    auto dO_ = reinterpret_cast<const float*>(dout);
+    const int nb = cdiv((long)BT * H, 256);
+    switch (hs) {
+      case 4: attn_bwd_dvec<float, 4><<<nb, 256, 0, s>>>(BT, T, H, O_, dO_, dvec); break;
+      case 8: attn_bwd_dvec<float, 8><<<nb, 256, 0, s>>>(BT, T, H, O_, dO_, dvec); break;
+      case 16: attn_bwd_dvec<float, 16><<<nb, 256, 0, s>>>(BT, T, H, O_, dO_, dvec); break;
+      case 32: attn_bwd_dvec<float, 32><<<nb, 256, 0, s>>>(BT, T, H, O_, dO_, dvec); break;
+      case 64: attn_bwd_dvec<float, 64><<<nb, 256, 0, s>>>(BT, T, H, O_, dO_, dvec); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   auto Q = reinterpret_cast<const float*>(qkv);
   auto dO = reinterpret_cast<const float*>(dout);
   auto dQ = reinterpret_cast<float*>(dqkv);

@@ -176,4 +176,25 @@ __device__ __forceinline__ float gelu_bwd(float x) {
 
 __host__ __device__ constexpr int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// out[c] (+)= sum_{y < ny} part[y * ld + c] for c < ncols, summed in a fixed order.
+// Block of 256 threads handles 32 columns: 8 row-groups stride over y, then 8 partials per
+// column are added in order. Grid: cdiv(ncols, 32).
+__device__ __forceinline__ void reduce_partials_block(const float* __restrict__ part, int ny, long ld, int ncols,
+                                                      float* __restrict__ out, int accumulate) {
+  __shared__ float sh[8][33];
+  const int cl = threadIdx.x & 31, yg = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
+  float s = 0.f;
+  if (c < ncols)
+    for (int y = yg; y < ny; y += 8) s += part[(size_t)y * ld + c];
+  sh[yg][cl] = s;
+  __syncthreads();
+  if (yg == 0 && c < ncols) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += sh[i][cl];
+    out[c] = accumulate ? out[c] + t : t;
+  }
+}
+
 }  // namespace g2

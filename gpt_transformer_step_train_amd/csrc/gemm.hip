@@ -7,14 +7,20 @@
 // run in the GEMM epilogue instead of separate passes over HBM.
 //
 // Design (CDNA4, wave64):
-//  * 128x128 block tile, 4 waves in a 2x2 grid, 64x64 per wave = 2x2 MFMA 32x32 blocks.
-//    bf16: v_mfma_f32_32x32x16_bf16, BK = 64.  fp32: v_mfma_f32_32x32x2f32, BK = 32.
-//  * LDS holds both operands as [row][k] (k contiguous, +16 B pad), so every MFMA operand is one
-//    LDS read per lane. Operands whose memory layout is K-contiguous are copied 16 B at a time;
-//    M/N-contiguous operands (the transposed side of NN / TN products) are loaded as 4 x 16 B
+//  * Two block tiles, both with 4 waves in a 2x2 grid: 256x256 (128x128 per wave = 4x4 MFMA
+//    32x32 blocks, 256 accumulator registers) for the wide products, 128x128 (64x64 per wave)
+//    for N = C products and split-K weight gradients, chosen per shape so the grid covers the
+//    256 CUs in whole rounds. bf16: v_mfma_f32_32x32x16_bf16, BK = 64; fp32:
+//    v_mfma_f32_32x32x2f32, BK = 32.
+//  * LDS holds both operands as [row][k] (k contiguous, +16 B pad: conflict-free 16-byte reads),
+//    so every MFMA operand is one LDS read per lane. K-contiguous operands are copied 16 B at a
+//    time; M/N-contiguous operands (the transposed side of NN / TN products) are loaded as 4 x 16 B
 //    row pieces and transposed in registers on the way into LDS.
 //  * Double-buffered LDS with register staging: the global loads of tile k+1 are in flight while
-//    tile k is multiplied; one barrier per K tile.
+//    tile k is multiplied (64 MFMAs per wave per tile on the 256x256 tile); one barrier per tile.
+//  * Epilogue through LDS: each wave parks 32 rows of fp32 accumulators in LDS and reads them back
+//    row-contiguous, so bias / residual / GELU inputs are read and results written as 16-byte
+//    coalesced vectors.
 //  * Block ids are remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs) gets a
 //    contiguous run of tiles, and tiles are ordered in groups of 8 tile-rows for L2 reuse.
 //  * Split-K (weight gradients, K = B*T) writes fp32 partials that a second kernel sums in a
@@ -48,79 +54,106 @@ template <> struct Mma<float> {
   }
 };
 
-constexpr int BM = 128, BN = 128, NTHR = 256, WGN = 2;
-constexpr int TM = 64, TN = 64, FM = 2, FN = 2;
+#ifndef GEMM_SCHED_HINT
+#define GEMM_SCHED_HINT __builtin_amdgcn_iglp_opt(1)
+#endif
+#ifndef GEMM_FRAG_DB
+#define GEMM_FRAG_DB 1
+#endif
+constexpr int NTHR = 256, WGM = 2, WGN = 2;
 constexpr int GROUP_M = 8;
+constexpr int TKR = 4;  // transposed piece: TKR k-rows x VEC row-contiguous elements
 
-// Transposed piece: TKR k-rows x VEC m-columns per thread.
-constexpr int TKR = 4;
-
-template <typename T> struct Tile {
+template <typename T, int BM_, int BN_> struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int VEC = Elt<T>::VEC;
   static constexpr int BK = Mma<T>::BK;
-  static constexpr int LD = BK + VEC;  // LDS row pitch in elements (16 B pad)
-  // K-contiguous copy: vectors per thread
-  static constexpr int NV_K = (BM * BK / VEC) / NTHR;
-  // transposed copy: pieces per thread
-  static constexpr int NV_T = ((BK / TKR) * (BM / VEC)) / NTHR;
+  static constexpr int LD = BK + VEC;  // LDS row pitch (elements)
+  static constexpr int EPI_LD = TN + 4;  // epilogue staging pitch (floats)
+  static constexpr size_t LDS_BYTES = 2ull * (BM + BN) * LD * sizeof(T);
+  static_assert(LDS_BYTES >= (size_t)4 * 32 * EPI_LD * 4, "epilogue staging must fit");
 };
 
-// Load one operand tile (ROWS=128 rows of the M or N side, BK of K) into registers.
-// kc: operand is K-contiguous (ptr[row*ld + k]) else row-contiguous (ptr[k*ld + row]).
-template <typename T, bool KC> struct Loader {
-  using TL = Tile<T>;
-  static constexpr int VEC = TL::VEC;
-  static constexpr int NREG = KC ? TL::NV_K : TL::NV_T * TKR;
+// One operand tile (ROWS rows of the M or N side, BK of K) staged through registers.
+// KC: operand is K-contiguous (ptr[row*ld + k]) else row-contiguous (ptr[k*ld + row]).
+template <typename T, bool KC, int ROWS> struct Loader {
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int BK = Mma<T>::BK;
+  static constexpr int LD = BK + VEC;
+  static constexpr int NV_K = (ROWS * BK / VEC) / NTHR;           // 16-byte vectors per thread
+  static constexpr int NV_T = ((BK / TKR) * (ROWS / VEC)) / NTHR;  // transposed pieces per thread
+  static constexpr int NREG = KC ? NV_K : NV_T * TKR;
+  static_assert(NREG > 0, "tile too small for the thread count");
   u32x4 r[NREG];
 
-  __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
-    const int tid = threadIdx.x;
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < TL::NV_K; ++i) {
-        const int v = i * NTHR + tid;
-        const int row = v / (TL::BK / VEC);
-        const int kc = (v % (TL::BK / VEC)) * VEC;
-        const int k = k0 + kc;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row0 + row < nrows && k < K) {
-          x = *reinterpret_cast<const u32x4*>(ptr + (size_t)(row0 + row) * ld + k);
-          if (k + VEC > K) mask_tail(x, K - k);
-        }
-        r[i] = x;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < TL::NV_T; ++i) {
-        const int pc = i * NTHR + tid;
-        const int mc = (pc % (BM / VEC)) * VEC;
-        const int kr = (pc / (BM / VEC)) * TKR;
-#pragma unroll
-        for (int j = 0; j < TKR; ++j) {
-          const int k = k0 + kr + j;
-          const int m = row0 + mc;
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (k < K && m < nrows) {
-            x = *reinterpret_cast<const u32x4*>(ptr + (size_t)k * ld + m);
-            if (m + VEC > nrows) mask_tail(x, nrows - m);
-          }
-          r[i * TKR + j] = x;
-        }
-      }
-    }
-  }
-
-  // zero elements [keep, VEC) of a 16-byte vector
-  __device__ __forceinline__ static void mask_tail(u32x4& x, int keep) {
+  // zero the elements [keep, VEC) of a 16-byte vector (keep <= 0: all), branch-free
+  __device__ __forceinline__ static u32x4 keep_first(u32x4 x, int keep) {
+    u32x4 o;
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e >= keep) x[e] = 0u;
+      for (int e = 0; e < 4; ++e) o[e] = e < keep ? x[e] : 0u;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (2 * e >= keep) x[e] = 0u;
-        else if (2 * e + 1 >= keep) x[e] &= 0xffffu;
+        const uint32_t m = 2 * e + 1 < keep ? 0xffffffffu : (2 * e < keep ? 0x0000ffffu : 0u);
+        o[e] = x[e] & m;
+      }
+    }
+    return o;
+  }
+
+  // Interior tiles take straight-line unchecked loads; edge tiles clamp the address to a valid
+  // one and zero the out-of-range elements with selects, so the loads stay in one basic block.
+  __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
+    const int tid = threadIdx.x;
+    const bool interior = row0 + ROWS <= nrows && k0 + BK <= K;
+    if constexpr (KC) {
+      if (interior) {
+#pragma unroll
+        for (int i = 0; i < NV_K; ++i) {
+          const int v = i * NTHR + tid;
+          const int row = v / (BK / VEC);
+          const int kc = (v % (BK / VEC)) * VEC;
+          r[i] = *reinterpret_cast<const u32x4*>(ptr + (size_t)(row0 + row) * ld + k0 + kc);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NV_K; ++i) {
+          const int v = i * NTHR + tid;
+          const int row = v / (BK / VEC);
+          const int k = k0 + (v % (BK / VEC)) * VEC;
+          const bool ok = row0 + row < nrows && k < K;
+          const T* src = ok ? ptr + (size_t)(row0 + row) * ld + k : ptr;
+          r[i] = keep_first(*reinterpret_cast<const u32x4*>(src), ok ? K - k : 0);
+        }
+      }
+    } else {
+      if (interior) {
+#pragma unroll
+        for (int i = 0; i < NV_T; ++i) {
+          const int pc = i * NTHR + tid;
+          const int kr = (pc % (BK / TKR)) * TKR;
+          const int mc = (pc / (BK / TKR)) * VEC;
+#pragma unroll
+          for (int j = 0; j < TKR; ++j)
+            r[i * TKR + j] = *reinterpret_cast<const u32x4*>(ptr + (size_t)(k0 + kr + j) * ld + row0 + mc);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NV_T; ++i) {
+          const int pc = i * NTHR + tid;
+          const int kr = (pc % (BK / TKR)) * TKR;
+          const int m = row0 + (pc / (BK / TKR)) * VEC;
+#pragma unroll
+          for (int j = 0; j < TKR; ++j) {
+            const int k = k0 + kr + j;
+            const bool ok = k < K && m < nrows;
+            const T* src = ok ? ptr + (size_t)k * ld + m : ptr;
+            r[i * TKR + j] = keep_first(*reinterpret_cast<const u32x4*>(src), ok ? nrows - m : 0);
+          }
+        }
       }
     }
   }
@@ -129,25 +162,25 @@ template <typename T, bool KC> struct Loader {
     const int tid = threadIdx.x;
     if constexpr (KC) {
 #pragma unroll
-      for (int i = 0; i < TL::NV_K; ++i) {
+      for (int i = 0; i < NV_K; ++i) {
         const int v = i * NTHR + tid;
-        const int row = v / (TL::BK / VEC);
-        const int kc = (v % (TL::BK / VEC)) * VEC;
-        *reinterpret_cast<u32x4*>(lds + row * TL::LD + kc) = r[i];
+        const int row = v / (BK / VEC);
+        const int kc = (v % (BK / VEC)) * VEC;
+        *reinterpret_cast<u32x4*>(lds + row * LD + kc) = r[i];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < TL::NV_T; ++i) {
+      for (int i = 0; i < NV_T; ++i) {
         const int pc = i * NTHR + tid;
-        const int mc = (pc % (BM / VEC)) * VEC;
-        const int kr = (pc / (BM / VEC)) * TKR;
+        const int kr = (pc % (BK / TKR)) * TKR;
+        const int mc = (pc / (BK / TKR)) * VEC;
         const u32x4* in = &r[i * TKR];
         if constexpr (sizeof(T) == 4) {
           // 4x4 floats: column c of the 4 k-rows becomes one 16-byte LDS row piece
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             u32x4 o = {in[0][c], in[1][c], in[2][c], in[3][c]};
-            *reinterpret_cast<u32x4*>(lds + (mc + c) * TL::LD + kr) = o;
+            *reinterpret_cast<u32x4*>(lds + (mc + c) * LD + kr) = o;
           }
         } else {
           // 4 k-rows x 8 bf16 columns -> 8 LDS rows of 4 bf16 (8 bytes)
@@ -162,7 +195,7 @@ template <typename T, bool KC> struct Loader {
               o[0] = (in[0][d] >> 16) | (in[1][d] & 0xffff0000u);
               o[1] = (in[2][d] >> 16) | (in[3][d] & 0xffff0000u);
             }
-            *reinterpret_cast<u32x2*>(lds + (mc + c) * TL::LD + kr) = o;
+            *reinterpret_cast<u32x2*>(lds + (mc + c) * LD + kr) = o;
           }
         }
       }
@@ -170,53 +203,98 @@ template <typename T, bool KC> struct Loader {
   }
 };
 
+// Apply the epilogue to 8 consecutive columns [col, col+8) of one row and store them.
 template <typename T, int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[FM][FN], int m_base, int n_base) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
-  const T* bias = reinterpret_cast<const T*>(p.bias);
+__device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long ldc, int row, int col,
+                                           const float (&a)[8]) {
+  float o[8];
+  const bool full = col + 8 <= p.N;
+  if constexpr (EPI == EPI_F32) {
+    float* dst = C_f32 + (size_t)row * ldc + col;
+    if (full) {
+      f32x4 v0 = {a[0], a[1], a[2], a[3]}, v1 = {a[4], a[5], a[6], a[7]};
+      if (p.accumulate) {
+        v0 += reinterpret_cast<const f32x4*>(dst)[0];
+        v1 += reinterpret_cast<const f32x4*>(dst)[1];
+      }
+      reinterpret_cast<f32x4*>(dst)[0] = v0;
+      reinterpret_cast<f32x4*>(dst)[1] = v1;
+    } else {
+      for (int e = 0; e < 8 && col + e < p.N; ++e) dst[e] = p.accumulate ? dst[e] + a[e] : a[e];
+    }
+    return;
+  } else {
+    constexpr int VEC = Elt<T>::VEC;
+    const T* bias = reinterpret_cast<const T*>(p.bias);
+    const T* aux = reinterpret_cast<const T*>(p.aux);
+    float bv[8], xv[8];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = n_base + j * 32 + (lane & 31);
-    if (col >= p.N) continue;
-    float bv = 0.f;
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID)
-      if (bias) bv = ld1(bias, col);
+    for (int e = 0; e < 8; ++e) bv[e] = xv[e] = 0.f;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int h = 0; h < 8 / VEC; ++h) {
+        V16<T> t;
+        if ((EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID) && bias) {
+          t.load(bias + col + h * VEC);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m_base + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (row >= p.M) continue;
-        const float a = acc[i][j][r];
-        const size_t idx = (size_t)row * p.ldc + col;
-        if constexpr (EPI == EPI_BIAS) {
-          st1(reinterpret_cast<T*>(p.C), idx, a + bv);
-        } else if constexpr (EPI == EPI_GELU) {
-          const float pre = a + bv;
-          st1(reinterpret_cast<T*>(p.C), idx, pre);
-          st1(reinterpret_cast<T*>(p.C2), idx, gelu_fwd(pre));
-        } else if constexpr (EPI == EPI_RESID) {
-          const float res = ld1(reinterpret_cast<const T*>(p.aux), (size_t)row * p.ldaux + col);
-          st1(reinterpret_cast<T*>(p.C), idx, res + (a + bv));
-        } else if constexpr (EPI == EPI_GELU_BWD) {
-          const float pre = ld1(reinterpret_cast<const T*>(p.aux), (size_t)row * p.ldaux + col);
-          st1(reinterpret_cast<T*>(p.C), idx, a * gelu_bwd(pre));
-        } else {  // EPI_F32 ; split partials use ldc = N and a pre-offset C
-          float* C = reinterpret_cast<float*>(p.C);
-          C[idx] = p.accumulate ? C[idx] + a : a;
+          for (int e = 0; e < VEC; ++e) bv[h * VEC + e] = t.v[e];
         }
+        if (EPI == EPI_RESID || EPI == EPI_GELU_BWD) {
+          t.load(aux + (size_t)row * p.ldaux + col + h * VEC);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xv[h * VEC + e] = t.v[e];
+        }
+      }
+    } else {
+      for (int e = 0; e < 8 && col + e < p.N; ++e) {
+        if ((EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID) && bias) bv[e] = ld1(bias, col + e);
+        if (EPI == EPI_RESID || EPI == EPI_GELU_BWD) xv[e] = ld1(aux, (size_t)row * p.ldaux + col + e);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU) o[e] = a[e] + bv[e];
+      else if constexpr (EPI == EPI_RESID) o[e] = xv[e] + (a[e] + bv[e]);
+      else o[e] = a[e] * gelu_bwd(xv[e]);
+    }
+    T* dst = reinterpret_cast<T*>(p.C) + (size_t)row * ldc + col;
+    if (full) {
+#pragma unroll
+      for (int h = 0; h < 8 / VEC; ++h) {
+        V16<T> t;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t.v[e] = o[h * VEC + e];
+        t.store(dst + h * VEC);
+      }
+      if constexpr (EPI == EPI_GELU) {
+        T* dst2 = reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col;
+#pragma unroll
+        for (int h = 0; h < 8 / VEC; ++h) {
+          V16<T> t;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) t.v[e] = gelu_fwd(o[h * VEC + e]);
+          t.store(dst2 + h * VEC);
+        }
+      }
+    } else {
+      for (int e = 0; e < 8 && col + e < p.N; ++e) {
+        st1(dst, e, o[e]);
+        if constexpr (EPI == EPI_GELU) st1(reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col, e, gelu_fwd(o[e]));
       }
     }
   }
 }
 
-template <typename T, bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs p, int k_split, float* split_out) {
-  using TL = Tile<T>;
+template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, float* split_out) {
+  using CF = Cfg<T, BM, BN>;
   using MM = Mma<T>;
-  __shared__ __attribute__((aligned(16))) T As[2][BM * TL::LD];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN * TL::LD];
+  constexpr int LD = CF::LD, BK = CF::BK, TM = CF::TM, TN = CF::TN, FM = CF::FM, FN = CF::FN;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* As0 = reinterpret_cast<T*>(smem);
+  T* Bs0 = As0 + BM * LD;
+  T* As1 = Bs0 + BN * LD;
+  T* Bs1 = As1 + BM * LD;
 
   // tile mapping: XCD-contiguous runs, then grouped row-major order
   const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
@@ -232,7 +310,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs p, int k_split, 
 
   const int kbeg = blockIdx.z * k_split;
   const int kend = min(p.K, kbeg + k_split);
-  const int nkt = cdiv(kend - kbeg, TL::BK);
+  const int nkt = cdiv(kend - kbeg, BK);
 
   const T* A = reinterpret_cast<const T*>(p.A);
   const T* B = reinterpret_cast<const T*>(p.B);
@@ -250,13 +328,13 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs p, int k_split, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  Loader<T, AKC> la;
-  Loader<T, BKC> lb;
+  Loader<T, AKC, BM> la;
+  Loader<T, BKC, BN> lb;
   if (nkt > 0) {
     la.load(A, p.lda, m0, p.M, kbeg, kend);
     lb.load(B, p.ldb, n0, p.N, kbeg, kend);
-    la.store(As[0]);
-    lb.store(Bs[0]);
+    la.store(As0);
+    lb.store(Bs0);
   }
   __syncthreads();
 
@@ -265,45 +343,97 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs p, int k_split, 
   const int kofs = (lane >> 5) * MM::KPL;
 
   for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
+    const bool odd = kt & 1;
     const bool more = kt + 1 < nkt;
     if (more) {
-      const int k0 = kbeg + (kt + 1) * TL::BK;
+      const int k0 = kbeg + (kt + 1) * BK;
       la.load(A, p.lda, m0, p.M, k0, kend);
       lb.load(B, p.ldb, n0, p.N, k0, kend);
     }
-    const T* as = As[cur];
-    const T* bs = Bs[cur];
+    const T* as = odd ? As1 : As0;
+    const T* bs = odd ? Bs1 : Bs0;
+#if GEMM_FRAG_DB
+    // operand fragments are double-buffered: the LDS reads of k-step s+1 are issued before the
+    // MFMAs of k-step s, so their latency hides behind FM*FN MFMAs
+    constexpr int KS = BK / MM::KSTEP;
+    typename MM::frag fa[2][FM], fb[2][FN];
 #pragma unroll
-    for (int kk = 0; kk < TL::BK; kk += MM::KSTEP) {
+    for (int i = 0; i < FM; ++i) fa[0][i] = MM::load(as + (arow + i * 32) * LD + kofs);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = MM::load(bs + (brow + j * 32) * LD + kofs);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int cb = st & 1, nb = cb ^ 1;
+      if (st + 1 < KS) {
+        const int kk = (st + 1) * MM::KSTEP;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[nb][i] = MM::load(as + (arow + i * 32) * LD + kk + kofs);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[nb][j] = MM::load(bs + (brow + j * 32) * LD + kk + kofs);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[cb][i], fb[cb][j], acc[i][j]);
+    }
+#else
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += MM::KSTEP) {
       typename MM::frag fa[FM], fb[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = MM::load(as + (arow + i * 32) * TL::LD + kk + kofs);
+      for (int i = 0; i < FM; ++i) fa[i] = MM::load(as + (arow + i * 32) * LD + kk + kofs);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = MM::load(bs + (brow + j * 32) * TL::LD + kk + kofs);
+      for (int j = 0; j < FN; ++j) fb[j] = MM::load(bs + (brow + j * 32) * LD + kk + kofs);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
     }
+#endif
+    GEMM_SCHED_HINT;
     if (more) {
-      la.store(As[cur ^ 1]);
-      lb.store(Bs[cur ^ 1]);
+      la.store(odd ? As0 : As1);
+      lb.store(odd ? Bs0 : Bs1);
     }
     __syncthreads();
   }
 
+  // ---- epilogue: 32-row slabs of each wave go through LDS, then 16-byte row chunks out
+  float* C_f32 = reinterpret_cast<float*>(p.C);
+  long ldc = p.ldc;
+  GemmArgs q = p;
   if constexpr (EPI == EPI_F32) {
     if (split_out) {
-      GemmArgs q = p;
-      q.C = split_out + (size_t)blockIdx.z * p.M * p.N;
-      q.ldc = p.N;
+      C_f32 = split_out + (size_t)blockIdx.z * p.M * p.N;
+      ldc = p.N;
       q.accumulate = 0;
-      epilogue<T, EPI>(q, acc, m0 + wm * TM, n0 + wn * TN);
-      return;
     }
   }
-  epilogue<T, EPI>(p, acc, m0 + wm * TM, n0 + wn * TN);
+  float* stage = reinterpret_cast<float*>(smem) + w * 32 * CF::EPI_LD;
+  const int g = lane >> 5, l32 = lane & 31;
+  constexpr int CPR = TN / 8;  // 8-column chunks per staged row
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage[((r >> 2) * 8 + g * 4 + (r & 3)) * CF::EPI_LD + j * 32 + l32] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < (32 * CPR) / 64; ++it) {
+      const int id = it * 64 + lane;
+      const int rr = id / CPR, cc = (id % CPR) * 8;
+      const int row = m0 + wm * TM + i * 32 + rr;
+      const int col = n0 + wn * TN + cc;
+      if (row < p.M && col < p.N) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc + 4);
+        const float a8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // dst[i] (+)= sum_z part[z][i], z in order
@@ -322,36 +452,56 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
   }
 }
 
+constexpr int NCU = 256;
+
+static bool use_big(DType dt, int M, int N) {
+  if (dt != DT_BF16) return false;
+  const long t = (long)cdiv(M, 256) * cdiv(N, 256);
+  return t >= 384;
+}
+
 int gemm_splits(int M, int N, int K, size_t scratch_floats) {
-  const long tiles = (long)cdiv(M, BM) * cdiv(N, BN);
+  const long tiles = (long)cdiv(M, 128) * cdiv(N, 128);
   int s = 1;
-  // aim for >= ~2 waves of 256 CUs x 2 blocks; each split keeps >= 1024 of K
-  while (tiles * s < 1024 && K / (s * 2) >= 1024 && (size_t)(s * 2) * M * N <= scratch_floats) s *= 2;
+  // grow until the grid covers >= 2 rounds of the CUs; each split keeps >= 1024 of K
+  while (tiles * s < 2 * NCU && K / (s * 2) >= 1024 && (size_t)(s * 2) * M * N <= scratch_floats) s *= 2;
   return s;
 }
 
-template <typename T, bool AKC, bool BKC>
+template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
+static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, hipStream_t s) {
+  using CF = Cfg<T, BM, BN>;
+  static bool attr = false;
+  auto kern = gemm_kernel<T, BM, BN, AKC, BKC, EPI>;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)CF::LDS_BYTES);
+    attr = true;
+  }
+  kern<<<grid, NTHR, CF::LDS_BYTES, s>>>(a, k_split, split);
+}
+
+template <typename T, int BM, int BN, bool AKC, bool BKC>
 static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t scratch_floats, hipStream_t s) {
   const int tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
   int splits = 1;
   if (epi == EPI_F32 && scratch) splits = gemm_splits(a.M, a.N, a.K, scratch_floats);
   int k_split = a.K;
   if (splits > 1) {
-    k_split = cdiv(cdiv(a.K, splits), Tile<T>::BK) * Tile<T>::BK;
+    k_split = cdiv(cdiv(a.K, splits), Mma<T>::BK) * Mma<T>::BK;
     splits = cdiv(a.K, k_split);
   }
   dim3 grid(tiles, 1, splits);
   switch (epi) {
-    case EPI_BIAS: gemm_kernel<T, AKC, BKC, EPI_BIAS><<<grid, NTHR, 0, s>>>(a, k_split, nullptr); break;
-    case EPI_GELU: gemm_kernel<T, AKC, BKC, EPI_GELU><<<grid, NTHR, 0, s>>>(a, k_split, nullptr); break;
-    case EPI_RESID: gemm_kernel<T, AKC, BKC, EPI_RESID><<<grid, NTHR, 0, s>>>(a, k_split, nullptr); break;
-    case EPI_GELU_BWD: gemm_kernel<T, AKC, BKC, EPI_GELU_BWD><<<grid, NTHR, 0, s>>>(a, k_split, nullptr); break;
+    case EPI_BIAS: launch_cfg<T, BM, BN, AKC, BKC, EPI_BIAS>(grid, a, k_split, nullptr, s); break;
+    case EPI_GELU: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU>(grid, a, k_split, nullptr, s); break;
+    case EPI_RESID: launch_cfg<T, BM, BN, AKC, BKC, EPI_RESID>(grid, a, k_split, nullptr, s); break;
+    case EPI_GELU_BWD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_BWD>(grid, a, k_split, nullptr, s); break;
     case EPI_F32:
-      gemm_kernel<T, AKC, BKC, EPI_F32><<<grid, NTHR, 0, s>>>(a, k_split, splits > 1 ? scratch : nullptr);
+      launch_cfg<T, BM, BN, AKC, BKC, EPI_F32>(grid, a, k_split, splits > 1 ? scratch : nullptr, s);
       if (splits > 1) {
         const size_t n = (size_t)a.M * a.N;
         const int blocks = (int)std::min<size_t>(4096, (n / 4 + 255) / 256 + 1);
-        // C must be dense (ldc == N) for the reduction
         splitk_reduce<<<blocks, 256, 0, s>>>(scratch, splits, n, reinterpret_cast<float*>(a.C), a.accumulate);
       }
       break;
@@ -359,62 +509,93 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
   return hipGetLastError();
 }
 
+template <typename T, bool AKC, bool BKC>
+static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
+  // split-K weight gradients stay on the 128x128 tile (their M x N is small)
+  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.M, a.N))
+    return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
+  if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.M, a.N))
+    return launch_t<T, 256, 256, AKC, BKC>(epi, a, nullptr, 0, s);
+  return launch_t<T, 128, 128, AKC, BKC>(epi, a, scratch, sf, s);
+}
+
 hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& a, float* scratch,
                        size_t scratch_floats, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (epi == EPI_F32 && scratch && a.ldc != a.N) scratch = nullptr;
   if (dt == DT_BF16) {
-    if (a_kc && b_kc) return launch_t<bf16, true, true>(epi, a, scratch, scratch_floats, s);
-    if (a_kc && !b_kc) return launch_t<bf16, true, false>(epi, a, scratch, scratch_floats, s);
-    if (!a_kc && !b_kc) return launch_t<bf16, false, false>(epi, a, scratch, scratch_floats, s);
-    return launch_t<bf16, false, true>(epi, a, scratch, scratch_floats, s);
+    if (a_kc && b_kc) return launch_sel<bf16, true, true>(epi, a, scratch, scratch_floats, s);
+    if (a_kc && !b_kc) return launch_sel<bf16, true, false>(epi, a, scratch, scratch_floats, s);
+    if (!a_kc && !b_kc) return launch_sel<bf16, false, false>(epi, a, scratch, scratch_floats, s);
+    return launch_sel<bf16, false, true>(epi, a, scratch, scratch_floats, s);
   }
-  if (a_kc && b_kc) return launch_t<float, true, true>(epi, a, scratch, scratch_floats, s);
-  if (a_kc && !b_kc) return launch_t<float, true, false>(epi, a, scratch, scratch_floats, s);
-  if (!a_kc && !b_kc) return launch_t<float, false, false>(epi, a, scratch, scratch_floats, s);
-  return launch_t<float, false, true>(epi, a, scratch, scratch_floats, s);
+  if (a_kc && b_kc) return launch_t<float, 128, 128, true, true>(epi, a, scratch, scratch_floats, s);
+  if (a_kc && !b_kc) return launch_t<float, 128, 128, true, false>(epi, a, scratch, scratch_floats, s);
+  if (!a_kc && !b_kc) return launch_t<float, 128, 128, false, false>(epi, a, scratch, scratch_floats, s);
+  return launch_t<float, 128, 128, false, true>(epi, a, scratch, scratch_floats, s);
 }
 
 // ----------------------------------------------------------------------------------------
-// Column sums (bias gradients): partial[y][n] = sum over rows of chunk y; then db (+)= sum_y.
+// Column sums (bias gradients): partial[y][n] over a chunk of rows, 16-byte loads, then a
+// fixed-order sum over the chunks. Block: 32 column vectors x 8 row groups.
 // ----------------------------------------------------------------------------------------
+constexpr int CS_ROWS = 128;  // rows per partial
+
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_partial(const T* __restrict__ x, long ld, int M, int N, int rows_per,
+__global__ __launch_bounds__(256) void colsum_partial(const T* __restrict__ x, long ld, int M, int N,
                                                       float* __restrict__ partial) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= N) return;
-  const int r0 = blockIdx.y * rows_per;
-  const int r1 = min(M, r0 + rows_per);
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += ld1(x, (size_t)r * ld + col);
-  partial[(size_t)blockIdx.y * N + col] = s;
+  constexpr int VEC = Elt<T>::VEC;
+  __shared__ float sh[8][32 * VEC + 1];
+  const int cv = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int col = (blockIdx.x * 32 + cv) * VEC;
+  const int r0 = blockIdx.y * CS_ROWS;
+  float s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+  if (col < N) {
+    const int r1 = min(M, r0 + CS_ROWS);
+#pragma unroll 4
+    for (int r = r0 + rg; r < r1; r += 8) {
+      V16<T> v;
+      v.load(x + (size_t)r * ld + col);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s[e] += v.v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) sh[rg][cv * VEC + e] = s[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < 32 * VEC; c += 256) {
+    const int gc = blockIdx.x * 32 * VEC + c;
+    if (gc < N) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t += sh[i][c];
+      partial[(size_t)blockIdx.y * N + gc] = t;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void colsum_finish(const float* __restrict__ partial, int ny, int N,
                                                      float* __restrict__ out, int accumulate) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= N) return;
-  float s = 0.f;
-  for (int y = 0; y < ny; ++y) s += partial[(size_t)y * N + col];
-  out[col] = accumulate ? out[col] + s : s;
+  reduce_partials_block(partial, ny, N, N, out, accumulate);
 }
 
 hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float* db, int accumulate,
                          float* partial, size_t partial_floats, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  int ny = std::max(1, std::min(cdiv(M, 64), 256));
-  while ((size_t)ny * N > partial_floats && ny > 1) ny /= 2;
-  const int rows_per = cdiv(M, ny);
-  ny = cdiv(M, rows_per);
-  if (M <= 0) ny = 0;
-  dim3 grid(cdiv(N, 256), std::max(ny, 1));
-  if (ny > 0) {
+  const int ny = std::max(1, cdiv(M, CS_ROWS));
+  if ((size_t)ny * N > partial_floats) return hipErrorInvalidValue;
+  const int vec = dt == DT_BF16 ? 8 : 4;
+  if (N % vec || ld % vec) return hipErrorInvalidValue;
+  dim3 grid(cdiv(N / vec, 32), ny);
+  if (M > 0) {
     if (dt == DT_BF16)
-      colsum_partial<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(dY), ld, M, N, rows_per, partial);
+      colsum_partial<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(dY), ld, M, N, partial);
     else
-      colsum_partial<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(dY), ld, M, N, rows_per, partial);
+      colsum_partial<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(dY), ld, M, N, partial);
   }
-  colsum_finish<<<cdiv(N, 256), 256, 0, s>>>(partial, ny, N, db, accumulate);
+  colsum_finish<<<cdiv(N, 32), 256, 0, s>>>(partial, M > 0 ? ny : 0, N, db, accumulate);
   return hipGetLastError();
 }
 

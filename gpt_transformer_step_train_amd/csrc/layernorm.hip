@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
   }
 }
 
-constexpr int LNB_BLOCKS = 256;
+constexpr int LNB_BLOCKS = 1024;
 
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_per_block,
@@ -157,16 +157,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_p
   }
 }
 
+// grid (cdiv(C, 32), 2): y = 0 -> dw, y = 1 -> db
 __global__ __launch_bounds__(256) void ln_bwd_finish(const float* __restrict__ partial, int nblocks, int C,
                                                      float* __restrict__ dw, float* __restrict__ db,
                                                      int accumulate) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= 2 * C) return;
-  float s = 0.f;
-  for (int bk = 0; bk < nblocks; ++bk) s += partial[(size_t)bk * 2 * C + c];
-  float* out = c < C ? dw + c : (db ? db + (c - C) : nullptr);
+  float* out = blockIdx.y == 0 ? dw : db;
   if (!out) return;
-  *out = accumulate ? *out + s : s;
+  reduce_partials_block(partial + (size_t)blockIdx.y * C, nblocks, 2L * C, C, out, accumulate);
 }
 
 size_t layernorm_bwd_partial_floats(int rows, int C) { return (size_t)LNB_BLOCKS * 2 * C; }
@@ -216,7 +213,7 @@ static hipError_t ln_bwd_t(int rows, int C, const void* dy, const void* x, const
     else if (nv <= 8) ln_bwd_kernel<T, 8><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, partial);
     else return hipErrorInvalidValue;
   }
-  ln_bwd_finish<<<cdiv(2 * C, 256), 256, 0, s>>>(partial, nb, C, dw, db, accumulate);
+  ln_bwd_finish<<<dim3(cdiv(C, 32), 2), 256, 0, s>>>(partial, nb, C, dw, db, accumulate);
   return hipGetLastError();
 }
 

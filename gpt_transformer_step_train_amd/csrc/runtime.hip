@@ -75,6 +75,9 @@ struct Model {
   bool fwd_targets = false; // last forward had targets and its backward has not run yet
   bool fwd_logits = false;  // last forward had no targets: logits are readable
   hipStream_t stream = nullptr;
+  // side stream: the (token, position) sort for the embedding gradient overlaps the forward
+  hipStream_t side = nullptr;
+  hipEvent_t ev_tokens = nullptr, ev_sorted = nullptr;
 };
 
 Model g;
@@ -269,6 +272,39 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
 }
 
 
+
+// ------------------------------------------------------------------ per-class kernel timing
+// HIP events recorded on the model's stream around every launch of an enabled class.
+struct Prof {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::pair<int, int>> recs;  // (class, first event index)
+  int used = 0;
+};
+Prof prof;
+
+struct ProfScope {
+  int cls, idx = -1;
+  explicit ProfScope(int c) : cls(c) {
+    if (!(prof.mask >> c & 1u)) return;
+    if (prof.used + 2 > (int)prof.pool.size()) {
+      for (int i = 0; i < 512; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        prof.pool.push_back(e);
+      }
+    }
+    idx = prof.used;
+    prof.used += 2;
+    (void)hipEventRecord(prof.pool[idx], g.stream);
+  }
+  ~ProfScope() {
+    if (idx < 0) return;
+    (void)hipEventRecord(prof.pool[idx + 1], g.stream);
+    prof.recs.push_back({cls, idx});
+  }
+};
+
 // weight pointer in the compute dtype (bf16 shadow or fp32 master)
 const void* W(size_t off) {
   if (off == NONE) return nullptr;
@@ -312,29 +348,68 @@ int forward_impl(const int32_t* tokens, const int32_t* targets) {
   const size_t es = g.es;
   hipStream_t s = g.stream;
   set_scalars_kernel<<<1, 1, 0, s>>>(g.err_dev);
-  HIPCHK(launch_encoder_fwd(g.dt, g.B, g.T, C, g.V, tokens, W(g.o_wte), W(g.o_wpe), g.encoded, g.err_dev, s));
-  if (targets) HIPCHK(launch_encoder_sort(BT, g.V, tokens, g.keys, s));
+  {
+      ProfScope ps_(GPT2_K_ENCODER_FWD);
+      HIPCHK(launch_encoder_fwd(g.dt, g.B, g.T, C, g.V, tokens, W(g.o_wte), W(g.o_wpe), g.encoded, g.err_dev, s));
+    }
+  if (targets) {
+    HIPCHK(hipEventRecord(g.ev_tokens, s));
+    HIPCHK(hipStreamWaitEvent(g.side, g.ev_tokens, 0));
+    HIPCHK(launch_encoder_sort(BT, g.V, tokens, g.keys, g.side));
+    HIPCHK(hipEventRecord(g.ev_sorted, g.side));
+  }
   const char* x = g.encoded;
   for (int l = 0; l < L; ++l) {
     const LayerOff& o = g.lo[l];
     LayerAct& a = g.la[l];
-    HIPCHK(launch_layernorm_fwd(g.dt, BT, C, x, W(o.ln1w), W(o.ln1b), a.ln1, a.ln1_mean, a.ln1_rstd, s));
-    RUN(gemm(true, true, EPI_BIAS, BT, 3 * C, C, a.ln1, C, W(o.qkvw), C, a.qkv, 3 * C, W(o.qkvb)));
-    HIPCHK(launch_attention_fwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, a.lse, s));
-    RUN(gemm(true, true, EPI_RESID, BT, C, C, a.atty, C, W(o.attprojw), C, a.res1, C, W(o.attprojb), x, C));
-    HIPCHK(launch_layernorm_fwd(g.dt, BT, C, a.res1, W(o.ln2w), W(o.ln2b), a.ln2, a.ln2_mean, a.ln2_rstd, s));
-    RUN(gemm(true, true, EPI_GELU, BT, 4 * C, C, a.ln2, C, W(o.fcw), C, a.fch, 4 * C, W(o.fcb), nullptr, 0, a.fchg));
-    RUN(gemm(true, true, EPI_RESID, BT, C, 4 * C, a.fchg, 4 * C, W(o.fcprojw), 4 * C, a.res2, C, W(o.fcprojb),
+    {
+      ProfScope ps_(GPT2_K_LAYERNORM_FWD);
+      HIPCHK(launch_layernorm_fwd(g.dt, BT, C, x, W(o.ln1w), W(o.ln1b), a.ln1, a.ln1_mean, a.ln1_rstd, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_QKV);
+      RUN(gemm(true, true, EPI_BIAS, BT, 3 * C, C, a.ln1, C, W(o.qkvw), C, a.qkv, 3 * C, W(o.qkvb)));
+    }
+    {
+      ProfScope ps_(GPT2_K_ATTENTION_FWD);
+      HIPCHK(launch_attention_fwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, a.lse, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_ATTPROJ);
+      RUN(gemm(true, true, EPI_RESID, BT, C, C, a.atty, C, W(o.attprojw), C, a.res1, C, W(o.attprojb), x, C));
+    }
+    {
+      ProfScope ps_(GPT2_K_LAYERNORM_FWD);
+      HIPCHK(launch_layernorm_fwd(g.dt, BT, C, a.res1, W(o.ln2w), W(o.ln2b), a.ln2, a.ln2_mean, a.ln2_rstd, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_FC);
+      RUN(gemm(true, true, EPI_GELU, BT, 4 * C, C, a.ln2, C, W(o.fcw), C, a.fch, 4 * C, W(o.fcb), nullptr, 0, a.fchg));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_FCPROJ);
+      RUN(gemm(true, true, EPI_RESID, BT, C, 4 * C, a.fchg, 4 * C, W(o.fcprojw), 4 * C, a.res2, C, W(o.fcprojb),
              a.res1, C));
+    }
     x = a.res2;
   }
-  HIPCHK(launch_layernorm_fwd(g.dt, BT, C, x, W(g.o_lnfw), W(g.o_lnfb), g.lnf, g.lnf_mean, g.lnf_rstd, s));
-  RUN(gemm(true, true, EPI_BIAS, BT, g.Vp, C, g.lnf, C, W(g.o_wte), C, g.logits, g.ldl));
+  {
+      ProfScope ps_(GPT2_K_LAYERNORM_FWD);
+      HIPCHK(launch_layernorm_fwd(g.dt, BT, C, x, W(g.o_lnfw), W(g.o_lnfb), g.lnf, g.lnf_mean, g.lnf_rstd, s));
+    }
+  {
+      ProfScope ps_(GPT2_K_GEMM_CLASSIFIER);
+      RUN(gemm(true, true, EPI_BIAS, BT, g.Vp, C, g.lnf, C, W(g.o_wte), C, g.logits, g.ldl));
+    }
   if (targets) {
     HIPCHK(launch_count_targets(targets, BT, g.V, g.cfg.grad_accum, g.dloss_dev, g.nvalid_dev, g.err_dev, s));
-    HIPCHK(launch_cross_entropy(g.dt, BT, g.V, g.ldl, g.logits, targets, g.dloss_dev, g.losses, s));
+    {
+      ProfScope ps_(GPT2_K_CROSS_ENTROPY);
+      HIPCHK(launch_cross_entropy(g.dt, BT, g.V, g.ldl, g.logits, targets, g.dloss_dev, g.losses, s));
+    }
     HIPCHK(launch_loss_mean(g.losses, BT, g.nvalid_dev, g.loss_dev, s));
     HIPCHK(hipMemcpyAsync(g.pinned, g.loss_dev, 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamWaitEvent(s, g.ev_sorted, 0));  // tokens are no longer read after this call
   }
   HIPCHK(hipMemcpyAsync(g.pinned + 1, g.err_dev, 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
@@ -350,44 +425,102 @@ int backward_impl() {
   float* sc = g.scratch;
   const size_t sf = g.scratch_floats;
   // classifier (tied wte): dz = dlogits wte ; dwte (+)= dlogits^T z
-  RUN(gemm(true, false, EPI_BIAS, BT, C, g.Vp, g.logits, g.ldl, W(g.o_wte), C, g.dbuf2, C));
-  RUN(gemm(false, false, EPI_F32, g.Vp, C, BT, g.logits, g.ldl, g.lnf, C, G(g.o_wte), C, nullptr, nullptr, 0,
+  {
+      ProfScope ps_(GPT2_K_GEMM_CLASSIFIER_DX);
+      RUN(gemm(true, false, EPI_BIAS, BT, C, g.Vp, g.logits, g.ldl, W(g.o_wte), C, g.dbuf2, C));
+    }
+  {
+      ProfScope ps_(GPT2_K_GEMM_CLASSIFIER_DW);
+      RUN(gemm(false, false, EPI_F32, g.Vp, C, BT, g.logits, g.ldl, g.lnf, C, G(g.o_wte), C, nullptr, nullptr, 0,
            nullptr, acc, true));
+    }
   const char* xlast = L > 0 ? g.la[L - 1].res2 : g.encoded;
-  HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xlast, W(g.o_lnfw), g.lnf_mean, g.lnf_rstd, g.dres, 0,
+  {
+      ProfScope ps_(GPT2_K_LAYERNORM_BWD);
+      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xlast, W(g.o_lnfw), g.lnf_mean, g.lnf_rstd, g.dres, 0,
                               G(g.o_lnfw), G(g.o_lnfb), acc, sc, sf, s));
+    }
   for (int l = L - 1; l >= 0; --l) {
     const LayerOff& o = g.lo[l];
     LayerAct& a = g.la[l];
     const char* xin = l > 0 ? g.la[l - 1].res2 : g.encoded;
     // fcproj: res2 = res1 + gelu(fch) Wfcproj^T + b
-    RUN(gemm(true, false, EPI_GELU_BWD, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr,
+    {
+      ProfScope ps_(GPT2_K_GEMM_FCPROJ_DX);
+      RUN(gemm(true, false, EPI_GELU_BWD, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr,
              a.fch, 4 * C));
-    RUN(gemm(false, false, EPI_F32, C, 4 * C, BT, g.dres, C, a.fchg, 4 * C, G(o.fcprojw), 4 * C, nullptr, nullptr,
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_FCPROJ_DW);
+      RUN(gemm(false, false, EPI_F32, C, 4 * C, BT, g.dres, C, a.fchg, 4 * C, G(o.fcprojw), 4 * C, nullptr, nullptr,
              0, nullptr, acc, true));
-    if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.fcprojb), acc, sc, sf, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_BIAS_GRAD);
+      if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.fcprojb), acc, sc, sf, s));
+    }
     // fc: fch = ln2 Wfc^T + b
-    RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
-    RUN(gemm(false, false, EPI_F32, 4 * C, C, BT, g.dbuf1, 4 * C, a.ln2, C, G(o.fcw), C, nullptr, nullptr, 0,
+    {
+      ProfScope ps_(GPT2_K_GEMM_FC_DX);
+      RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_FC_DW);
+      RUN(gemm(false, false, EPI_F32, 4 * C, C, BT, g.dbuf1, 4 * C, a.ln2, C, G(o.fcw), C, nullptr, nullptr, 0,
              nullptr, acc, true));
-    if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 4 * C, BT, 4 * C, G(o.fcb), acc, sc, sf, s));
-    HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, a.res1, W(o.ln2w), a.ln2_mean, a.ln2_rstd, g.dres, 1,
+    }
+    {
+      ProfScope ps_(GPT2_K_BIAS_GRAD);
+      if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 4 * C, BT, 4 * C, G(o.fcb), acc, sc, sf, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_LAYERNORM_BWD);
+      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, a.res1, W(o.ln2w), a.ln2_mean, a.ln2_rstd, g.dres, 1,
                                 G(o.ln2w), G(o.ln2b), acc, sc, sf, s));
+    }
     // attproj: res1 = xin + atty Wproj^T + b
-    RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
-    RUN(gemm(false, false, EPI_F32, C, C, BT, g.dres, C, a.atty, C, G(o.attprojw), C, nullptr, nullptr, 0, nullptr,
+    {
+      ProfScope ps_(GPT2_K_GEMM_ATTPROJ_DX);
+      RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_ATTPROJ_DW);
+      RUN(gemm(false, false, EPI_F32, C, C, BT, g.dres, C, a.atty, C, G(o.attprojw), C, nullptr, nullptr, 0, nullptr,
              acc, true));
-    if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.attprojb), acc, sc, sf, s));
-    HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_BIAS_GRAD);
+      if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.attprojb), acc, sc, sf, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_ATTENTION_BWD);
+      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec, s));
+    }
     // qkv = ln1 Wqkv^T + b
-    RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
-    RUN(gemm(false, false, EPI_F32, 3 * C, C, BT, g.dbuf1, 3 * C, a.ln1, C, G(o.qkvw), C, nullptr, nullptr, 0,
+    {
+      ProfScope ps_(GPT2_K_GEMM_QKV_DX);
+      RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
+    }
+    {
+      ProfScope ps_(GPT2_K_GEMM_QKV_DW);
+      RUN(gemm(false, false, EPI_F32, 3 * C, C, BT, g.dbuf1, 3 * C, a.ln1, C, G(o.qkvw), C, nullptr, nullptr, 0,
              nullptr, acc, true));
-    if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
-    HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, g.dres, 1, G(o.ln1w),
+    }
+    {
+      ProfScope ps_(GPT2_K_BIAS_GRAD);
+      if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_LAYERNORM_BWD);
+      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, g.dres, 1, G(o.ln1w),
                                 G(o.ln1b), acc, sc, sf, s));
+    }
   }
-  HIPCHK(launch_encoder_bwd(g.dt, g.B, g.T, g.maxT, C, g.keys, g.dres, G(g.o_wte), G(g.o_wpe), acc, sc, sf, s));
+  HIPCHK(hipStreamWaitEvent(s, g.ev_sorted, 0));
+  {
+      ProfScope ps_(GPT2_K_ENCODER_BWD);
+      HIPCHK(launch_encoder_bwd(g.dt, g.B, g.T, g.maxT, C, g.keys, g.dres, G(g.o_wte), G(g.o_wpe), acc, sc, sf, s));
+    }
   return GPT2_OK;
 }
 
@@ -411,7 +544,12 @@ uint64_t gpt2_workspace_bytes(const gpt2_config* cfg) {
 }
 
 void gpt2_free(void) {
+  if (g.stream) (void)hipStreamSynchronize(g.stream);
+  if (g.side) (void)hipStreamSynchronize(g.side);
   if (g.pinned) (void)hipHostFree(g.pinned);
+  if (g.ev_tokens) (void)hipEventDestroy(g.ev_tokens);
+  if (g.ev_sorted) (void)hipEventDestroy(g.ev_sorted);
+  if (g.side) (void)hipStreamDestroy(g.side);
   g = Model();
 }
 
@@ -441,6 +579,9 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed) {
   plan(cfg, &g, reinterpret_cast<char*>(cfg->workspace));
   g.stream = reinterpret_cast<hipStream_t>(cfg->stream);
   HIPCHK(hipHostMalloc((void**)&g.pinned, 16, hipHostMallocDefault));
+  HIPCHK(hipStreamCreateWithFlags(&g.side, hipStreamNonBlocking));
+  HIPCHK(hipEventCreateWithFlags(&g.ev_tokens, hipEventDisableTiming));
+  HIPCHK(hipEventCreateWithFlags(&g.ev_sorted, hipEventDisableTiming));
   HIPCHK(hipMemcpyAsync(g.items, g.items_host.data(), g.items_host.size() * sizeof(WorkItem), hipMemcpyHostToDevice,
                         g.stream));
   HIPCHK(launch_init_params(g.items, (int)g.items_host.size(), g.params, seed, 0.02, g.stream));
@@ -490,7 +631,10 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
   if (t < 1) return fail(GPT2_EINVAL, "t must be >= 1");
   if (g.micro == 0) return fail(GPT2_ESTATE, "gpt2_adamw_step needs at least one gpt2_backward since the last update");
   hipStream_t s = g.stream;
-  HIPCHK(launch_sumsq_partial(g.grads, g.N, g.norm_partial, NORM_PARTS, s));
+  {
+      ProfScope ps_(GPT2_K_GRAD_NORM);
+      HIPCHK(launch_sumsq_partial(g.grads, g.N, g.norm_partial, NORM_PARTS, s));
+    }
   HIPCHK(launch_grad_norm_finish(g.norm_partial, NORM_PARTS, g.norm2, g.clip_scale, g.cfg.grad_clip, s));
   AdamArgs a;
   a.lr = lr;
@@ -501,8 +645,11 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
   a.bc1 = (float)(1.0 / (1.0 - pow((double)b1, (double)t)));
   a.bc2 = (float)(1.0 / (1.0 - pow((double)b2, (double)t)));
   a.clip = g.cfg.grad_clip;
-  HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale, g.norm2,
+  {
+      ProfScope ps_(GPT2_K_ADAMW);
+      HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale, g.norm2,
                       a, s));
+    }
   g.micro = 0;
   return ok();
 }
@@ -518,6 +665,37 @@ float gpt2_grad_norm(void) {
   }
   ok();
   return (float)sqrt(n2);
+}
+
+
+int gpt2_profile_enable(uint32_t mask) {
+  RUN(check_ready());
+  HIPCHK(hipStreamSynchronize(g.stream));
+  prof.mask = mask;
+  prof.recs.clear();
+  prof.used = 0;
+  return ok();
+}
+
+int gpt2_profile_read(float* ms, int32_t* launches, int32_t n) {
+  RUN(check_ready());
+  if (!ms || !launches || n < 0) return fail(GPT2_EINVAL, "null output");
+  HIPCHK(hipStreamSynchronize(g.stream));
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.f;
+    launches[i] = 0;
+  }
+  for (auto& r : prof.recs) {
+    float t = 0.f;
+    HIPCHK(hipEventElapsedTime(&t, prof.pool[r.second], prof.pool[r.second + 1]));
+    if (r.first < n) {
+      ms[r.first] += t;
+      launches[r.first] += 1;
+    }
+  }
+  prof.recs.clear();
+  prof.used = 0;
+  return ok();
 }
 
 int gpt2_last_status(void) { return g_status; }

@@ -98,8 +98,42 @@ int gpt2_get_params(float* dst, uint64_t n);      /* fp32 master, layout order *
 int gpt2_set_params(const float* src, uint64_t n); /* also refreshes the bf16 copy */
 int gpt2_get_grads(float* dst, uint64_t n);
 int gpt2_get_adam_state(float* m, float* v, uint64_t n);
-/* Logits of the last forward, [B*T, V] as float (real vocabulary only). Valid until backward. */
+/* Logits [B*T, V] as float (real vocabulary only) of the last gpt2_forward, which must have had
+ * targets == NULL (with targets the logit buffer is overwritten by its gradient). */
 int gpt2_get_logits(float* dst, uint64_t n);
+/* Kernel timing (diagnostics). Each enabled class gets a pair of HIP events recorded on
+ * cfg.stream around every launch of that class; gpt2_profile_read synchronises the stream and
+ * returns, per class, the summed milliseconds and the number of launches since the last
+ * enable/read. mask = 0 turns timing off. Classes (bit index): */
+#define GPT2_K_ENCODER_FWD 0
+#define GPT2_K_LAYERNORM_FWD 1
+#define GPT2_K_GEMM_QKV 2           /* [BT,C] x [3C,C]^T + bias              */
+#define GPT2_K_ATTENTION_FWD 3
+#define GPT2_K_GEMM_ATTPROJ 4       /* [BT,C] x [C,C]^T + bias + residual    */
+#define GPT2_K_GEMM_FC 5            /* [BT,C] x [4C,C]^T + bias, GELU        */
+#define GPT2_K_GEMM_FCPROJ 6        /* [BT,4C] x [C,4C]^T + bias + residual  */
+#define GPT2_K_GEMM_CLASSIFIER 7    /* [BT,C] x [Vp,C]^T                     */
+#define GPT2_K_CROSS_ENTROPY 8
+#define GPT2_K_GEMM_CLASSIFIER_DX 9
+#define GPT2_K_GEMM_CLASSIFIER_DW 10
+#define GPT2_K_LAYERNORM_BWD 11
+#define GPT2_K_GEMM_FCPROJ_DX 12
+#define GPT2_K_GEMM_FCPROJ_DW 13
+#define GPT2_K_BIAS_GRAD 14
+#define GPT2_K_GEMM_FC_DX 15
+#define GPT2_K_GEMM_FC_DW 16
+#define GPT2_K_GEMM_ATTPROJ_DX 17
+#define GPT2_K_GEMM_ATTPROJ_DW 18
+#define GPT2_K_ATTENTION_BWD 19
+#define GPT2_K_GEMM_QKV_DX 20
+#define GPT2_K_GEMM_QKV_DW 21
+#define GPT2_K_ENCODER_BWD 22
+#define GPT2_K_GRAD_NORM 23
+#define GPT2_K_ADAMW 24
+#define GPT2_K_COUNT 25
+int gpt2_profile_enable(uint32_t mask);
+int gpt2_profile_read(float* ms, int32_t* launches, int32_t n);
+
 void gpt2_free(void);
 
 #ifdef __cplusplus

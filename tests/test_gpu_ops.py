@@ -88,6 +88,45 @@ def test_gemm_layouts_bias(dt, akc, bkc, shape):
     assert rel(h64(Cd)[:, :N], ref) <= tol(dt)
 
 
+BIG_CASES = [((1, 1), bd.EPI_BIAS), ((1, 0), bd.EPI_BIAS), ((0, 0), bd.EPI_BIAS), ((0, 1), bd.EPI_BIAS),
+             ((1, 1), bd.EPI_GELU), ((1, 1), bd.EPI_RESID), ((1, 0), bd.EPI_GELU_BWD), ((0, 0), bd.EPI_F32)]
+
+
+@pytest.mark.parametrize("layout,epi", BIG_CASES)
+def test_gemm_bf16_256_tile_path(layout, epi):
+    """Shapes with >= 384 tiles of 256 x 256 take the large-tile kernel; ragged M and N."""
+    akc, bkc = layout
+    M, N, K = 4100, 6392, 72
+    rng = np.random.default_rng(epi * 10 + akc * 2 + bkc)
+    A, Bm = rng.normal(0, 1, (M, K)), rng.normal(0, 1, (N, K))
+    bias = rng.normal(0, 1, N)
+    aux = rng.normal(0, 1, (M, N))
+    dt = bd.GPT2_BF16
+    lda = K if akc else -(-M // 8) * 8
+    ldb = K if bkc else N
+    As = A if akc else np.zeros((K, lda))
+    if not akc:
+        As[:, :M] = A.T
+    Bs = Bm if bkc else np.ascontiguousarray(Bm.T)
+    Ad, Bd, bd_, auxd = dev(As, dt), dev(Bs, dt), dev(bias, dt), dev(aux, dt)
+    out_dt = torch.float32 if epi == bd.EPI_F32 else torch.bfloat16
+    Cd = torch.zeros((M, N), dtype=out_dt, device="cuda")
+    C2 = torch.zeros((M, N), dtype=out_dt, device="cuda")
+    rc = bd.load().gpt2op_gemm(dt, akc, bkc, epi, M, N, K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Cd.data_ptr(), N,
+                               bd_.data_ptr(), auxd.data_ptr(), N, C2.data_ptr(), 0, None, 0, stream())
+    assert rc == 0, bd.last_error()
+    torch.cuda.synchronize()
+    a64 = h64(Ad) if akc else h64(Ad)[:, :M].T
+    b64 = h64(Bd) if bkc else h64(Bd).T
+    acc = O.matmul_nt(a64, b64)
+    b = h64(bd_)
+    want = {bd.EPI_BIAS: acc + b, bd.EPI_GELU: acc + b, bd.EPI_RESID: h64(auxd) + acc + b,
+            bd.EPI_GELU_BWD: acc * O.gelu_grad(h64(auxd)), bd.EPI_F32: acc}[epi]
+    assert rel(h64(Cd), want) <= (2e-5 if epi == bd.EPI_F32 else 8e-3)
+    if epi == bd.EPI_GELU:
+        assert rel(h64(C2), O.gelu(acc + b)) <= 8e-3
+
+
 @pytest.mark.parametrize("dt", DTS)
 def test_gemm_gelu_resid_and_gelu_backward_epilogues(dt):
     M, N, K = 160, 200, 96
