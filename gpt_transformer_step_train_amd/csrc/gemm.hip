@@ -460,13 +460,21 @@ static bool use_big(DType dt, int M, int N) {
   return t >= 384;
 }
 
-int gemm_splits(int M, int N, int K, size_t scratch_floats) {
-  const long tiles = (long)cdiv(M, 128) * cdiv(N, 128);
+#ifndef GEMM_DW_BIG
+#define GEMM_DW_BIG 1
+#endif
+#ifndef GEMM_DW_ROUNDS
+#define GEMM_DW_ROUNDS 1
+#endif
+int gemm_splits_t(int M, int N, int K, size_t scratch_floats, int tile) {
+  const long tiles = (long)cdiv(M, tile) * cdiv(N, tile);
   int s = 1;
-  // grow until the grid covers >= 2 rounds of the CUs; each split keeps >= 1024 of K
-  while (tiles * s < 2 * NCU && K / (s * 2) >= 1024 && (size_t)(s * 2) * M * N <= scratch_floats) s *= 2;
+  // grow until the grid covers GEMM_DW_ROUNDS rounds of the CUs; each split keeps >= 1024 of K
+  while (tiles * s < GEMM_DW_ROUNDS * NCU && K / (s * 2) >= 1024 && (size_t)(s * 2) * M * N <= scratch_floats)
+    s *= 2;
   return s;
 }
+int gemm_splits(int M, int N, int K, size_t scratch_floats) { return gemm_splits_t(M, N, K, scratch_floats, 128); }
 
 template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
 static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, hipStream_t s) {
@@ -485,7 +493,7 @@ template <typename T, int BM, int BN, bool AKC, bool BKC>
 static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t scratch_floats, hipStream_t s) {
   const int tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
   int splits = 1;
-  if (epi == EPI_F32 && scratch) splits = gemm_splits(a.M, a.N, a.K, scratch_floats);
+  if (epi == EPI_F32 && scratch) splits = gemm_splits_t(a.M, a.N, a.K, scratch_floats, BM);
   int k_split = a.K;
   if (splits > 1) {
     k_split = cdiv(cdiv(a.K, splits), Mma<T>::BK) * Mma<T>::BK;
@@ -511,7 +519,8 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
 
 template <typename T, bool AKC, bool BKC>
 static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
-  // split-K weight gradients stay on the 128x128 tile (their M x N is small)
+  // split-K weight gradients (their M x N is small)
+  if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2) return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
   if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.M, a.N))
     return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
   if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.M, a.N))

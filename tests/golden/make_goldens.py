@@ -3,12 +3,15 @@
 Calls only oracle/ (and the seeded input generators). Run from the repository root:
     python tests/golden/make_goldens.py cfg2     # GPT-2 124M fp32, B=4: one step   (~2 min)
     python tests/golden/make_goldens.py cfg3     # GPT-2 124M, B=16: 10 updates     (~45 min)
+    python tests/golden/make_goldens.py seq350 seq1558   # initial loss of one sequence (~2 + 6 min)
 
 cfg2 -> tests/golden/gpt2_124m_fp32_b4_step1.npz: the loss, the pre-clip gradient norm, and
         for every tensor its max |g| plus g, and theta/m/v after one AdamW update, at 64
         seeded sample positions (the full vectors are 124M elements).
 cfg3 -> tests/golden/gpt2_124m_b16_10steps.json: the per-update mean losses and norms of
         10 updates with lr 6e-4, betas (0.9, 0.95), eps 1e-8, wd 0.1, clip 1.0.
+seq350 / seq1558 -> tests/golden/gpt2_{350m,1558m}_seq0_init_loss.json: the mean loss at init of
+        the first sequence (T=1024) of micro-step 0 (the first row of the B=16 batch).
 Inputs: parameters from the seed-1337 normal(0, 0.02) init, Zipf(1.1) token stream of seed 42
 (micro-step s uses stream positions s*(B*T+1) ...).
 """
@@ -89,6 +92,18 @@ def make_cfg3():
                       f, indent=1)
 
 
+def make_seq(cfg, tag):
+    p = init(cfg)
+    tok, tgt = synth.zipf_batch(cfg.vocab, 1, cfg.max_seq, 0)
+    t0 = time.time()
+    loss, _ = O.forward_backward(cfg, p, tok, tgt, need_grads=False)
+    print(f"{tag}: loss {loss:.6f} ({time.time() - t0:.0f} s)", flush=True)
+    with open(os.path.join(HERE, f"gpt2_{tag}_seq0_init_loss.json"), "w") as f:
+        json.dump({"config": f"GPT-2 {tag}, first sequence (T={cfg.max_seq}) of the Zipf(1.1) seed-42 stream, "
+                             f"init seed 1337", "loss": loss}, f, indent=1)
+
+
 if __name__ == "__main__":
     for what in sys.argv[1:]:
-        {"cfg2": make_cfg2, "cfg3": make_cfg3}[what]()
+        {"cfg2": make_cfg2, "cfg3": make_cfg3, "seq350": lambda: make_seq(O.CFG_350M, "350m"),
+         "seq1558": lambda: make_seq(O.CFG_1558M, "1558m")}[what]()
