@@ -261,11 +261,15 @@ __device__ __forceinline__ f32x16 zero16() {
 // row (M index) of accumulator element i for lane group g (= lane / 32)
 __device__ __forceinline__ int acc_row(int i, int g) { return (i >> 2) * 8 + g * 4 + (i & 3); }
 
-// A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile).
+// A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile). Row groups
+// vary fastest across lanes, so the transposed 8-byte LDS writes of 16 lanes fill one 128-byte
+// LDS row (no bank conflicts) while 4 lanes still read 64 contiguous bytes of each global row.
 struct Piece {
   u32x4 r[4];
+  __device__ __forceinline__ static int rgrp(int p) { return (p & 15) * 4; }
+  __device__ __forceinline__ static int cgrp(int p) { return (p >> 4) * 8; }
   __device__ __forceinline__ void load(const uint16_t* src, long ld, int row0, int nrows, int p) {
-    const int rg = (p >> 3) * 4, cg = (p & 7) * 8;
+    const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = row0 + rg + j;
@@ -273,12 +277,12 @@ struct Piece {
     }
   }
   __device__ __forceinline__ void store_rows(uint16_t* lds, int p) const {  // lds[row][col]
-    const int rg = (p >> 3) * 4, cg = (p & 7) * 8;
+    const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + j) * LDP + cg) = r[j];
   }
   __device__ __forceinline__ void store_cols(uint16_t* lds, int p) const {  // lds[col][row]
-    const int rg = (p >> 3) * 4, cg = (p & 7) * 8;
+    const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int d = c >> 1;
@@ -347,11 +351,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
       for (int s = 0; s < 4; ++s) st = mfma(lds_frag16(Ks + (sb * 32 + l32) * LDP + 16 * s + 8 * g), qf[s], st);
       float sc[16];
       float mloc = -INFINITY;
+      if (kb + 31 > qw0) {  // diagonal sub-block: mask keys after the query
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb + acc_row(i, g);
-        sc[i] = key <= myq ? st[i] * c2 : -INFINITY;
-        mloc = fmaxf(mloc, sc[i]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + acc_row(i, g);
+          sc[i] = key <= myq ? st[i] * c2 : -INFINITY;
+          mloc = fmaxf(mloc, sc[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sc[i] = st[i] * c2;
+          mloc = fmaxf(mloc, sc[i]);
+        }
       }
       mloc = pair_max(mloc);
       const float m_new = fmaxf(m_run, mloc);
@@ -410,7 +422,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   __shared__ __attribute__((aligned(16))) uint16_t dOs[KT * LDP];  // [q][d]
   __shared__ __attribute__((aligned(16))) uint16_t Qt[HD * LDP];   // [d][q]
   __shared__ __attribute__((aligned(16))) uint16_t dOt[HD * LDP];  // [d][q]
-  __shared__ float Ls[KT], Dsh[KT];
+  __shared__ __attribute__((aligned(16))) float Ls[KT];
+  __shared__ __attribute__((aligned(16))) float Dsh[KT];
   const int nkt = gridDim.x;
   const int kt_blk = nkt - 1 - blockIdx.x;  // heaviest (earliest keys) first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -477,14 +490,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
         sacc = mfma(qa, kf[s], sacc);
         dpacc = mfma(da, vf[s], dpacc);
       }
+      // LSE (log2 units) and D of this lane's 16 accumulator rows: rows 32qb + 8*r4 + 4g + 0..3
       float pr[16], ds[16];
+      const bool diag = qq0 < kw0 + 31 || qq0 + 32 > T;  // some (q, key) pairs masked or out of range
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = 32 * qb + acc_row(i, g);
-        const int q = qt0 + qr;
-        const float pv = (mykey <= q && q < T) ? fast_exp2(sacc[i] * c2 - Ls[qr]) : 0.f;
-        pr[i] = pv;
-        ds[i] = pv * (dpacc[i] - Dsh[qr]);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + 32 * qb + 8 * r4 + 4 * g);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dsh + 32 * qb + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r4 + e;
+          float pv = fast_exp2(sacc[i] * c2 - l4[e]);
+          if (diag) {
+            const int q = qq0 + acc_row(i, g);
+            pv = (mykey <= q && q < T) ? pv : 0.f;
+          }
+          pr[i] = pv;
+          ds[i] = pv * (dpacc[i] - d4[e]);
+        }
       }
       // dV += P^T dO ; dK += dS^T Q  (A = accumulator as [key][q], B from transposed tiles)
 #pragma unroll
@@ -585,10 +608,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
         dpt = mfma(lds_frag16(Vs + (sb * 32 + l32) * LDP + 16 * s + 8 * g), df[s], dpt);
       }
       float ds[16];
+      const bool diag = kb + 31 > qw0 || qw0 + 32 > T;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kb + acc_row(i, g);
-        const float pv = (key <= myq && myq < T) ? fast_exp2(st[i] * c2 - L2) : 0.f;
+        float pv = fast_exp2(st[i] * c2 - L2);
+        if (diag) {
+          const int key = kb + acc_row(i, g);
+          pv = (key <= myq && myq < T) ? pv : 0.f;
+        }
         ds[i] = pv * (dpt[i] - Dq);
       }
       // dQ += dS K : A = dS (rows q, k = keys) from the accumulator, B = K from Kt [d][key]

@@ -177,22 +177,32 @@ __device__ __forceinline__ float gelu_bwd(float x) {
 __host__ __device__ constexpr int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // out[c] (+)= sum_{y < ny} part[y * ld + c] for c < ncols, summed in a fixed order.
-// Block of 256 threads handles 32 columns: 8 row-groups stride over y, then 8 partials per
-// column are added in order. Grid: cdiv(ncols, 32).
+// Block of 1024 threads handles 32 columns: 32 row-groups stride over y (8 independent loads in
+// flight per thread), then the 32 group sums of a column are added in order. Grid: cdiv(ncols, 32).
+constexpr int RP_THREADS = 1024;
 __device__ __forceinline__ void reduce_partials_block(const float* __restrict__ part, int ny, long ld, int ncols,
                                                       float* __restrict__ out, int accumulate) {
-  __shared__ float sh[8][33];
+  __shared__ float sh[32][33];
   const int cl = threadIdx.x & 31, yg = threadIdx.x >> 5;
   const int c = blockIdx.x * 32 + cl;
   float s = 0.f;
-  if (c < ncols)
-    for (int y = yg; y < ny; y += 8) s += part[(size_t)y * ld + c];
+  if (c < ncols) {
+    int y = yg;
+    for (; y + 7 * 32 < ny; y += 8 * 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(y + u * 32) * ld + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; y < ny; y += 32) s += part[(size_t)y * ld + c];
+  }
   sh[yg][cl] = s;
   __syncthreads();
   if (yg == 0 && c < ncols) {
     float t = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t += sh[i][cl];
+    for (int i = 0; i < 32; ++i) t += sh[i][cl];
     out[c] = accumulate ? out[c] + t : t;
   }
 }

@@ -20,7 +20,7 @@ constexpr int CE_WAVES = CE_THREADS / 64;
 // dloss_out = 1/(n_valid * accum) (0 when n_valid == 0); nvalid_out = n_valid; err |= 2 on bad target
 __global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __restrict__ targets, int rows, int V,
                                                              int accum, float* dloss_out, int* nvalid_out, int* err) {
-  __shared__ float red[16];
+  __shared__ float red[16];  // count_targets runs with 1024 threads
   float c = 0.f;
   bool bad = false;
   for (int i = threadIdx.x; i < rows; i += 1024) {

@@ -12,12 +12,14 @@
 //    for N = C products and split-K weight gradients, chosen per shape so the grid covers the
 //    256 CUs in whole rounds. bf16: v_mfma_f32_32x32x16_bf16, BK = 64; fp32:
 //    v_mfma_f32_32x32x2f32, BK = 32.
-//  * LDS holds both operands as [row][k] (k contiguous, +16 B pad: conflict-free 16-byte reads),
-//    so every MFMA operand is one LDS read per lane. K-contiguous operands are copied 16 B at a
-//    time; M/N-contiguous operands (the transposed side of NN / TN products) are loaded as 4 x 16 B
-//    row pieces and transposed in registers on the way into LDS.
-//  * Double-buffered LDS with register staging: the global loads of tile k+1 are in flight while
-//    tile k is multiplied (64 MFMAs per wave per tile on the 256x256 tile); one barrier per tile.
+//  * LDS holds both operands as [row][k], so every MFMA operand is one 16-byte LDS read per lane.
+//    K-contiguous operands are stored unpadded with the 16-byte chunks of row r XOR-swizzled by
+//    r & 7 (conflict-free fragment reads) and, for interior tiles, copied global -> LDS directly
+//    with global_load_lds_dwordx4 (no staging registers, no LDS write instructions). Edge tiles
+//    and M/N-contiguous operands (the transposed side of NN / TN products) go through registers;
+//    the latter are loaded as 4 x 16 B row pieces and transposed in registers into padded rows.
+//  * Double-buffered LDS: the copies of tile k+1 are in flight while tile k is multiplied
+//    (64 MFMAs per wave per tile on the 256x256 tile); one barrier per tile.
 //  * Epilogue through LDS: each wave parks 32 rows of fp32 accumulators in LDS and reads them back
 //    row-contiguous, so bias / residual / GELU inputs are read and results written as 16-byte
 //    coalesced vectors.
@@ -64,29 +66,35 @@ constexpr int NTHR = 256, WGM = 2, WGN = 2;
 constexpr int GROUP_M = 8;
 constexpr int TKR = 4;  // transposed piece: TKR k-rows x VEC row-contiguous elements
 
-template <typename T, int BM_, int BN_> struct Cfg {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr int TM = BM / WGM, TN = BN / WGN;
-  static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int VEC = Elt<T>::VEC;
-  static constexpr int BK = Mma<T>::BK;
-  static constexpr int LD = BK + VEC;  // LDS row pitch (elements)
-  static constexpr int EPI_LD = TN + 4;  // epilogue staging pitch (floats)
-  static constexpr size_t LDS_BYTES = 2ull * (BM + BN) * LD * sizeof(T);
-  static_assert(LDS_BYTES >= (size_t)4 * 32 * EPI_LD * 4, "epilogue staging must fit");
-};
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// One operand tile (ROWS rows of the M or N side, BK of K) staged through registers.
-// KC: operand is K-contiguous (ptr[row*ld + k]) else row-contiguous (ptr[k*ld + row]).
-template <typename T, bool KC, int ROWS> struct Loader {
+// One operand (ROWS rows of the M or N side, BK of K per stage).
+// KC: the operand is K-contiguous in memory (ptr[row*ld + k]); else row-contiguous (ptr[k*ld + row]).
+//  * KC operands live in LDS unpadded, BK elements per row (128 bytes), with the 16-byte chunk c of
+//    row r stored at chunk position c ^ (r & 7): a fragment read (32 consecutive rows, one chunk)
+//    touches every bank once. Interior tiles are copied global -> LDS directly
+//    (global_load_lds_dwordx4: lane l of a wave lands at LDS base + 16 l, so each lane fetches the
+//    global chunk that belongs at its swizzled position); edge tiles go through registers with
+//    out-of-range elements zeroed.
+//  * Row-contiguous operands (the transposed side of NN / TN products) are loaded as 4 x 16 B row
+//    pieces, transposed in registers and stored into rows padded by 16 bytes.
+template <typename T, bool KC, int ROWS> struct Operand {
   static constexpr int VEC = Elt<T>::VEC;
   static constexpr int BK = Mma<T>::BK;
-  static constexpr int LD = BK + VEC;
+  static constexpr int LD = KC ? BK : BK + VEC;  // LDS row pitch (elements)
+  static constexpr int ELEMS = ROWS * LD;        // one stage
+  static_assert(!KC || BK / VEC == 8, "the swizzle assumes 8 chunks per row");
   static constexpr int NV_K = (ROWS * BK / VEC) / NTHR;           // 16-byte vectors per thread
   static constexpr int NV_T = ((BK / TKR) * (ROWS / VEC)) / NTHR;  // transposed pieces per thread
   static constexpr int NREG = KC ? NV_K : NV_T * TKR;
   static_assert(NREG > 0, "tile too small for the thread count");
   u32x4 r[NREG];
+
+  // element offset of (row, k) inside one stage
+  __device__ __forceinline__ static int idx(int row, int k) {
+    if constexpr (KC) return row * BK + ((((k / VEC) ^ (row & 7)) * VEC) | (k % VEC));
+    else return row * LD + k;
+  }
 
   // zero the elements [keep, VEC) of a 16-byte vector (keep <= 0: all), branch-free
   __device__ __forceinline__ static u32x4 keep_first(u32x4 x, int keep) {
@@ -104,13 +112,32 @@ template <typename T, bool KC, int ROWS> struct Loader {
     return o;
   }
 
-  // Interior tiles take straight-line unchecked loads; edge tiles clamp the address to a valid
-  // one and zero the out-of-range elements with selects, so the loads stay in one basic block.
+  __device__ __forceinline__ static bool interior(int row0, int nrows, int k0, int K) {
+    return row0 + ROWS <= nrows && k0 + BK <= K;
+  }
+
+  // KC, interior tile: global -> LDS without registers
+  __device__ __forceinline__ static void issue_direct(const T* __restrict__ ptr, long ld, int row0, int k0,
+                                                      T* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int RPW = ROWS / (NTHR / 64);  // rows per wave
+#pragma unroll
+    for (int j = 0; j < RPW / 8; ++j) {
+      const int rb = w * RPW + j * 8;
+      const int rr = rb + (lane >> 3);
+      const int c = (lane & 7) ^ (rr & 7);
+      const T* g = ptr + (size_t)(row0 + rr) * ld + k0 + c * VEC;
+      __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + rb * BK), 16, 0, 0);
+    }
+  }
+
+  // Register path. Interior tiles take straight-line unchecked loads; edge tiles clamp the address
+  // to a valid one and zero the out-of-range elements with selects (loads stay in one block).
   __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
     const int tid = threadIdx.x;
-    const bool interior = row0 + ROWS <= nrows && k0 + BK <= K;
+    const bool inner = interior(row0, nrows, k0, K);
     if constexpr (KC) {
-      if (interior) {
+      if (inner) {
 #pragma unroll
         for (int i = 0; i < NV_K; ++i) {
           const int v = i * NTHR + tid;
@@ -130,7 +157,7 @@ template <typename T, bool KC, int ROWS> struct Loader {
         }
       }
     } else {
-      if (interior) {
+      if (inner) {
 #pragma unroll
         for (int i = 0; i < NV_T; ++i) {
           const int pc = i * NTHR + tid;
@@ -166,7 +193,7 @@ template <typename T, bool KC, int ROWS> struct Loader {
         const int v = i * NTHR + tid;
         const int row = v / (BK / VEC);
         const int kc = (v % (BK / VEC)) * VEC;
-        *reinterpret_cast<u32x4*>(lds + row * LD + kc) = r[i];
+        *reinterpret_cast<u32x4*>(lds + idx(row, kc)) = r[i];
       }
     } else {
 #pragma unroll
@@ -201,6 +228,19 @@ template <typename T, bool KC, int ROWS> struct Loader {
       }
     }
   }
+};
+
+template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int BK = Mma<T>::BK;
+  using OA = Operand<T, AKC, BM>;
+  using OB = Operand<T, BKC, BN>;
+  static constexpr int STAGE = OA::ELEMS + OB::ELEMS;  // elements per LDS stage
+  static constexpr int EPI_LD = TN + 4;                 // epilogue staging pitch (floats)
+  static constexpr size_t LDS_BYTES = 2ull * STAGE * sizeof(T);
+  static_assert(LDS_BYTES >= (size_t)4 * 32 * EPI_LD * 4, "epilogue staging must fit");
 };
 
 // Apply the epilogue to 8 consecutive columns [col, col+8) of one row and store them.
@@ -285,16 +325,113 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
   }
 }
 
+// The K loop of one block. DA / DB: every tile of that operand in this block is interior and
+// K-contiguous, so it is copied global -> LDS directly; otherwise it goes through registers.
+template <typename T, int BM, int BN, bool AKC, bool BKC, bool DA, bool DB>
+__device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0, int kbeg, int kend, T* st0,
+                                              f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  using CF = Cfg<T, BM, BN, AKC, BKC>;
+  using MM = Mma<T>;
+  using OA = typename CF::OA;
+  using OB = typename CF::OB;
+  constexpr int BK = CF::BK, TM = CF::TM, TN = CF::TN, FM = CF::FM, FN = CF::FN;
+  auto Abuf = [&](int stg) { return st0 + stg * CF::STAGE; };
+  auto Bbuf = [&](int stg) { return st0 + stg * CF::STAGE + OA::ELEMS; };
+  const T* A = reinterpret_cast<const T*>(p.A);
+  const T* B = reinterpret_cast<const T*>(p.B);
+  const int nkt = cdiv(kend - kbeg, BK);
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+
+  struct Empty {};
+  struct NoRegs {
+    __device__ void load(const T*, long, int, int, int, int) {}
+    __device__ void store(T*) const {}
+  };
+  using RA = typename std::conditional<DA, NoRegs, OA>::type;
+  using RB = typename std::conditional<DB, NoRegs, OB>::type;
+  RA la;
+  RB lb;
+  auto fetch = [&](int k0, int stg) {
+    if constexpr (DA) OA::issue_direct(A, p.lda, m0, k0, Abuf(stg));
+    else la.load(A, p.lda, m0, p.M, k0, kend);
+    if constexpr (DB) OB::issue_direct(B, p.ldb, n0, k0, Bbuf(stg));
+    else lb.load(B, p.ldb, n0, p.N, k0, kend);
+  };
+  if (nkt > 0) {
+    fetch(kbeg, 0);
+    la.store(Abuf(0));
+    lb.store(Bbuf(0));
+  }
+  if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int arow = wm * TM + (lane & 31);
+  const int brow = wn * TN + (lane & 31);
+  const int kofs = (lane >> 5) * MM::KPL;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nkt;
+    if (more) fetch(kbeg + (kt + 1) * BK, cur ^ 1);
+    const T* as = Abuf(cur);
+    const T* bs = Bbuf(cur);
+#if GEMM_FRAG_DB
+    // operand fragments are double-buffered: the LDS reads of k-step s+1 are issued before the
+    // MFMAs of k-step s, so their latency hides behind FM*FN MFMAs
+    constexpr int KS = BK / MM::KSTEP;
+    typename MM::frag fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = MM::load(as + OA::idx(arow + i * 32, kofs));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = MM::load(bs + OB::idx(brow + j * 32, kofs));
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int cb = st & 1, nb = cb ^ 1;
+      if (st + 1 < KS) {
+        const int kk = (st + 1) * MM::KSTEP;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[nb][i] = MM::load(as + OA::idx(arow + i * 32, kk + kofs));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[nb][j] = MM::load(bs + OB::idx(brow + j * 32, kk + kofs));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[cb][i], fb[cb][j], acc[i][j]);
+    }
+#else
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += MM::KSTEP) {
+      typename MM::frag fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = MM::load(as + OA::idx(arow + i * 32, kk + kofs));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = MM::load(bs + OB::idx(brow + j * 32, kk + kofs));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
+    }
+#endif
+    GEMM_SCHED_HINT;
+    if (more) {
+      la.store(Abuf(cur ^ 1));
+      lb.store(Bbuf(cur ^ 1));
+    }
+    if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);  // direct copies of the next stage landed
+    __syncthreads();
+  }
+}
+
 template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, float* split_out) {
-  using CF = Cfg<T, BM, BN>;
-  using MM = Mma<T>;
-  constexpr int LD = CF::LD, BK = CF::BK, TM = CF::TM, TN = CF::TN, FM = CF::FM, FN = CF::FN;
+  using CF = Cfg<T, BM, BN, AKC, BKC>;
+  constexpr int BK = CF::BK, TM = CF::TM, TN = CF::TN, FM = CF::FM, FN = CF::FN;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* As0 = reinterpret_cast<T*>(smem);
-  T* Bs0 = As0 + BM * LD;
-  T* As1 = Bs0 + BN * LD;
-  T* Bs1 = As1 + BM * LD;
+  T* const st0 = reinterpret_cast<T*>(smem);
 
   // tile mapping: XCD-contiguous runs, then grouped row-major order
   const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
@@ -310,10 +447,6 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
 
   const int kbeg = blockIdx.z * k_split;
   const int kend = min(p.K, kbeg + k_split);
-  const int nkt = cdiv(kend - kbeg, BK);
-
-  const T* A = reinterpret_cast<const T*>(p.A);
-  const T* B = reinterpret_cast<const T*>(p.B);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,74 +461,20 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  Loader<T, AKC, BM> la;
-  Loader<T, BKC, BN> lb;
-  if (nkt > 0) {
-    la.load(A, p.lda, m0, p.M, kbeg, kend);
-    lb.load(B, p.ldb, n0, p.N, kbeg, kend);
-    la.store(As0);
-    lb.store(Bs0);
-  }
-  __syncthreads();
-
-  const int arow = wm * TM + (lane & 31);
-  const int brow = wn * TN + (lane & 31);
-  const int kofs = (lane >> 5) * MM::KPL;
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bool odd = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(A, p.lda, m0, p.M, k0, kend);
-      lb.load(B, p.ldb, n0, p.N, k0, kend);
-    }
-    const T* as = odd ? As1 : As0;
-    const T* bs = odd ? Bs1 : Bs0;
-#if GEMM_FRAG_DB
-    // operand fragments are double-buffered: the LDS reads of k-step s+1 are issued before the
-    // MFMAs of k-step s, so their latency hides behind FM*FN MFMAs
-    constexpr int KS = BK / MM::KSTEP;
-    typename MM::frag fa[2][FM], fb[2][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[0][i] = MM::load(as + (arow + i * 32) * LD + kofs);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[0][j] = MM::load(bs + (brow + j * 32) * LD + kofs);
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const int cb = st & 1, nb = cb ^ 1;
-      if (st + 1 < KS) {
-        const int kk = (st + 1) * MM::KSTEP;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[nb][i] = MM::load(as + (arow + i * 32) * LD + kk + kofs);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[nb][j] = MM::load(bs + (brow + j * 32) * LD + kk + kofs);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[cb][i], fb[cb][j], acc[i][j]);
-    }
-#else
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += MM::KSTEP) {
-      typename MM::frag fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = MM::load(as + (arow + i * 32) * LD + kk + kofs);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = MM::load(bs + (brow + j * 32) * LD + kk + kofs);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
-    }
-#endif
-    GEMM_SCHED_HINT;
-    if (more) {
-      la.store(odd ? As0 : As1);
-      lb.store(odd ? Bs0 : Bs1);
-    }
-    __syncthreads();
+  const bool kfull = (kend - kbeg) % BK == 0;
+  const bool da = AKC && kfull && m0 + BM <= p.M;
+  const bool db = BKC && kfull && n0 + BN <= p.N;
+  if constexpr (AKC && BKC) {
+    if (da && db) gemm_mainloop<T, BM, BN, AKC, BKC, true, true>(p, m0, n0, kbeg, kend, st0, acc);
+    else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
+  } else if constexpr (AKC) {
+    if (da) gemm_mainloop<T, BM, BN, AKC, BKC, true, false>(p, m0, n0, kbeg, kend, st0, acc);
+    else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
+  } else if constexpr (BKC) {
+    if (db) gemm_mainloop<T, BM, BN, AKC, BKC, false, true>(p, m0, n0, kbeg, kend, st0, acc);
+    else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
+  } else {
+    gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
   }
 
   // ---- epilogue: 32-row slabs of each wave go through LDS, then 16-byte row chunks out
@@ -478,7 +557,7 @@ int gemm_splits(int M, int N, int K, size_t scratch_floats) { return gemm_splits
 
 template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
 static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, hipStream_t s) {
-  using CF = Cfg<T, BM, BN>;
+  using CF = Cfg<T, BM, BN, AKC, BKC>;
   static bool attr = false;
   auto kern = gemm_kernel<T, BM, BN, AKC, BKC, EPI>;
   if (!attr) {
@@ -585,7 +664,7 @@ __global__ __launch_bounds__(256) void colsum_partial(const T* __restrict__ x, l
   }
 }
 
-__global__ __launch_bounds__(256) void colsum_finish(const float* __restrict__ partial, int ny, int N,
+__global__ __launch_bounds__(RP_THREADS) void colsum_finish(const float* __restrict__ partial, int ny, int N,
                                                      float* __restrict__ out, int accumulate) {
   reduce_partials_block(partial, ny, N, N, out, accumulate);
 }
@@ -604,7 +683,7 @@ hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float*
     else
       colsum_partial<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(dY), ld, M, N, partial);
   }
-  colsum_finish<<<cdiv(N, 32), 256, 0, s>>>(partial, M > 0 ? ny : 0, N, db, accumulate);
+  colsum_finish<<<cdiv(N, 32), RP_THREADS, 0, s>>>(partial, M > 0 ? ny : 0, N, db, accumulate);
   return hipGetLastError();
 }
 

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_p
 }
 
 // grid (cdiv(C, 32), 2): y = 0 -> dw, y = 1 -> db
-__global__ __launch_bounds__(256) void ln_bwd_finish(const float* __restrict__ partial, int nblocks, int C,
+__global__ __launch_bounds__(RP_THREADS) void ln_bwd_finish(const float* __restrict__ partial, int nblocks, int C,
                                                      float* __restrict__ dw, float* __restrict__ db,
                                                      int accumulate) {
   float* out = blockIdx.y == 0 ? dw : db;
@@ -213,7 +213,7 @@ static hipError_t ln_bwd_t(int rows, int C, const void* dy, const void* x, const
     else if (nv <= 8) ln_bwd_kernel<T, 8><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, partial);
     else return hipErrorInvalidValue;
   }
-  ln_bwd_finish<<<dim3(cdiv(C, 32), 2), 256, 0, s>>>(partial, nb, C, dw, db, accumulate);
+  ln_bwd_finish<<<dim3(cdiv(C, 32), 2), RP_THREADS, 0, s>>>(partial, nb, C, dw, db, accumulate);
   return hipGetLastError();
 }
 
