@@ -70,30 +70,72 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One operand (ROWS rows of the M or N side, BK of K per stage).
 // KC: the operand is K-contiguous in memory (ptr[row*ld + k]); else row-contiguous (ptr[k*ld + row]).
-//  * KC operands live in LDS unpadded, BK elements per row (128 bytes), with the 16-byte chunk c of
+// Three LDS layouts (MODE):
+//  0 (K-contiguous): unpadded [row][k], BK elements per row (128 bytes), the 16-byte chunk c of
 //    row r stored at chunk position c ^ (r & 7): a fragment read (32 consecutive rows, one chunk)
-//    touches every bank once. Interior tiles are copied global -> LDS directly
-//    (global_load_lds_dwordx4: lane l of a wave lands at LDS base + 16 l, so each lane fetches the
-//    global chunk that belongs at its swizzled position); edge tiles go through registers with
-//    out-of-range elements zeroed.
-//  * Row-contiguous operands (the transposed side of NN / TN products) are loaded as 4 x 16 B row
-//    pieces, transposed in registers and stored into rows padded by 16 bytes.
+//    touches every bank once.
+//  2 (bf16 row-contiguous): [k][row] as in memory, so interior tiles can be copied directly too;
+//    the MFMA fragments (8 consecutive k of one row per lane) come out of ds_read_b64_tr_b16,
+//    which hands lane 16g+i the element (i & 3) of the 8 bytes addressed by lane 16g+4j+(i>>2)
+//    as its element j. The k-rows are packed RB = 512/ROWS to a 1024-byte block (one wave-wide
+//    direct copy); block b holds the rows k = (b/4)*4*RB + 4q + (b & 3), q < RB, and blocks are
+//    1088 bytes apart, so the four k-rows one transpose read touches fall in four different
+//    64-byte bank groups.
+//  1 (fp32 row-contiguous): loaded as 4 x 16 B row pieces, transposed in registers and stored as
+//    [row][k] with rows padded by 16 bytes.
+// Interior tiles of modes 0 and 2 are copied global -> LDS with global_load_lds_dwordx4 (lane l
+// of a wave lands at LDS base + 16 l, so each lane fetches the global chunk that belongs there);
+// edge tiles and mode 1 go through registers, with out-of-range elements zeroed.
 template <typename T, bool KC, int ROWS> struct Operand {
   static constexpr int VEC = Elt<T>::VEC;
   static constexpr int BK = Mma<T>::BK;
-  static constexpr int LD = KC ? BK : BK + VEC;  // LDS row pitch (elements)
-  static constexpr int ELEMS = ROWS * LD;        // one stage
-  static_assert(!KC || BK / VEC == 8, "the swizzle assumes 8 chunks per row");
+  static constexpr int MODE = KC ? 0 : (sizeof(T) == 2 ? 2 : 1);
+  static constexpr bool DIRECT = MODE != 1;  // interior tiles can be copied global -> LDS
+  static constexpr int LD = MODE == 0 ? BK : BK + VEC;  // [row][k] pitch (elements), modes 0 / 1
+  // mode 2 geometry
+  static constexpr int RB = 512 / ROWS;             // k-rows per 1024-byte block
+  static constexpr int BLK = (1024 + 64) / 2;       // block pitch (elements)
+  static constexpr int NBLK = BK / RB;              // blocks per stage
+  static constexpr int ELEMS = MODE == 2 ? NBLK * BLK : ROWS * LD;  // one stage
+  static_assert(MODE != 0 || BK / VEC == 8, "the swizzle assumes 8 chunks per row");
+  static_assert(MODE != 2 || ((ROWS == 128 || ROWS == 256) && NBLK % 4 == 0), "mode 2 tile shape");
   static constexpr int NV_K = (ROWS * BK / VEC) / NTHR;           // 16-byte vectors per thread
   static constexpr int NV_T = ((BK / TKR) * (ROWS / VEC)) / NTHR;  // transposed pieces per thread
-  static constexpr int NREG = KC ? NV_K : NV_T * TKR;
+  static constexpr int NREG = MODE == 1 ? NV_T * TKR : NV_K;
   static_assert(NREG > 0, "tile too small for the thread count");
   u32x4 r[NREG];
 
-  // element offset of (row, k) inside one stage
+  // element offset of (row, k) inside one stage, modes 0 and 1
   __device__ __forceinline__ static int idx(int row, int k) {
-    if constexpr (KC) return row * BK + ((((k / VEC) ^ (row & 7)) * VEC) | (k % VEC));
+    if constexpr (MODE == 0) return row * BK + ((((k / VEC) ^ (row & 7)) * VEC) | (k % VEC));
     else return row * LD + k;
+  }
+
+  // mode 2: block j of wave w; lane l holds (k-row, first row element) of its 16 bytes
+  __device__ __forceinline__ static void tr_slot(int b, int lane, int& k, int& m) {
+    constexpr int LPR = ROWS / 8;  // lanes per k-row
+    const int q = lane / LPR;
+    m = (lane % LPR) * 8;
+    k = (b >> 2) * 4 * RB + q * 4 + (b & 3);
+  }
+
+  // mode 2: per-lane part of the transpose-read address for the wave whose rows start at wrow
+  __device__ __forceinline__ static int tr_lane_off(int wrow, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int kh = g >> 1, j = s >> 2;
+    const int mq = (g & 1) * 16 + 4 * (s & 3);
+    return j * BLK + (RB == 2 ? kh * 4 * BLK : kh * 2 * ROWS) + wrow + mq;
+  }
+  // mode 2: the fragment of 32-row block i at k-step st (k = 16 st .. 16 st + 15)
+  __device__ __forceinline__ static bf16x8 tr_frag(const T* stage, int lane_off, int i, int st) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    const int c0 = (RB == 2 ? st * 8 : st * 4) * BLK + i * 32;
+    const T* p0 = stage + lane_off + c0;
+    const T* p1 = p0 + ROWS;  // k + 4
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(p0)));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(p1)));
+    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8, v);
   }
 
   // zero the elements [keep, VEC) of a 16-byte vector (keep <= 0: all), branch-free
@@ -116,18 +158,30 @@ template <typename T, bool KC, int ROWS> struct Operand {
     return row0 + ROWS <= nrows && k0 + BK <= K;
   }
 
-  // KC, interior tile: global -> LDS without registers
+  // interior tile, modes 0 and 2: global -> LDS without registers
   __device__ __forceinline__ static void issue_direct(const T* __restrict__ ptr, long ld, int row0, int k0,
                                                       T* lds) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    constexpr int RPW = ROWS / (NTHR / 64);  // rows per wave
+    if constexpr (MODE == 0) {
+      constexpr int RPW = ROWS / (NTHR / 64);  // rows per wave
 #pragma unroll
-    for (int j = 0; j < RPW / 8; ++j) {
-      const int rb = w * RPW + j * 8;
-      const int rr = rb + (lane >> 3);
-      const int c = (lane & 7) ^ (rr & 7);
-      const T* g = ptr + (size_t)(row0 + rr) * ld + k0 + c * VEC;
-      __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + rb * BK), 16, 0, 0);
+      for (int j = 0; j < RPW / 8; ++j) {
+        const int rb = w * RPW + j * 8;
+        const int rr = rb + (lane >> 3);
+        const int c = (lane & 7) ^ (rr & 7);
+        const T* g = ptr + (size_t)(row0 + rr) * ld + k0 + c * VEC;
+        __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + rb * BK), 16, 0, 0);
+      }
+    } else {
+      constexpr int BPW = NBLK / (NTHR / 64);  // blocks per wave
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        const int b = w * BPW + j;
+        int k, m;
+        tr_slot(b, lane, k, m);
+        const T* g = ptr + (size_t)(k0 + k) * ld + row0 + m;
+        __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + b * BLK), 16, 0, 0);
+      }
     }
   }
 
@@ -136,7 +190,21 @@ template <typename T, bool KC, int ROWS> struct Operand {
   __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
     const int tid = threadIdx.x;
     const bool inner = interior(row0, nrows, k0, K);
-    if constexpr (KC) {
+    if constexpr (MODE == 2) {
+      // same lane -> slot map as the direct copy; used for edge tiles only
+      const int lane = tid & 63, w = tid >> 6;
+      constexpr int BPW = NBLK / (NTHR / 64);
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        int k, m;
+        tr_slot(w * BPW + j, lane, k, m);
+        k += k0;
+        m += row0;
+        const bool ok = k < K && m < nrows;
+        const T* src = ok ? ptr + (size_t)k * ld + m : ptr;
+        r[j] = keep_first(*reinterpret_cast<const u32x4*>(src), ok ? nrows - m : 0);
+      }
+    } else if constexpr (MODE == 0) {
       if (inner) {
 #pragma unroll
         for (int i = 0; i < NV_K; ++i) {
@@ -187,7 +255,12 @@ template <typename T, bool KC, int ROWS> struct Operand {
 
   __device__ __forceinline__ void store(T* __restrict__ lds) const {
     const int tid = threadIdx.x;
-    if constexpr (KC) {
+    if constexpr (MODE == 2) {
+      const int lane = tid & 63, w = tid >> 6;
+      constexpr int BPW = NBLK / (NTHR / 64);
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) *reinterpret_cast<u32x4*>(lds + (w * BPW + j) * BLK + lane * 8) = r[j];
+    } else if constexpr (MODE == 0) {
 #pragma unroll
       for (int i = 0; i < NV_K; ++i) {
         const int v = i * NTHR + tid;
@@ -371,6 +444,18 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
   const int arow = wm * TM + (lane & 31);
   const int brow = wn * TN + (lane & 31);
   const int kofs = (lane >> 5) * MM::KPL;
+  int atr = 0, btr = 0;
+  if constexpr (OA::MODE == 2) atr = OA::tr_lane_off(wm * TM, lane);
+  if constexpr (OB::MODE == 2) btr = OB::tr_lane_off(wn * TN, lane);
+  // operand fragments of 32-row block i at k-step st
+  auto fragA = [&](const T* as, int i, int st) {
+    if constexpr (OA::MODE == 2) return OA::tr_frag(as, atr, i, st);
+    else return MM::load(as + OA::idx(arow + i * 32, st * MM::KSTEP + kofs));
+  };
+  auto fragB = [&](const T* bs, int j, int st) {
+    if constexpr (OB::MODE == 2) return OB::tr_frag(bs, btr, j, st);
+    else return MM::load(bs + OB::idx(brow + j * 32, st * MM::KSTEP + kofs));
+  };
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
@@ -384,18 +469,17 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
     constexpr int KS = BK / MM::KSTEP;
     typename MM::frag fa[2][FM], fb[2][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[0][i] = MM::load(as + OA::idx(arow + i * 32, kofs));
+    for (int i = 0; i < FM; ++i) fa[0][i] = fragA(as, i, 0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[0][j] = MM::load(bs + OB::idx(brow + j * 32, kofs));
+    for (int j = 0; j < FN; ++j) fb[0][j] = fragB(bs, j, 0);
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       const int cb = st & 1, nb = cb ^ 1;
       if (st + 1 < KS) {
-        const int kk = (st + 1) * MM::KSTEP;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[nb][i] = MM::load(as + OA::idx(arow + i * 32, kk + kofs));
+        for (int i = 0; i < FM; ++i) fa[nb][i] = fragA(as, i, st + 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[nb][j] = MM::load(bs + OB::idx(brow + j * 32, kk + kofs));
+        for (int j = 0; j < FN; ++j) fb[nb][j] = fragB(bs, j, st + 1);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -404,12 +488,12 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
     }
 #else
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += MM::KSTEP) {
+    for (int st = 0; st < BK / MM::KSTEP; ++st) {
       typename MM::frag fa[FM], fb[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = MM::load(as + OA::idx(arow + i * 32, kk + kofs));
+      for (int i = 0; i < FM; ++i) fa[i] = fragA(as, i, st);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = MM::load(bs + OB::idx(brow + j * 32, kk + kofs));
+      for (int j = 0; j < FN; ++j) fb[j] = fragB(bs, j, st);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -461,16 +545,17 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  constexpr bool XA = CF::OA::DIRECT, XB = CF::OB::DIRECT;
   const bool kfull = (kend - kbeg) % BK == 0;
-  const bool da = AKC && kfull && m0 + BM <= p.M;
-  const bool db = BKC && kfull && n0 + BN <= p.N;
-  if constexpr (AKC && BKC) {
+  const bool da = XA && kfull && m0 + BM <= p.M;
+  const bool db = XB && kfull && n0 + BN <= p.N;
+  if constexpr (XA && XB) {
     if (da && db) gemm_mainloop<T, BM, BN, AKC, BKC, true, true>(p, m0, n0, kbeg, kend, st0, acc);
     else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
-  } else if constexpr (AKC) {
+  } else if constexpr (XA) {
     if (da) gemm_mainloop<T, BM, BN, AKC, BKC, true, false>(p, m0, n0, kbeg, kend, st0, acc);
     else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
-  } else if constexpr (BKC) {
+  } else if constexpr (XB) {
     if (db) gemm_mainloop<T, BM, BN, AKC, BKC, false, true>(p, m0, n0, kbeg, kend, st0, acc);
     else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
   } else {

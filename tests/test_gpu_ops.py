@@ -50,7 +50,7 @@ DTS = [bd.GPT2_FP32, bd.GPT2_BF16]
 
 # ---------------------------------------------------------------------------- GEMM
 
-GEMM_SHAPES = [(200, 136, 72), (256, 384, 256), (36, 16, 2), (130, 264, 520)]
+GEMM_SHAPES = [(200, 136, 72), (256, 384, 256), (36, 16, 2), (130, 264, 520), (260, 392, 512)]
 
 
 @pytest.mark.parametrize("dt", DTS)
@@ -92,11 +92,14 @@ BIG_CASES = [((1, 1), bd.EPI_BIAS), ((1, 0), bd.EPI_BIAS), ((0, 0), bd.EPI_BIAS)
              ((1, 1), bd.EPI_GELU), ((1, 1), bd.EPI_RESID), ((1, 0), bd.EPI_GELU_BWD), ((0, 0), bd.EPI_F32)]
 
 
+@pytest.mark.parametrize("K", [72, 192])
 @pytest.mark.parametrize("layout,epi", BIG_CASES)
-def test_gemm_bf16_256_tile_path(layout, epi):
-    """Shapes with >= 384 tiles of 256 x 256 take the large-tile kernel; ragged M and N."""
+def test_gemm_bf16_256_tile_path(layout, epi, K):
+    """Shapes with >= 384 tiles of 256 x 256 take the large-tile kernel; ragged M and N. With K a
+    multiple of 64 the interior tiles take the direct global -> LDS copies, the edge tiles the
+    register path; with K = 72 every tile has a ragged K tail."""
     akc, bkc = layout
-    M, N, K = 4100, 6392, 72
+    M, N = 4100, 6392
     rng = np.random.default_rng(epi * 10 + akc * 2 + bkc)
     A, Bm = rng.normal(0, 1, (M, K)), rng.normal(0, 1, (N, K))
     bias = rng.normal(0, 1, N)
