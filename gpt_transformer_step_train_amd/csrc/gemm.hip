@@ -316,52 +316,88 @@ template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   static_assert(LDS_BYTES >= (size_t)4 * 32 * EPI_LD * 4, "epilogue staging must fit");
 };
 
-// Apply the epilogue to 8 consecutive columns [col, col+8) of one row and store them.
+// Per 8-column chunk, the epilogue inputs besides the accumulators: the residual / GELU input
+// (aux) or, for fp32 accumulation, the old C. They are fetched for a whole slab before any of
+// its results is stored, so the loads are in flight together.
+template <typename T, int EPI> struct EpiX {
+  static constexpr bool USED = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32;
+  static constexpr int NW = EPI == EPI_F32 ? 2 : 8 / Elt<T>::VEC;  // 16-byte words per chunk
+  u32x4 w[NW];
+};
+
 template <typename T, int EPI>
-__device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long ldc, int row, int col,
-                                           const float (&a)[8]) {
-  float o[8];
+__device__ __forceinline__ void epi_fetch8(const GemmArgs& p, const float* C_f32, long ldc, int row, int col,
+                                           EpiX<T, EPI>& x) {
   const bool full = col + 8 <= p.N;
   if constexpr (EPI == EPI_F32) {
-    float* dst = C_f32 + (size_t)row * ldc + col;
+    if (!p.accumulate) return;
+    const float* src = C_f32 + (size_t)row * ldc + col;
     if (full) {
-      f32x4 v0 = {a[0], a[1], a[2], a[3]}, v1 = {a[4], a[5], a[6], a[7]};
-      if (p.accumulate) {
-        v0 += reinterpret_cast<const f32x4*>(dst)[0];
-        v1 += reinterpret_cast<const f32x4*>(dst)[1];
-      }
-      reinterpret_cast<f32x4*>(dst)[0] = v0;
-      reinterpret_cast<f32x4*>(dst)[1] = v1;
+      x.w[0] = reinterpret_cast<const u32x4*>(src)[0];
+      x.w[1] = reinterpret_cast<const u32x4*>(src)[1];
     } else {
-      for (int e = 0; e < 8 && col + e < p.N; ++e) dst[e] = p.accumulate ? dst[e] + a[e] : a[e];
-    }
-    return;
-  } else {
-    constexpr int VEC = Elt<T>::VEC;
-    const T* bias = reinterpret_cast<const T*>(p.bias);
-    const T* aux = reinterpret_cast<const T*>(p.aux);
-    float bv[8], xv[8];
+      V16<float> t[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bv[e] = xv[e] = 0.f;
+      for (int e = 0; e < 8; ++e) t[e / 4].v[e % 4] = col + e < p.N ? src[e] : 0.f;
+      x.w[0] = t[0].pack();
+      x.w[1] = t[1].pack();
+    }
+  } else if constexpr (EPI == EPI_RESID || EPI == EPI_GELU_BWD) {
+    constexpr int VEC = Elt<T>::VEC;
+    const T* src = reinterpret_cast<const T*>(p.aux) + (size_t)row * p.ldaux + col;
     if (full) {
+#pragma unroll
+      for (int h = 0; h < 8 / VEC; ++h) x.w[h] = reinterpret_cast<const u32x4*>(src)[h];
+    } else {
 #pragma unroll
       for (int h = 0; h < 8 / VEC; ++h) {
         V16<T> t;
-        if ((EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID) && bias) {
-          t.load(bias + col + h * VEC);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) bv[h * VEC + e] = t.v[e];
-        }
-        if (EPI == EPI_RESID || EPI == EPI_GELU_BWD) {
-          t.load(aux + (size_t)row * p.ldaux + col + h * VEC);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) xv[h * VEC + e] = t.v[e];
-        }
+        for (int e = 0; e < VEC; ++e) t.v[e] = col + h * VEC + e < p.N ? ld1(src, h * VEC + e) : 0.f;
+        x.w[h] = t.pack();
       }
+    }
+  }
+}
+
+// Apply the epilogue to 8 consecutive columns of one row and store them (16-byte vectors when
+// the chunk is whole, element by element at the right edge). bv: bias of the 8 columns.
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long ldc, int row, int col,
+                                           const float (&a)[8], const float (&bv)[8], const EpiX<T, EPI>& x) {
+  const bool full = col + 8 <= p.N;
+  if constexpr (EPI == EPI_F32) {
+    float* dst = C_f32 + (size_t)row * ldc + col;
+    V16<float> v[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e / 4].v[e % 4] = a[e];
+    if (p.accumulate) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        V16<float> o;
+        o.unpack(x.w[h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[h].v[e] += o.v[e];
+      }
+    }
+    if (full) {
+      v[0].store(dst);
+      v[1].store(dst + 4);
     } else {
-      for (int e = 0; e < 8 && col + e < p.N; ++e) {
-        if ((EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID) && bias) bv[e] = ld1(bias, col + e);
-        if (EPI == EPI_RESID || EPI == EPI_GELU_BWD) xv[e] = ld1(aux, (size_t)row * p.ldaux + col + e);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < p.N) dst[e] = v[e / 4].v[e % 4];
+    }
+  } else {
+    constexpr int VEC = Elt<T>::VEC;
+    float xv[8], o[8];
+    if constexpr (EPI == EPI_RESID || EPI == EPI_GELU_BWD) {
+#pragma unroll
+      for (int h = 0; h < 8 / VEC; ++h) {
+        V16<T> t;
+        t.unpack(x.w[h]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xv[h * VEC + e] = t.v[e];
       }
     }
 #pragma unroll
@@ -390,9 +426,12 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
         }
       }
     } else {
-      for (int e = 0; e < 8 && col + e < p.N; ++e) {
-        st1(dst, e, o[e]);
-        if constexpr (EPI == EPI_GELU) st1(reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col, e, gelu_fwd(o[e]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (col + e < p.N) {
+          st1(dst, e, o[e]);
+          if constexpr (EPI == EPI_GELU) st1(reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col, e, gelu_fwd(o[e]));
+        }
       }
     }
   }
@@ -575,28 +614,67 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
   }
   float* stage = reinterpret_cast<float*>(smem) + w * 32 * CF::EPI_LD;
   const int g = lane >> 5, l32 = lane & 31;
-  constexpr int CPR = TN / 8;  // 8-column chunks per staged row
+  constexpr int CPR = TN / 8;             // 8-column chunks per staged row
+  constexpr int NIT = (32 * CPR) / 64;    // chunks per lane per slab
+  static_assert(64 % CPR == 0, "a lane keeps its column chunk across a slab");
+  const int cc = (lane % CPR) * 8;
+  const int col = n0 + wn * TN + cc;
+  float bv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID) {
+    if (p.bias && col < p.N) {
+      const T* bias = reinterpret_cast<const T*>(p.bias) + col;
+      if (col + 8 <= p.N) {
+        constexpr int VEC = Elt<T>::VEC;
+#pragma unroll
+        for (int h = 0; h < 8 / VEC; ++h) {
+          V16<T> t;
+          t.load(bias + h * VEC);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) bv[h * VEC + e] = t.v[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < p.N) bv[e] = ld1(bias, e);
+      }
+    }
+  }
+  // the staging area is private to the wave: wave-level ordering is enough
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    const int row0 = m0 + wm * TM + i * 32;
+    EpiX<T, EPI> xs[NIT];
+    if constexpr (EpiX<T, EPI>::USED) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int row = row0 + (it * 64 + lane) / CPR;
+        if (row < p.M && col < p.N) epi_fetch8<T, EPI>(q, C_f32, ldc, row, col, xs[it]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) stage[((r >> 2) * 8 + g * 4 + (r & 3)) * CF::EPI_LD + j * 32 + l32] = acc[i][j][r];
-    __syncthreads();
+    wave_sync();
 #pragma unroll
-    for (int it = 0; it < (32 * CPR) / 64; ++it) {
-      const int id = it * 64 + lane;
-      const int rr = id / CPR, cc = (id % CPR) * 8;
-      const int row = m0 + wm * TM + i * 32 + rr;
-      const int col = n0 + wn * TN + cc;
+    for (int it = 0; it < NIT; ++it) {
+      const int rr = (it * 64 + lane) / CPR;
+      const int row = row0 + rr;
       if (row < p.M && col < p.N) {
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc + 4);
         const float a8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8);
+        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv, xs[it]);
       }
     }
-    __syncthreads();
+    wave_sync();
   }
 }
 
