@@ -10,16 +10,17 @@
 //  * Two block tiles, both with 4 waves in a 2x2 grid: 256x256 (128x128 per wave = 4x4 MFMA
 //    32x32 blocks, 256 accumulator registers) for the wide products, 128x128 (64x64 per wave)
 //    for N = C products and split-K weight gradients, chosen per shape so the grid covers the
-//    256 CUs in whole rounds. bf16: v_mfma_f32_32x32x16_bf16, BK = 64; fp32:
-//    v_mfma_f32_32x32x2f32, BK = 32.
-//  * LDS holds both operands as [row][k], so every MFMA operand is one 16-byte LDS read per lane.
-//    K-contiguous operands are stored unpadded with the 16-byte chunks of row r XOR-swizzled by
-//    r & 7 (conflict-free fragment reads) and, for interior tiles, copied global -> LDS directly
-//    with global_load_lds_dwordx4 (no staging registers, no LDS write instructions). Edge tiles
-//    and M/N-contiguous operands (the transposed side of NN / TN products) go through registers;
-//    the latter are loaded as 4 x 16 B row pieces and transposed in registers into padded rows.
-//  * Double-buffered LDS: the copies of tile k+1 are in flight while tile k is multiplied
-//    (64 MFMAs per wave per tile on the 256x256 tile); one barrier per tile.
+//    256 CUs in whole rounds. bf16: v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2f32.
+//  * K-contiguous bf16 products (the forward GEMMs) stage 64 of K per tile; their interior tiles
+//    are copied global -> LDS directly (global_load_lds_dwordx4: no staging registers, no LDS
+//    write instructions) into [row][k] rows whose 16-byte chunks are XOR-swizzled so that the
+//    MFMA fragment reads are free of bank conflicts.
+//  * Products with a row-contiguous operand (input and weight gradients) stage 32 of K per tile
+//    through registers; the row-contiguous side stays [k][row] in LDS and its MFMA fragments are
+//    read with the gfx950 transpose load ds_read_b64_tr_b16. (Those reads are kept away from
+//    direct copies: the compiler makes each of them wait for every copy in flight.)
+//  * Double-buffered LDS, one barrier per tile; operand fragments double-buffered in registers
+//    so the LDS reads of one k-step overlap the MFMAs of the previous one.
 //  * Epilogue through LDS: each wave parks 32 rows of fp32 accumulators in LDS and reads them back
 //    row-contiguous, so bias / residual / GELU inputs are read and results written as 16-byte
 //    coalesced vectors.
@@ -36,7 +37,6 @@ template <typename T> struct Mma;
 template <> struct Mma<bf16> {
   static constexpr int KSTEP = 16;  // k per instruction
   static constexpr int KPL = 8;     // k elements supplied by one lane
-  static constexpr int BK = 64;
   typedef bf16x8 frag;
   __device__ static frag load(const bf16* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -48,7 +48,6 @@ template <> struct Mma<bf16> {
 template <> struct Mma<float> {
   static constexpr int KSTEP = 2;
   static constexpr int KPL = 1;
-  static constexpr int BK = 32;
   typedef float frag;
   __device__ static frag load(const float* p) { return *p; }
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
@@ -58,9 +57,6 @@ template <> struct Mma<float> {
 
 #ifndef GEMM_SCHED_HINT
 #define GEMM_SCHED_HINT __builtin_amdgcn_iglp_opt(1)
-#endif
-#ifndef GEMM_FRAG_DB
-#define GEMM_FRAG_DB 1
 #endif
 constexpr int NTHR = 256, WGM = 2, WGN = 2;
 constexpr int GROUP_M = 8;
@@ -86,18 +82,21 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Interior tiles of modes 0 and 2 are copied global -> LDS with global_load_lds_dwordx4 (lane l
 // of a wave lands at LDS base + 16 l, so each lane fetches the global chunk that belongs there);
 // edge tiles and mode 1 go through registers, with out-of-range elements zeroed.
-template <typename T, bool KC, int ROWS> struct Operand {
+template <typename T, bool KC, int ROWS, int BK_> struct Operand {
   static constexpr int VEC = Elt<T>::VEC;
-  static constexpr int BK = Mma<T>::BK;
+  static constexpr int BK = BK_;
   static constexpr int MODE = KC ? 0 : (sizeof(T) == 2 ? 2 : 1);
-  static constexpr bool DIRECT = MODE != 1;  // interior tiles can be copied global -> LDS
+  // interior tiles can be copied global -> LDS (mode 2 is not: the compiler waits for every
+  // pending global -> LDS copy before each ds_read_b64_tr_b16, which would serialise the pipeline)
+  static constexpr bool DIRECT = MODE == 0;
   static constexpr int LD = MODE == 0 ? BK : BK + VEC;  // [row][k] pitch (elements), modes 0 / 1
   // mode 2 geometry
   static constexpr int RB = 512 / ROWS;             // k-rows per 1024-byte block
   static constexpr int BLK = (1024 + 64) / 2;       // block pitch (elements)
   static constexpr int NBLK = BK / RB;              // blocks per stage
   static constexpr int ELEMS = MODE == 2 ? NBLK * BLK : ROWS * LD;  // one stage
-  static_assert(MODE != 0 || BK / VEC == 8, "the swizzle assumes 8 chunks per row");
+  static constexpr int CPK = BK / VEC;  // 16-byte chunks per [row][k] row, mode 0
+  static_assert(MODE != 0 || CPK == 4 || CPK == 8, "the swizzle assumes 4 or 8 chunks per row");
   static_assert(MODE != 2 || ((ROWS == 128 || ROWS == 256) && NBLK % 4 == 0), "mode 2 tile shape");
   static constexpr int NV_K = (ROWS * BK / VEC) / NTHR;           // 16-byte vectors per thread
   static constexpr int NV_T = ((BK / TKR) * (ROWS / VEC)) / NTHR;  // transposed pieces per thread
@@ -105,11 +104,20 @@ template <typename T, bool KC, int ROWS> struct Operand {
   static_assert(NREG > 0, "tile too small for the thread count");
   u32x4 r[NREG];
 
+  // mode 0: chunk c of row r sits at chunk position c ^ swz(r). The LDS serves a 16-byte read
+  // for 16 consecutive lanes per clock over 64 banks; the fragment read of 16 consecutive rows at
+  // one chunk then touches every bank once.
+  __device__ __forceinline__ static int swz(int row) {
+    if constexpr (CPK == 8) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
+  }
   // element offset of (row, k) inside one stage, modes 0 and 1
   __device__ __forceinline__ static int idx(int row, int k) {
-    if constexpr (MODE == 0) return row * BK + ((((k / VEC) ^ (row & 7)) * VEC) | (k % VEC));
+    if constexpr (MODE == 0) return row * BK + ((((k / VEC) ^ swz(row)) * VEC) | (k % VEC));
     else return row * LD + k;
   }
+  // direct copies per wave per tile
+  static constexpr int NDIRECT = MODE == 0 ? (ROWS / (NTHR / 64)) / (64 / CPK) : NBLK / (NTHR / 64);
 
   // mode 2: block j of wave w; lane l holds (k-row, first row element) of its 16 bytes
   __device__ __forceinline__ static void tr_slot(int b, int lane, int& k, int& m) {
@@ -164,11 +172,12 @@ template <typename T, bool KC, int ROWS> struct Operand {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if constexpr (MODE == 0) {
       constexpr int RPW = ROWS / (NTHR / 64);  // rows per wave
+      constexpr int RPI = 64 / CPK;            // rows per wave-wide copy
 #pragma unroll
-      for (int j = 0; j < RPW / 8; ++j) {
-        const int rb = w * RPW + j * 8;
-        const int rr = rb + (lane >> 3);
-        const int c = (lane & 7) ^ (rr & 7);
+      for (int j = 0; j < RPW / RPI; ++j) {
+        const int rb = w * RPW + j * RPI;
+        const int rr = rb + lane / CPK;
+        const int c = (lane % CPK) ^ swz(rr);
         const T* g = ptr + (size_t)(row0 + rr) * ld + k0 + c * VEC;
         __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds + rb * BK), 16, 0, 0);
       }
@@ -185,75 +194,58 @@ template <typename T, bool KC, int ROWS> struct Operand {
     }
   }
 
-  // Register path. Interior tiles take straight-line unchecked loads; edge tiles clamp the address
-  // to a valid one and zero the out-of-range elements with selects (loads stay in one block).
-  __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
+  // Register path. load() only issues the loads (straight-line on interior tiles; on edge tiles
+  // out-of-range addresses are clamped to a valid one); store() zeroes the out-of-range elements
+  // of edge tiles and writes LDS, so no instruction between the two waits for the loads.
+  // Per vector i of this thread: its row (M/N side) and k, relative to the tile.
+  __device__ __forceinline__ static void coords(int i, int& row, int& k) {
     const int tid = threadIdx.x;
-    const bool inner = interior(row0, nrows, k0, K);
     if constexpr (MODE == 2) {
-      // same lane -> slot map as the direct copy; used for edge tiles only
-      const int lane = tid & 63, w = tid >> 6;
       constexpr int BPW = NBLK / (NTHR / 64);
-#pragma unroll
-      for (int j = 0; j < BPW; ++j) {
-        int k, m;
-        tr_slot(w * BPW + j, lane, k, m);
-        k += k0;
-        m += row0;
-        const bool ok = k < K && m < nrows;
-        const T* src = ok ? ptr + (size_t)k * ld + m : ptr;
-        r[j] = keep_first(*reinterpret_cast<const u32x4*>(src), ok ? nrows - m : 0);
-      }
+      tr_slot((tid >> 6) * BPW + i, tid & 63, k, row);  // 8 consecutive rows at one k
     } else if constexpr (MODE == 0) {
-      if (inner) {
-#pragma unroll
-        for (int i = 0; i < NV_K; ++i) {
-          const int v = i * NTHR + tid;
-          const int row = v / (BK / VEC);
-          const int kc = (v % (BK / VEC)) * VEC;
-          r[i] = *reinterpret_cast<const u32x4*>(ptr + (size_t)(row0 + row) * ld + k0 + kc);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NV_K; ++i) {
-          const int v = i * NTHR + tid;
-          const int row = v / (BK / VEC);
-          const int k = k0 + (v % (BK / VEC)) * VEC;
-          const bool ok = row0 + row < nrows && k < K;
-          const T* src = ok ? ptr + (size_t)(row0 + row) * ld + k : ptr;
-          r[i] = keep_first(*reinterpret_cast<const u32x4*>(src), ok ? K - k : 0);
-        }
-      }
+      const int v = i * NTHR + tid;
+      row = v / CPK;
+      k = (v % CPK) * VEC;  // VEC consecutive k of one row
     } else {
+      const int pc = (i / TKR) * NTHR + tid;
+      k = (pc % (BK / TKR)) * TKR + i % TKR;
+      row = (pc / (BK / TKR)) * VEC;  // VEC consecutive rows at one k
+    }
+  }
+  // elements of vector i that are in range (0 when it is out of range altogether)
+  __device__ __forceinline__ static int keep_count(int i, int row0, int nrows, int k0, int K) {
+    int row, k;
+    coords(i, row, k);
+    row += row0;
+    k += k0;
+    if constexpr (MODE == 0) return row < nrows && k < K ? K - k : 0;
+    else return k < K && row < nrows ? nrows - row : 0;
+  }
+
+  __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
+    const bool inner = interior(row0, nrows, k0, K);
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      int row, k;
+      coords(i, row, k);
+      row += row0;
+      k += k0;
+      const size_t off = MODE == 0 ? (size_t)row * ld + k : (size_t)k * ld + row;
       if (inner) {
-#pragma unroll
-        for (int i = 0; i < NV_T; ++i) {
-          const int pc = i * NTHR + tid;
-          const int kr = (pc % (BK / TKR)) * TKR;
-          const int mc = (pc / (BK / TKR)) * VEC;
-#pragma unroll
-          for (int j = 0; j < TKR; ++j)
-            r[i * TKR + j] = *reinterpret_cast<const u32x4*>(ptr + (size_t)(k0 + kr + j) * ld + row0 + mc);
-        }
+        r[i] = *reinterpret_cast<const u32x4*>(ptr + off);
       } else {
-#pragma unroll
-        for (int i = 0; i < NV_T; ++i) {
-          const int pc = i * NTHR + tid;
-          const int kr = (pc % (BK / TKR)) * TKR;
-          const int m = row0 + (pc / (BK / TKR)) * VEC;
-#pragma unroll
-          for (int j = 0; j < TKR; ++j) {
-            const int k = k0 + kr + j;
-            const bool ok = k < K && m < nrows;
-            const T* src = ok ? ptr + (size_t)k * ld + m : ptr;
-            r[i * TKR + j] = keep_first(*reinterpret_cast<const u32x4*>(src), ok ? nrows - m : 0);
-          }
-        }
+        const bool ok = MODE == 0 ? (row < nrows && k < K) : (k < K && row < nrows);
+        r[i] = *reinterpret_cast<const u32x4*>(ok ? ptr + off : ptr);
       }
     }
   }
 
-  __device__ __forceinline__ void store(T* __restrict__ lds) const {
+  __device__ __forceinline__ void store(T* __restrict__ lds, int row0, int nrows, int k0, int K) {
+    if (!interior(row0, nrows, k0, K)) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) r[i] = keep_first(r[i], keep_count(i, row0, nrows, k0, K));
+    }
     const int tid = threadIdx.x;
     if constexpr (MODE == 2) {
       const int lane = tid & 63, w = tid >> 6;
@@ -263,10 +255,9 @@ template <typename T, bool KC, int ROWS> struct Operand {
     } else if constexpr (MODE == 0) {
 #pragma unroll
       for (int i = 0; i < NV_K; ++i) {
-        const int v = i * NTHR + tid;
-        const int row = v / (BK / VEC);
-        const int kc = (v % (BK / VEC)) * VEC;
-        *reinterpret_cast<u32x4*>(lds + idx(row, kc)) = r[i];
+        int row, k;
+        coords(i, row, k);
+        *reinterpret_cast<u32x4*>(lds + idx(row, k)) = r[i];
       }
     } else {
 #pragma unroll
@@ -307,13 +298,20 @@ template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int TM = BM / WGM, TN = BN / WGN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int BK = Mma<T>::BK;
-  using OA = Operand<T, AKC, BM>;
-  using OB = Operand<T, BKC, BN>;
+  // k per LDS stage: 64 when both bf16 operands are K-contiguous (direct copies, 64 MFMAs per
+  // wave between barriers), else 32 (register staging; half the staging registers)
+  static constexpr int BK = sizeof(T) == 2 && AKC && BKC ? 64 : 32;
+  // bf16 K-contiguous products are scheduled with the MFMA / LDS interleave hint
+  static constexpr bool HINT = sizeof(T) == 2 && AKC && BKC;
+  using OA = Operand<T, AKC, BM, BK>;
+  using OB = Operand<T, BKC, BN, BK>;
   static constexpr int STAGE = OA::ELEMS + OB::ELEMS;  // elements per LDS stage
+  static constexpr int NS = 2;  // LDS stages
   static constexpr int EPI_LD = TN + 4;                 // epilogue staging pitch (floats)
-  static constexpr size_t LDS_BYTES = 2ull * STAGE * sizeof(T);
-  static_assert(LDS_BYTES >= (size_t)4 * 32 * EPI_LD * 4, "epilogue staging must fit");
+  static constexpr size_t OPS_BYTES = (size_t)NS * STAGE * sizeof(T);
+  static constexpr size_t EPI_BYTES = (size_t)4 * 32 * EPI_LD * 4;
+  static constexpr size_t LDS_BYTES = OPS_BYTES > EPI_BYTES ? OPS_BYTES : EPI_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 // Per 8-column chunk, the epilogue inputs besides the accumulators: the residual / GELU input
@@ -437,9 +435,10 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
   }
 }
 
-// The K loop of one block. DA / DB: every tile of that operand in this block is interior and
-// K-contiguous, so it is copied global -> LDS directly; otherwise it goes through registers.
-template <typename T, int BM, int BN, bool AKC, bool BKC, bool DA, bool DB>
+// The K loop of one block. DIRECT: every tile of both operands is interior and K-contiguous and
+// is copied global -> LDS directly, NS - 1 tiles ahead through NS LDS stages (one barrier per
+// tile). Otherwise the tiles go through registers.
+template <typename T, int BM, int BN, bool AKC, bool BKC, bool DIRECT>
 __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0, int kbeg, int kend, T* st0,
                                               f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
   using CF = Cfg<T, BM, BN, AKC, BKC>;
@@ -457,29 +456,6 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
   const int w = threadIdx.x >> 6;
   const int wm = w / WGN, wn = w % WGN;
 
-  struct Empty {};
-  struct NoRegs {
-    __device__ void load(const T*, long, int, int, int, int) {}
-    __device__ void store(T*) const {}
-  };
-  using RA = typename std::conditional<DA, NoRegs, OA>::type;
-  using RB = typename std::conditional<DB, NoRegs, OB>::type;
-  RA la;
-  RB lb;
-  auto fetch = [&](int k0, int stg) {
-    if constexpr (DA) OA::issue_direct(A, p.lda, m0, k0, Abuf(stg));
-    else la.load(A, p.lda, m0, p.M, k0, kend);
-    if constexpr (DB) OB::issue_direct(B, p.ldb, n0, k0, Bbuf(stg));
-    else lb.load(B, p.ldb, n0, p.N, k0, kend);
-  };
-  if (nkt > 0) {
-    fetch(kbeg, 0);
-    la.store(Abuf(0));
-    lb.store(Bbuf(0));
-  }
-  if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
   const int arow = wm * TM + (lane & 31);
   const int brow = wn * TN + (lane & 31);
   const int kofs = (lane >> 5) * MM::KPL;
@@ -495,16 +471,9 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
     if constexpr (OB::MODE == 2) return OB::tr_frag(bs, btr, j, st);
     else return MM::load(bs + OB::idx(brow + j * 32, st * MM::KSTEP + kofs));
   };
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) fetch(kbeg + (kt + 1) * BK, cur ^ 1);
-    const T* as = Abuf(cur);
-    const T* bs = Bbuf(cur);
-#if GEMM_FRAG_DB
-    // operand fragments are double-buffered: the LDS reads of k-step s+1 are issued before the
-    // MFMAs of k-step s, so their latency hides behind FM*FN MFMAs
+  // all MFMAs of one staged tile; operand fragments are double-buffered: the LDS reads of k-step
+  // s+1 are issued before the MFMAs of k-step s, so their latency hides behind FM*FN MFMAs
+  auto compute = [&](const T* as, const T* bs) {
     constexpr int KS = BK / MM::KSTEP;
     typename MM::frag fa[2][FM], fb[2][FN];
 #pragma unroll
@@ -525,27 +494,62 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[cb][i], fb[cb][j], acc[i][j]);
     }
-#else
+  };
+
+  if constexpr (DIRECT) {
+    constexpr int NS = CF::NS;
+    static_assert(NS >= 2, "stages");
+    // copies in flight per wave while tile kt is consumed: those of tiles kt+1 .. kt+NS-2
+    constexpr int WAIT_N = (NS - 2) * (OA::NDIRECT + OB::NDIRECT);
+    static_assert(WAIT_N < 64, "vmcnt range");
+    constexpr int WAIT_IMM = (WAIT_N & 15) | (7 << 4) | (15 << 8) | ((WAIT_N >> 4) << 14);
+    auto issue = [&](int t) {
+      OA::issue_direct(A, p.lda, m0, kbeg + t * BK, Abuf(t % NS));
+      OB::issue_direct(B, p.ldb, n0, kbeg + t * BK, Bbuf(t % NS));
+    };
 #pragma unroll
-    for (int st = 0; st < BK / MM::KSTEP; ++st) {
-      typename MM::frag fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = fragA(as, i, st);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = fragB(bs, j, st);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[i], fb[j], acc[i][j]);
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < nkt) issue(t);
+    for (int kt = 0; kt < nkt; ++kt) {
+      // loads return in order: this wave's copies of tile kt have landed once at most WAIT_N remain
+      if (kt + NS - 2 < nkt) __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+      else __builtin_amdgcn_s_waitcnt(0);
+      // Every wave's copies of tile kt have landed and every wave is done with stage (kt-1) % NS
+      // (its fragments fed MFMAs already issued). A bare s_barrier: a workgroup fence here would
+      // make the compiler wait for all copies in flight.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NS - 1 < nkt) issue(kt + NS - 1);
+      compute(Abuf(kt % NS), Bbuf(kt % NS));
+      if constexpr (CF::HINT) GEMM_SCHED_HINT;
     }
-#endif
-    GEMM_SCHED_HINT;
-    if (more) {
-      la.store(Abuf(cur ^ 1));
-      lb.store(Bbuf(cur ^ 1));
+    __syncthreads();  // the epilogue reuses the LDS
+  } else {
+    OA la;
+    OB lb;
+    if (nkt > 0) {
+      la.load(A, p.lda, m0, p.M, kbeg, kend);
+      lb.load(B, p.ldb, n0, p.N, kbeg, kend);
+      la.store(Abuf(0), m0, p.M, kbeg, kend);
+      lb.store(Bbuf(0), n0, p.N, kbeg, kend);
     }
-    if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);  // direct copies of the next stage landed
     __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nkt;
+      if (more) {
+        la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * BK, kend);
+        lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend);
+      }
+      compute(Abuf(cur), Bbuf(cur));
+      if constexpr (CF::HINT) GEMM_SCHED_HINT;
+      if (more) {
+        la.store(Abuf(cur ^ 1), m0, p.M, kbeg + (kt + 1) * BK, kend);
+        lb.store(Bbuf(cur ^ 1), n0, p.N, kbeg + (kt + 1) * BK, kend);
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -584,21 +588,14 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  constexpr bool XA = CF::OA::DIRECT, XB = CF::OB::DIRECT;
   const bool kfull = (kend - kbeg) % BK == 0;
-  const bool da = XA && kfull && m0 + BM <= p.M;
-  const bool db = XB && kfull && n0 + BN <= p.N;
-  if constexpr (XA && XB) {
-    if (da && db) gemm_mainloop<T, BM, BN, AKC, BKC, true, true>(p, m0, n0, kbeg, kend, st0, acc);
-    else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
-  } else if constexpr (XA) {
-    if (da) gemm_mainloop<T, BM, BN, AKC, BKC, true, false>(p, m0, n0, kbeg, kend, st0, acc);
-    else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
-  } else if constexpr (XB) {
-    if (db) gemm_mainloop<T, BM, BN, AKC, BKC, false, true>(p, m0, n0, kbeg, kend, st0, acc);
-    else gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
+  if constexpr (CF::OA::DIRECT && CF::OB::DIRECT) {
+    if (kfull && m0 + BM <= p.M && n0 + BN <= p.N)
+      gemm_mainloop<T, BM, BN, AKC, BKC, true>(p, m0, n0, kbeg, kend, st0, acc);
+    else
+      gemm_mainloop<T, BM, BN, AKC, BKC, false>(p, m0, n0, kbeg, kend, st0, acc);
   } else {
-    gemm_mainloop<T, BM, BN, AKC, BKC, false, false>(p, m0, n0, kbeg, kend, st0, acc);
+    gemm_mainloop<T, BM, BN, AKC, BKC, false>(p, m0, n0, kbeg, kend, st0, acc);
   }
 
   // ---- epilogue: 32-row slabs of each wave go through LDS, then 16-byte row chunks out
@@ -738,7 +735,8 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
   if (epi == EPI_F32 && scratch) splits = gemm_splits_t(a.M, a.N, a.K, scratch_floats, BM);
   int k_split = a.K;
   if (splits > 1) {
-    k_split = cdiv(cdiv(a.K, splits), Mma<T>::BK) * Mma<T>::BK;
+    constexpr int BK = Cfg<T, BM, BN, AKC, BKC>::BK;
+    k_split = cdiv(cdiv(a.K, splits), BK) * BK;
     splits = cdiv(a.K, k_split);
   }
   dim3 grid(tiles, 1, splits);
