@@ -221,10 +221,12 @@ static void f32_fwd(int B, int T, int H, const float* qkv, float* out, float* ls
 }
 template <int HS>
 static void f32_bwd(int B, int T, int H, const float* qkv, const float* dout, const float* lse, const float* dvec,
-                    float* dqkv, hipStream_t s) {
+                    float* dqkv, int parts, hipStream_t s) {
   dim3 grid(cdiv(T, AT), B * H);
-  attn_bwd_kv_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, dout, lse, dvec, dqkv, 1.0f / sqrtf((float)HS));
-  attn_bwd_q_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, dout, lse, dvec, dqkv, 1.0f / sqrtf((float)HS));
+  if (parts & ATT_BWD_KV)
+    attn_bwd_kv_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, dout, lse, dvec, dqkv, 1.0f / sqrtf((float)HS));
+  if (parts & ATT_BWD_Q)
+    attn_bwd_q_f32<HS><<<grid, AT, 0, s>>>(T, H, qkv, dout, lse, dvec, dqkv, 1.0f / sqrtf((float)HS));
 }
 
 // =====================================================================================
@@ -669,22 +671,24 @@ hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const voi
 }
 
 hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
-                                const void* dout, const float* lse, void* dqkv, float* dvec, hipStream_t s) {
+                                const void* dout, const float* lse, void* dqkv, float* dvec, int parts,
+                                hipStream_t s) {
   if (B * T <= 0) return hipSuccess;
   const int BT = B * T;
   if (dt == DT_BF16) {
     if (hs != HD) return hipErrorInvalidValue;
-    attn_bwd_dvec<bf16, HD><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, reinterpret_cast<const bf16*>(out),
-                                                                    reinterpret_cast<const bf16*>(dout), dvec);
+    if (parts & ATT_BWD_PRE)
+      attn_bwd_dvec<bf16, HD><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, reinterpret_cast<const bf16*>(out),
+                                                                      reinterpret_cast<const bf16*>(dout), dvec);
     dim3 grid(cdiv(T, BQ), B * H);
     auto Q = reinterpret_cast<const uint16_t*>(qkv);
     auto dO = reinterpret_cast<const uint16_t*>(dout);
     auto dQ = reinterpret_cast<uint16_t*>(dqkv);
-    attn_bwd_kv_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
-    attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
+    if (parts & ATT_BWD_KV) attn_bwd_kv_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
+    if (parts & ATT_BWD_Q) attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
     return hipGetLastError();
   }
-  {
+  if (parts & ATT_BWD_PRE) {
     auto O_ = reinterpret_cast<const float*>(out);
     auto dO_ = reinterpret_cast<const float*>(dout);
     const int nb = cdiv((long)BT * H, 256);
@@ -701,11 +705,11 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
   auto dO = reinterpret_cast<const float*>(dout);
   auto dQ = reinterpret_cast<float*>(dqkv);
   switch (hs) {
-    case 4: f32_bwd<4>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
-    case 8: f32_bwd<8>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
-    case 16: f32_bwd<16>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
-    case 32: f32_bwd<32>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
-    case 64: f32_bwd<64>(B, T, H, Q, dO, lse, dvec, dQ, s); break;
+    case 4: f32_bwd<4>(B, T, H, Q, dO, lse, dvec, dQ, parts, s); break;
+    case 8: f32_bwd<8>(B, T, H, Q, dO, lse, dvec, dQ, parts, s); break;
+    case 16: f32_bwd<16>(B, T, H, Q, dO, lse, dvec, dQ, parts, s); break;
+    case 32: f32_bwd<32>(B, T, H, Q, dO, lse, dvec, dQ, parts, s); break;
+    case 64: f32_bwd<64>(B, T, H, Q, dO, lse, dvec, dQ, parts, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

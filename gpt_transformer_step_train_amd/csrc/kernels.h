@@ -67,8 +67,10 @@ size_t encoder_bwd_partial_floats(int BT, int C);
 hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const void* qkv, void* out,
                                 float* lse, hipStream_t s);
 // dqkv [B,T,3C] is fully written. `dvec` holds B*H*T floats of scratch.
+// parts: any of ATT_BWD_PRE (D = rowsum(dO * O)), ATT_BWD_KV (dK, dV), ATT_BWD_Q (dQ), in that order
+constexpr int ATT_BWD_PRE = 1, ATT_BWD_KV = 2, ATT_BWD_Q = 4, ATT_BWD_ALL = 7;
 hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
-                                const void* dout, const float* lse, void* dqkv, float* dvec,
+                                const void* dout, const float* lse, void* dqkv, float* dvec, int parts,
                                 hipStream_t s);
 
 // Softmax cross-entropy over the first V columns of each row (row stride ld).

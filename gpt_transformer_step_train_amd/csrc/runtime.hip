@@ -493,8 +493,19 @@ int backward_impl() {
       if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.attprojb), acc, sc, sf, s));
     }
     {
+      ProfScope ps_(GPT2_K_ATTENTION_BWD_PRE);
+      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
+                                  ATT_BWD_PRE, s));
+    }
+    {
       ProfScope ps_(GPT2_K_ATTENTION_BWD);
-      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec, s));
+      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
+                                  ATT_BWD_KV, s));
+    }
+    {
+      ProfScope ps_(GPT2_K_ATTENTION_BWD_Q);
+      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
+                                  ATT_BWD_Q, s));
     }
     // qkv = ln1 Wqkv^T + b
     {
@@ -809,7 +820,7 @@ int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void*
 
 int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
                               const void* dout, const float* lse, void* dqkv, float* dvec, void* stream) {
-  return op_ret(launch_attention_bwd(to_dt(dtype), B, T, H, hs, qkv, out, dout, lse, dqkv, dvec,
+  return op_ret(launch_attention_bwd(to_dt(dtype), B, T, H, hs, qkv, out, dout, lse, dqkv, dvec, ATT_BWD_ALL,
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 

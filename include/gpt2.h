@@ -124,13 +124,15 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_GEMM_FC_DW 16
 #define GPT2_K_GEMM_ATTPROJ_DX 17
 #define GPT2_K_GEMM_ATTPROJ_DW 18
-#define GPT2_K_ATTENTION_BWD 19
+#define GPT2_K_ATTENTION_BWD 19      /* dK, dV                                */
 #define GPT2_K_GEMM_QKV_DX 20
 #define GPT2_K_GEMM_QKV_DW 21
 #define GPT2_K_ENCODER_BWD 22
 #define GPT2_K_GRAD_NORM 23
 #define GPT2_K_ADAMW 24
-#define GPT2_K_COUNT 25
+#define GPT2_K_ATTENTION_BWD_Q 25    /* dQ                                    */
+#define GPT2_K_ATTENTION_BWD_PRE 26  /* D = rowsum(dO * O) per query          */
+#define GPT2_K_COUNT 27
 int gpt2_profile_enable(uint32_t mask);
 int gpt2_profile_read(float* ms, int32_t* launches, int32_t n);
 

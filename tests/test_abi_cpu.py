@@ -41,6 +41,10 @@ def test_header_constants_match_binding():
     for k in ("GPT2_OK", "GPT2_EINVAL", "GPT2_ENOMEM", "GPT2_EHIP", "GPT2_ESTATE", "GPT2_ERANGE",
               "GPT2_ENONFINITE", "GPT2_FP32", "GPT2_BF16"):
         assert consts[k] == getattr(bd, k), k
+    classes = {k.lower(): int(v) for k, v in re.findall(r"#define GPT2_K_([A-Z0-9_]+) (\d+)", text)}
+    assert classes.pop("count") == len(bd.KERNEL_CLASSES)
+    for name, i in classes.items():
+        assert bd.KERNEL_CLASSES[i] == name
     ops = open(os.path.join(ROOT, "include", "gpt2_ops.h")).read()
     epi = dict((k, int(v)) for k, v in re.findall(r"#define GPT2_(EPI_[A-Z_0-9]+) (\d+)", ops))
     for k, v in epi.items():
