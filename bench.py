@@ -53,12 +53,15 @@ def class_work(name, w):
         return "mfma", 2.0 * M * N * K
     if name == "attention_fwd":      # QK^T and PV over the causal half
         return "mfma", 2.0 * B * H * T * T * hs
-    if name == "attention_bwd":      # dV, dP, dQ, dK (recompute not credited)
-        return "mfma", 4.0 * B * H * T * T * hs
+    if name == "attention_bwd":      # dK/dV kernel: dP, dV, dK (the recompute of P is not credited)
+        return "mfma", 3.0 * B * H * T * T * hs
+    if name == "attention_bwd_q":    # dQ kernel: dQ (the recomputes of P and dP are not credited)
+        return "mfma", 1.0 * B * H * T * T * hs
     e = 2  # bf16 activations
     N = num_params(w)
     bytes_ = {
         "encoder_fwd": BT * C * e * 2 + T * C * e + BT * 4,          # gather rows + wpe + write
+        "attention_bwd_pre": BT * C * e * 2 + BT * H * 4,            # read O and dO, write D
         "layernorm_fwd": BT * C * e * 2 + BT * 8 + 2 * C * e,
         "cross_entropy": BT * Vp * e * 2 + BT * 8,                   # read logits, write dlogits in place
         "layernorm_bwd": BT * C * e * 4 + BT * 8 + 2 * C * 4,         # dy, x, dres read+write

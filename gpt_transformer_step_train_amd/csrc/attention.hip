@@ -240,11 +240,18 @@ constexpr int BQ = 128;         // rows owned by a block (4 waves x 32)
 __device__ __forceinline__ bf16x8 lds_frag16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-// two 8-byte LDS reads: slots 0..3 from p0, 4..7 from p1
-__device__ __forceinline__ bf16x8 lds_frag8x2(const uint16_t* p0, const uint16_t* p1) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(p0);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(p1);
-  const u32x4 r = {a[0], a[1], b[0], b[1]};
+// MFMA operand whose k index runs down the rows of a [k][n] LDS tile (pitch LDP), read with
+// the gfx950 transpose load ds_read_b64_tr_b16 (lane 16G+i receives as element j the element
+// i & 3 of the 8 bytes addressed by lane 16G+4j+(i>>2)). Lane l gets column n = nb + l % 32 and
+// k-slots 0..3 = rows kb + 4(l / 32) + 0..3, slots 4..7 = rows kb + 8 + 4(l / 32) + 0..3: the
+// k order in which pack_frag lays out accumulator rows, so the two operands agree.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int kb, int nb, int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+  const int G = lane >> 4, t = lane & 15;
+  const uint16_t* p = tile + (kb + 4 * (G >> 1) + (t >> 2)) * LDP + nb + (G & 1) * 16 + 4 * (t & 3);
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)p));
+  const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(p + 8 * LDP)));
+  const u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8, r);
 }
 __device__ __forceinline__ bf16x8 pack_frag(const float* x) {  // 8 fp32 -> bf16x8
@@ -263,9 +270,8 @@ __device__ __forceinline__ f32x16 zero16() {
 // row (M index) of accumulator element i for lane group g (= lane / 32)
 __device__ __forceinline__ int acc_row(int i, int g) { return (i >> 2) * 8 + g * 4 + (i & 3); }
 
-// A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile). Row groups
-// vary fastest across lanes, so the transposed 8-byte LDS writes of 16 lanes fill one 128-byte
-// LDS row (no bank conflicts) while 4 lanes still read 64 contiguous bytes of each global row.
+// A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile); 4 lanes read
+// 64 contiguous bytes of each global row.
 struct Piece {
   u32x4 r[4];
   __device__ __forceinline__ static int rgrp(int p) { return (p & 15) * 4; }
@@ -283,22 +289,6 @@ struct Piece {
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + j) * LDP + cg) = r[j];
   }
-  __device__ __forceinline__ void store_cols(uint16_t* lds, int p) const {  // lds[col][row]
-    const int rg = rgrp(p), cg = cgrp(p);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d = c >> 1;
-      u32x2 o;
-      if ((c & 1) == 0) {
-        o[0] = (r[0][d] & 0xffffu) | (r[1][d] << 16);
-        o[1] = (r[2][d] & 0xffffu) | (r[3][d] << 16);
-      } else {
-        o[0] = (r[0][d] >> 16) | (r[1][d] & 0xffff0000u);
-        o[1] = (r[2][d] >> 16) | (r[3][d] & 0xffff0000u);
-      }
-      *reinterpret_cast<u32x2*>(lds + (cg + c) * LDP + rg) = o;
-    }
-  }
 };
 
 // ---------------------------------------------------------------- forward
@@ -306,7 +296,7 @@ struct Piece {
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint16_t* __restrict__ qkv,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * LDP];  // [d][key]
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
   const int nqt = gridDim.x;
   const int qt = nqt - 1 - blockIdx.x;  // heaviest tiles first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -340,8 +330,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
   };
   load_tile(0);
   for (int kt = 0; kt < ntiles; ++kt) {
-    if (is_k) pc.store_rows(Ks, p);
-    else pc.store_cols(Vt, p);
+    pc.store_rows(is_k ? Ks : Vs, p);
     __syncthreads();
     if (kt + 1 < ntiles) load_tile(kt + 1);
 #pragma unroll
@@ -386,12 +375,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 pf = pack_frag(sc + 8 * ks);
-        const int kofs = sb * 32 + 16 * ks + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const uint16_t* vrow = Vt + (db * 32 + l32) * LDP;
-          o[db] = mfma(lds_frag8x2(vrow + kofs, vrow + kofs + 8), pf, o[db]);
-        }
+        for (int db = 0; db < 2; ++db) o[db] = mfma(tr_frag(Vs, sb * 32 + 16 * ks, db * 32, lane), pf, o[db]);
       }
     }
     __syncthreads();
@@ -422,8 +407,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
                                                            uint16_t* __restrict__ dqkv) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[KT * LDP];   // [q][d]
   __shared__ __attribute__((aligned(16))) uint16_t dOs[KT * LDP];  // [q][d]
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[HD * LDP];   // [d][q]
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[HD * LDP];  // [d][q]
   __shared__ __attribute__((aligned(16))) float Ls[KT];
   __shared__ __attribute__((aligned(16))) float Dsh[KT];
   const int nkt = gridDim.x;
@@ -458,25 +441,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   Piece pc;
   const int p = tid & 127;
   const bool is_q = tid < 128;
+  float lnext = 0.f, dnext = 0.f;  // LSE and D of query tid of the next tile (tid < 64)
   auto load_tile = [&](int it) {
     const int qt0 = qstart + it * KT;
     if (is_q) pc.load(base + h * HD, C3, qt0, T, p);
     else pc.load(dbase + h * HD, C, qt0, T, p);
+    if (tid < KT) {
+      const int qr = qt0 + tid;
+      lnext = qr < T ? lse[(size_t)bh * T + qr] * LOG2E : 0.f;
+      dnext = qr < T ? dvec[(size_t)bh * T + qr] : 0.f;
+    }
   };
   if (ntiles > 0) load_tile(0);
   for (int it = 0; it < ntiles; ++it) {
     const int qt0 = qstart + it * KT;
-    if (is_q) {
-      pc.store_rows(Qs, p);
-      pc.store_cols(Qt, p);
-    } else {
-      pc.store_rows(dOs, p);
-      pc.store_cols(dOt, p);
-    }
+    pc.store_rows(is_q ? Qs : dOs, p);
     if (tid < KT) {
-      const int qr = qt0 + tid;
-      Ls[tid] = qr < T ? lse[(size_t)bh * T + qr] * LOG2E : 0.f;
-      Dsh[tid] = qr < T ? dvec[(size_t)bh * T + qr] : 0.f;
+      Ls[tid] = lnext;
+      Dsh[tid] = dnext;
     }
     __syncthreads();
     if (it + 1 < ntiles) load_tile(it + 1);
@@ -516,13 +498,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 pa = pack_frag(pr + 8 * ks);
         const bf16x8 sa = pack_frag(ds + 8 * ks);
-        const int qofs = 32 * qb + 16 * ks + 4 * g;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const uint16_t* dorow = dOt + (db * 32 + l32) * LDP;
-          const uint16_t* qrow = Qt + (db * 32 + l32) * LDP;
-          dv[db] = mfma(pa, lds_frag8x2(dorow + qofs, dorow + qofs + 8), dv[db]);
-          dk[db] = mfma(sa, lds_frag8x2(qrow + qofs, qrow + qofs + 8), dk[db]);
+          dv[db] = mfma(pa, tr_frag(dOs, 32 * qb + 16 * ks, db * 32, lane), dv[db]);
+          dk[db] = mfma(sa, tr_frag(Qs, 32 * qb + 16 * ks, db * 32, lane), dk[db]);
         }
       }
     }
@@ -554,7 +533,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
                                                           uint16_t* __restrict__ dqkv) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[HD * LDP];  // [d][key]
   const int nqt = gridDim.x;
   const int qt = nqt - 1 - blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -591,12 +569,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
   auto load_tile = [&](int kt) { pc.load(base + (is_k ? C : 2 * C) + h * HD, C3, kt * KT, T, p); };
   load_tile(0);
   for (int kt = 0; kt < ntiles; ++kt) {
-    if (is_k) {
-      pc.store_rows(Ks, p);
-      pc.store_cols(Kt, p);
-    } else {
-      pc.store_rows(Vs, p);
-    }
+    pc.store_rows(is_k ? Ks : Vs, p);
     __syncthreads();
     if (kt + 1 < ntiles) load_tile(kt + 1);
 #pragma unroll
@@ -620,16 +593,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
         }
         ds[i] = pv * (dpt[i] - Dq);
       }
-      // dQ += dS K : A = dS (rows q, k = keys) from the accumulator, B = K from Kt [d][key]
+      // dQ += dS K : A = dS (rows q, k = keys) from the accumulator, B = K read transposed
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 sa = pack_frag(ds + 8 * ks);
-        const int kofs = sb * 32 + 16 * ks + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const uint16_t* krow = Kt + (db * 32 + l32) * LDP;
-          dq[db] = mfma(sa, lds_frag8x2(krow + kofs, krow + kofs + 8), dq[db]);
-        }
+        for (int db = 0; db < 2; ++db) dq[db] = mfma(sa, tr_frag(Ks, sb * 32 + 16 * ks, db * 32, lane), dq[db]);
       }
     }
     __syncthreads();
