@@ -270,6 +270,23 @@ __device__ __forceinline__ f32x16 zero16() {
 // row (M index) of accumulator element i for lane group g (= lane / 32)
 __device__ __forceinline__ int acc_row(int i, int g) { return (i >> 2) * 8 + g * 4 + (i & 3); }
 
+// Grid (tiles, B*H) -> (b*h, work rank). Blocks are dealt round-robin to the 8 XCDs in linear
+// order; here XCD x takes the b*h range [x nbh/8, (x+1) nbh/8) whole (the tiles of one head
+// share its L2), and inside it the blocks run in order of decreasing causal work, so every XCD
+// gets the same share of heavy and light tiles. rank 0 = the heaviest tile.
+__device__ __forceinline__ void attn_block_map(int& bh, int& rank) {
+  const int ntile = gridDim.x, nbh = gridDim.y;
+  const int L = blockIdx.x + ntile * blockIdx.y;
+  if (nbh % 8 == 0) {
+    const int per = nbh / 8, xcd = L % 8, j = L / 8;
+    bh = xcd * per + j % per;
+    rank = j / per;
+  } else {
+    bh = L / ntile;
+    rank = L % ntile;
+  }
+}
+
 // A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile); 4 lanes read
 // 64 contiguous bytes of each global row.
 struct Piece {
@@ -297,13 +314,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
-  const int nqt = gridDim.x;
-  const int qt = nqt - 1 - blockIdx.x;  // heaviest tiles first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int bh, rank;
+  attn_block_map(bh, rank);
+  const int qt = gridDim.x - 1 - rank;  // the last query tiles see the most keys
+  const int b = bh / H, h = bh % H;
   const int C = H * HD;
   const long C3 = 3L * C;
   const uint16_t* base = qkv + (size_t)b * T * C3;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  // the wave index through readfirstlane: the compiler then keeps every per-wave bound below in
+  // scalar registers and branches on it instead of masking lanes
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5,
+            l32 = lane & 31;
   const int q0 = qt * BQ;
   const int qw0 = q0 + 32 * w;
   const int myq = qw0 + l32;
@@ -409,14 +430,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   __shared__ __attribute__((aligned(16))) uint16_t dOs[KT * LDP];  // [q][d]
   __shared__ __attribute__((aligned(16))) float Ls[KT];
   __shared__ __attribute__((aligned(16))) float Dsh[KT];
-  const int nkt = gridDim.x;
-  const int kt_blk = nkt - 1 - blockIdx.x;  // heaviest (earliest keys) first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int bh, rank;
+  attn_block_map(bh, rank);
+  const int kt_blk = rank;  // the first keys see the most queries
+  const int b = bh / H, h = bh % H;
   const int C = H * HD;
   const long C3 = 3L * C;
   const uint16_t* base = qkv + (size_t)b * T * C3;
   const uint16_t* dbase = dout + (size_t)b * T * C;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  // the wave index through readfirstlane: the compiler then keeps every per-wave bound below in
+  // scalar registers and branches on it instead of masking lanes
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5,
+            l32 = lane & 31;
   const int k0 = kt_blk * BQ;
   const int kw0 = k0 + 32 * w;
   const int mykey = kw0 + l32;
@@ -476,22 +501,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
       }
       // LSE (log2 units) and D of this lane's 16 accumulator rows: rows 32qb + 8*r4 + 4g + 0..3
       float pr[16], ds[16];
-      const bool diag = qq0 < kw0 + 31 || qq0 + 32 > T;  // some (q, key) pairs masked or out of range
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + 32 * qb + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[4 * r4 + e] = fast_exp2(sacc[4 * r4 + e] * c2 - l4[e]);
+      }
+      // some (q, key) pairs of the sub-block masked or out of range (uniform over the wave)
+      if (qq0 < kw0 + 31 || qq0 + 32 > T) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = qq0 + acc_row(i, g);
+          pr[i] = (mykey <= q && q < T) ? pr[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dsh + 32 * qb + 8 * r4 + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * r4 + e;
-          float pv = fast_exp2(sacc[i] * c2 - l4[e]);
-          if (diag) {
-            const int q = qq0 + acc_row(i, g);
-            pv = (mykey <= q && q < T) ? pv : 0.f;
-          }
-          pr[i] = pv;
-          ds[i] = pv * (dpacc[i] - d4[e]);
-        }
+        for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = pr[4 * r4 + e] * (dpacc[4 * r4 + e] - d4[e]);
       }
       // dV += P^T dO ; dK += dS^T Q  (A = accumulator as [key][q], B from transposed tiles)
 #pragma unroll
@@ -533,14 +561,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
                                                           uint16_t* __restrict__ dqkv) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
-  const int nqt = gridDim.x;
-  const int qt = nqt - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int bh, rank;
+  attn_block_map(bh, rank);
+  const int qt = gridDim.x - 1 - rank;
+  const int b = bh / H, h = bh % H;
   const int C = H * HD;
   const long C3 = 3L * C;
   const uint16_t* base = qkv + (size_t)b * T * C3;
   const uint16_t* dbase = dout + (size_t)b * T * C;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  // the wave index through readfirstlane: the compiler then keeps every per-wave bound below in
+  // scalar registers and branches on it instead of masking lanes
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5,
+            l32 = lane & 31;
   const int q0 = qt * BQ;
   const int qw0 = q0 + 32 * w;
   const int myq = qw0 + l32;
@@ -583,16 +615,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
         dpt = mfma(lds_frag16(Vs + (sb * 32 + l32) * LDP + 16 * s + 8 * g), df[s], dpt);
       }
       float ds[16];
-      const bool diag = kb + 31 > qw0 || qw0 + 32 > T;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(st[i] * c2 - L2);
-        if (diag) {
+      for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(st[i] * c2 - L2);
+      if (kb + 31 > qw0 || qw0 + 32 > T) {  // some pairs masked or out of range (uniform)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
           const int key = kb + acc_row(i, g);
-          pv = (key <= myq && myq < T) ? pv : 0.f;
+          ds[i] = (key <= myq && myq < T) ? ds[i] : 0.f;
         }
-        ds[i] = pv * (dpt[i] - Dq);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] *= dpt[i] - Dq;
       // dQ += dS K : A = dS (rows q, k = keys) from the accumulator, B = K read transposed
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
