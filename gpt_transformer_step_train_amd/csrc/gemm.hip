@@ -702,16 +702,26 @@ static bool use_big(DType dt, int M, int N) {
 #ifndef GEMM_DW_BIG
 #define GEMM_DW_BIG 1
 #endif
-#ifndef GEMM_DW_ROUNDS
-#define GEMM_DW_ROUNDS 1
-#endif
+// Split-K factor for the fp32 weight-gradient products. The blocks run in ceil(tiles s / NCU)
+// rounds of K / s each, and every split adds an fp32 partial of M x N that is written and read
+// back once; pick the s that minimises that time (K per split >= 512, partials within scratch).
 int gemm_splits_t(int M, int N, int K, size_t scratch_floats, int tile) {
   const long tiles = (long)cdiv(M, tile) * cdiv(N, tile);
-  int s = 1;
-  // grow until the grid covers GEMM_DW_ROUNDS rounds of the CUs; each split keeps >= 1024 of K
-  while (tiles * s < GEMM_DW_ROUNDS * NCU && K / (s * 2) >= 1024 && (size_t)(s * 2) * M * N <= scratch_floats)
-    s *= 2;
-  return s;
+  // per-CU MFMA rate and HBM rate as seen by these kernels (order of magnitude is enough)
+  const double cu_flops = 1.8e12, hbm = 5.0e12;
+  const double tile_flops_per_k = 2.0 * tile * tile;
+  int best = 1;
+  double best_t = 1e30;
+  for (int s = 1; s <= 32; ++s) {
+    if (s > 1 && ((long)K / s < 512 || (size_t)s * M * N > scratch_floats)) break;
+    const double rounds = (double)((tiles * s + NCU - 1) / NCU);
+    const double t = rounds * tile_flops_per_k * ((double)K / s) / cu_flops + (s > 1 ? s * 8.0 * M * N / hbm : 0.0);
+    if (t < best_t * 0.995) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
 }
 int gemm_splits(int M, int N, int K, size_t scratch_floats) { return gemm_splits_t(M, N, K, scratch_floats, 128); }
 

@@ -255,7 +255,7 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
   M->dbuf2 = take(BT * C * es);
   M->dvec = (float*)take(B * H * T * 4);
   M->keys = (uint32_t*)take(BT * 4);
-  size_t sf = std::max<size_t>(8 * 4 * C * C, (size_t)ldl * C * 2);
+  size_t sf = std::max<size_t>(8 * 4 * C * C, (size_t)ldl * C * 3);  // split-K partials of the dW GEMMs
   sf = std::max(sf, layernorm_bwd_partial_floats((int)BT, (int)C));
   sf = std::max(sf, encoder_bwd_partial_floats((int)BT, (int)C));
   sf = std::max<size_t>(sf, (size_t)256 * 4 * C);  // column-sum partials
