@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgpt2.so"
 
 GPT2_OK, GPT2_EINVAL, GPT2_ENOMEM, GPT2_EHIP, GPT2_ESTATE, GPT2_ERANGE, GPT2_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
 GPT2_FP32, GPT2_BF16 = 0, 1
-EPI_BIAS, EPI_GELU, EPI_RESID, EPI_GELU_BWD, EPI_F32 = 0, 1, 2, 3, 4
+EPI_BIAS, EPI_GELU, EPI_RESID, EPI_GELU_BWD, EPI_F32, EPI_GELU_GRAD, EPI_MUL = 0, 1, 2, 3, 4, 5, 6
 
 # every symbol the headers declare (checked by the CPU tests against include/*.h)
 EXPORTS = [

@@ -173,6 +173,12 @@ __device__ __forceinline__ float gelu_bwd(float x) {
   const float s = gelu_sig(x);
   return s + 2.0f * x * s * (1.0f - s) * GELU_K * (1.0f + 3.0f * GELU_C * x * x);
 }
+// gelu(x) and gelu'(x) sharing one sigmoid
+__device__ __forceinline__ void gelu_both(float x, float& g, float& dg) {
+  const float s = gelu_sig(x);
+  g = x * s;
+  dg = s + 2.0f * x * s * (1.0f - s) * GELU_K * (1.0f + 3.0f * GELU_C * x * x);
+}
 
 __host__ __device__ constexpr int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 

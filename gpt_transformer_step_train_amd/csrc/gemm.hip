@@ -318,7 +318,8 @@ template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
 // (aux) or, for fp32 accumulation, the old C. They are fetched for a whole slab before any of
 // its results is stored, so the loads are in flight together.
 template <typename T, int EPI> struct EpiX {
-  static constexpr bool USED = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_F32;
+  static constexpr bool AUX = EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_MUL;
+  static constexpr bool USED = AUX || EPI == EPI_F32;
   static constexpr int NW = EPI == EPI_F32 ? 2 : 8 / Elt<T>::VEC;  // 16-byte words per chunk
   u32x4 w[NW];
 };
@@ -340,7 +341,7 @@ __device__ __forceinline__ void epi_fetch8(const GemmArgs& p, const float* C_f32
       x.w[0] = t[0].pack();
       x.w[1] = t[1].pack();
     }
-  } else if constexpr (EPI == EPI_RESID || EPI == EPI_GELU_BWD) {
+  } else if constexpr (EpiX<T, EPI>::AUX) {
     constexpr int VEC = Elt<T>::VEC;
     const T* src = reinterpret_cast<const T*>(p.aux) + (size_t)row * p.ldaux + col;
     if (full) {
@@ -388,8 +389,8 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
     }
   } else {
     constexpr int VEC = Elt<T>::VEC;
-    float xv[8], o[8];
-    if constexpr (EPI == EPI_RESID || EPI == EPI_GELU_BWD) {
+    float xv[8], o[8], o2[8];
+    if constexpr (EpiX<T, EPI>::AUX) {
 #pragma unroll
       for (int h = 0; h < 8 / VEC; ++h) {
         V16<T> t;
@@ -400,8 +401,13 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU) o[e] = a[e] + bv[e];
+      if constexpr (EPI == EPI_BIAS) o[e] = a[e] + bv[e];
+      else if constexpr (EPI == EPI_GELU) {
+        o[e] = a[e] + bv[e];
+        o2[e] = gelu_fwd(o[e]);
+      } else if constexpr (EPI == EPI_GELU_GRAD) gelu_both(a[e] + bv[e], o2[e], o[e]);
       else if constexpr (EPI == EPI_RESID) o[e] = xv[e] + (a[e] + bv[e]);
+      else if constexpr (EPI == EPI_MUL) o[e] = a[e] * xv[e];
       else o[e] = a[e] * gelu_bwd(xv[e]);
     }
     T* dst = reinterpret_cast<T*>(p.C) + (size_t)row * ldc + col;
@@ -413,13 +419,13 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
         for (int e = 0; e < VEC; ++e) t.v[e] = o[h * VEC + e];
         t.store(dst + h * VEC);
       }
-      if constexpr (EPI == EPI_GELU) {
+      if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_GRAD) {
         T* dst2 = reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col;
 #pragma unroll
         for (int h = 0; h < 8 / VEC; ++h) {
           V16<T> t;
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) t.v[e] = gelu_fwd(o[h * VEC + e]);
+          for (int e = 0; e < VEC; ++e) t.v[e] = o2[h * VEC + e];
           t.store(dst2 + h * VEC);
         }
       }
@@ -428,7 +434,8 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
       for (int e = 0; e < 8; ++e) {
         if (col + e < p.N) {
           st1(dst, e, o[e]);
-          if constexpr (EPI == EPI_GELU) st1(reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col, e, gelu_fwd(o[e]));
+          if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_GRAD)
+            st1(reinterpret_cast<T*>(p.C2) + (size_t)row * ldc + col, e, o2[e]);
         }
       }
     }
@@ -619,7 +626,7 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
   float bv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) bv[e] = 0.f;
-  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID) {
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID || EPI == EPI_GELU_GRAD) {
     if (p.bias && col < p.N) {
       const T* bias = reinterpret_cast<const T*>(p.bias) + col;
       if (col + 8 <= p.N) {
@@ -644,17 +651,27 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
+  // residual / derivative inputs of all slabs are fetched up front (one memory round trip);
+  // the old C of fp32 accumulation (twice the registers) is fetched slab by slab
+  constexpr bool ALL_AT_ONCE = EpiX<T, EPI>::AUX;
+  constexpr int NXS = ALL_AT_ONCE ? FM : 1;
+  EpiX<T, EPI> xs[NXS][NIT];
+  auto fetch_slab = [&](int i, EpiX<T, EPI>(&xo)[NIT]) {
+    const int row0 = m0 + wm * TM + i * 32;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int row = row0 + (it * 64 + lane) / CPR;
+      if (row < p.M && col < p.N) epi_fetch8<T, EPI>(q, C_f32, ldc, row, col, xo[it]);
+    }
+  };
+  if constexpr (ALL_AT_ONCE) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fetch_slab(i, xs[i]);
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int row0 = m0 + wm * TM + i * 32;
-    EpiX<T, EPI> xs[NIT];
-    if constexpr (EpiX<T, EPI>::USED) {
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int row = row0 + (it * 64 + lane) / CPR;
-        if (row < p.M && col < p.N) epi_fetch8<T, EPI>(q, C_f32, ldc, row, col, xs[it]);
-      }
-    }
+    if constexpr (EpiX<T, EPI>::USED && !ALL_AT_ONCE) fetch_slab(i, xs[0]);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -668,7 +685,7 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc + 4);
         const float a8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv, xs[it]);
+        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv, xs[ALL_AT_ONCE ? i : 0][it]);
       }
     }
     wave_sync();
@@ -755,6 +772,8 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
     case EPI_GELU: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU>(grid, a, k_split, nullptr, s); break;
     case EPI_RESID: launch_cfg<T, BM, BN, AKC, BKC, EPI_RESID>(grid, a, k_split, nullptr, s); break;
     case EPI_GELU_BWD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_BWD>(grid, a, k_split, nullptr, s); break;
+    case EPI_GELU_GRAD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_GRAD>(grid, a, k_split, nullptr, s); break;
+    case EPI_MUL: launch_cfg<T, BM, BN, AKC, BKC, EPI_MUL>(grid, a, k_split, nullptr, s); break;
     case EPI_F32:
       launch_cfg<T, BM, BN, AKC, BKC, EPI_F32>(grid, a, k_split, splits > 1 ? scratch : nullptr, s);
       if (splits > 1) {

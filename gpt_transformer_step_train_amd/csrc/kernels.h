@@ -17,6 +17,8 @@ enum Epi {
   EPI_RESID = 2,     // C(T) = aux + acc + bias        (residual add)
   EPI_GELU_BWD = 3,  // C(T) = acc * gelu'(aux)
   EPI_F32 = 4,       // C(f32) = acc  (or += acc when accumulate)
+  EPI_GELU_GRAD = 5, // z = acc + bias ; C(T) = gelu'(z) ; C2(T) = gelu(z)
+  EPI_MUL = 6,       // C(T) = acc * aux
 };
 
 struct GemmArgs {

@@ -31,6 +31,7 @@ struct LayerOff {
   size_t ln1w, ln1b, qkvw, qkvb, attprojw, attprojb, ln2w, ln2b, fcw, fcb, fcprojw, fcprojb;
 };
 struct LayerAct {
+  // fch holds gelu'(z) of the MLP pre-activation z (all the backward needs of z), fchg gelu(z)
   char *ln1, *qkv, *atty, *res1, *ln2, *fch, *fchg, *res2;
   float *ln1_mean, *ln1_rstd, *ln2_mean, *ln2_rstd, *lse;
 };
@@ -384,7 +385,8 @@ int forward_impl(const int32_t* tokens, const int32_t* targets) {
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FC);
-      RUN(gemm(true, true, EPI_GELU, BT, 4 * C, C, a.ln2, C, W(o.fcw), C, a.fch, 4 * C, W(o.fcb), nullptr, 0, a.fchg));
+      RUN(gemm(true, true, EPI_GELU_GRAD, BT, 4 * C, C, a.ln2, C, W(o.fcw), C, a.fch, 4 * C, W(o.fcb), nullptr, 0,
+               a.fchg));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ);
@@ -444,11 +446,11 @@ int backward_impl() {
     const LayerOff& o = g.lo[l];
     LayerAct& a = g.la[l];
     const char* xin = l > 0 ? g.la[l - 1].res2 : g.encoded;
-    // fcproj: res2 = res1 + gelu(fch) Wfcproj^T + b
+    // fcproj: res2 = res1 + gelu(z) Wfcproj^T + b ; dz = (dres Wfcproj) * gelu'(z)
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DX);
-      RUN(gemm(true, false, EPI_GELU_BWD, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr,
-             a.fch, 4 * C));
+      RUN(gemm(true, false, EPI_MUL, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
+               4 * C));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DW);
@@ -459,7 +461,7 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_BIAS_GRAD);
       if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.fcprojb), acc, sc, sf, s));
     }
-    // fc: fch = ln2 Wfc^T + b
+    // fc: z = ln2 Wfc^T + b (fch = gelu'(z), fchg = gelu(z))
     {
       ProfScope ps_(GPT2_K_GEMM_FC_DX);
       RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
@@ -779,7 +781,7 @@ static int op_ret(hipError_t e) {
 int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias, const void* aux,
                 int64_t ldaux, void* C2, int accumulate, float* scratch, uint64_t scratch_floats, void* stream) {
-  if (epilogue < 0 || epilogue > 4 || M < 0 || N < 0 || K < 0) return fail(GPT2_EINVAL, "bad gemm arguments");
+  if (epilogue < 0 || epilogue > 6 || M < 0 || N < 0 || K < 0) return fail(GPT2_EINVAL, "bad gemm arguments");
   GemmArgs a{};
   a.M = M;
   a.N = N;

@@ -26,6 +26,8 @@ extern "C" {
 #define GPT2_EPI_RESID 2    /* C = aux + acc + bias                  (residual add)     */
 #define GPT2_EPI_GELU_BWD 3 /* C = acc * gelu_tanh'(aux)             (MLP backward)     */
 #define GPT2_EPI_F32 4      /* C(float) = acc, or += acc when accumulate (weight grads)  */
+#define GPT2_EPI_GELU_GRAD 5 /* z = acc + bias ; C = gelu_tanh'(z) ; C2 = gelu_tanh(z)       */
+#define GPT2_EPI_MUL 6      /* C = acc * aux                          (elementwise)      */
 
 /* C[M,N] = sum_k A(m,k) B(n,k) then the epilogue.
  * A(m,k) = A[m*lda + k] if a_kcontig else A[k*lda + m]; B(n,k) = B[n*ldb + k] if b_kcontig

@@ -89,7 +89,8 @@ def test_gemm_layouts_bias(dt, akc, bkc, shape):
 
 
 BIG_CASES = [((1, 1), bd.EPI_BIAS), ((1, 0), bd.EPI_BIAS), ((0, 0), bd.EPI_BIAS), ((0, 1), bd.EPI_BIAS),
-             ((1, 1), bd.EPI_GELU), ((1, 1), bd.EPI_RESID), ((1, 0), bd.EPI_GELU_BWD), ((0, 0), bd.EPI_F32)]
+             ((1, 1), bd.EPI_GELU), ((1, 1), bd.EPI_RESID), ((1, 0), bd.EPI_GELU_BWD), ((0, 0), bd.EPI_F32),
+             ((1, 1), bd.EPI_GELU_GRAD), ((1, 0), bd.EPI_MUL)]
 
 
 @pytest.mark.parametrize("K", [72, 192])
@@ -124,9 +125,10 @@ def test_gemm_bf16_256_tile_path(layout, epi, K):
     acc = O.matmul_nt(a64, b64)
     b = h64(bd_)
     want = {bd.EPI_BIAS: acc + b, bd.EPI_GELU: acc + b, bd.EPI_RESID: h64(auxd) + acc + b,
-            bd.EPI_GELU_BWD: acc * O.gelu_grad(h64(auxd)), bd.EPI_F32: acc}[epi]
+            bd.EPI_GELU_BWD: acc * O.gelu_grad(h64(auxd)), bd.EPI_F32: acc,
+            bd.EPI_GELU_GRAD: O.gelu_grad(acc + b), bd.EPI_MUL: acc * h64(auxd)}[epi]
     assert rel(h64(Cd), want) <= (2e-5 if epi == bd.EPI_F32 else 8e-3)
-    if epi == bd.EPI_GELU:
+    if epi in (bd.EPI_GELU, bd.EPI_GELU_GRAD):
         assert rel(h64(C2), O.gelu(acc + b)) <= 8e-3
 
 
@@ -158,6 +160,32 @@ def test_gemm_gelu_resid_and_gelu_backward_epilogues(dt):
     assert rel(h64(g), O.gelu(pre_ref)) <= tol(dt, 5e-5)
     assert rel(h64(res), h64(auxd) + pre_ref) <= tol(dt)
     assert rel(h64(gb), acc * O.gelu_grad(h64(auxd))) <= tol(dt, 5e-5)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_gemm_gelu_grad_and_mul_epilogues(dt):
+    """The MLP forward keeps gelu'(z) next to gelu(z); the backward multiplies by it."""
+    M, N, K = 160, 200, 96
+    rng = np.random.default_rng(4)
+    A, W, b = rng.normal(0, 1, (M, K)), rng.normal(0, 0.2, (N, K)), rng.normal(0, 0.5, N)
+    aux = rng.normal(0, 1, (M, N))
+    Ad, Wd, bd_, auxd = dev(A, dt), dev(W, dt), dev(b, dt), dev(aux, dt)
+    lib = bd.load()
+    dg = torch.zeros((M, N), dtype=TD[dt], device="cuda")
+    g = torch.zeros_like(dg)
+    rc = lib.gpt2op_gemm(dt, 1, 1, bd.EPI_GELU_GRAD, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, dg.data_ptr(), N,
+                         bd_.data_ptr(), None, 0, g.data_ptr(), 0, None, 0, stream())
+    assert rc == 0
+    mu = torch.zeros_like(dg)
+    rc = lib.gpt2op_gemm(dt, 1, 0, bd.EPI_MUL, M, N, K, Ad.data_ptr(), K, Wd.t().contiguous().data_ptr(), N,
+                         mu.data_ptr(), N, None, auxd.data_ptr(), N, None, 0, None, 0, stream())
+    assert rc == 0
+    torch.cuda.synchronize()
+    acc = O.matmul_nt(h64(Ad), h64(Wd))
+    z = acc + h64(bd_)
+    assert rel(h64(dg), O.gelu_grad(z)) <= tol(dt, 5e-5)
+    assert rel(h64(g), O.gelu(z)) <= tol(dt, 5e-5)
+    assert rel(h64(mu), acc * h64(auxd)) <= tol(dt)
 
 
 @pytest.mark.parametrize("dt", DTS)
