@@ -73,6 +73,40 @@ def class_work(name, w):
     return "hbm", float(bytes_.get(name, 0))
 
 
+def sources_sha256():
+    """Digest of the HIP sources and headers the library is built from."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "gpt_transformer_step_train_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cls):
+    """HBM bytes per launch of kernel class `cls` from the counter summaries under profiles/ (lines
+    'TRAFFIC class=... fetch_bytes=... write_bytes=... sources_sha256=...'), or None when there is
+    none for this class or the sources changed since the counters were taken."""
+    import glob
+    digest = None
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(f):
+            if not line.startswith("TRAFFIC "):
+                continue
+            kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+            if kv.get("class") != cls:
+                continue
+            digest = digest or sources_sha256()
+            if kv.get("sources_sha256") != digest:
+                return None
+            return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
 def cpu_baseline(w, seconds_hint=""):
     """The oracle (plain fp64 numpy, test infrastructure) on one sequence of the same workload."""
     import numpy as np
@@ -102,6 +136,8 @@ def main():
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", action="store_true", help="print the per-class kernel times to stderr")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -179,7 +215,16 @@ def main():
     scale = 1e12 if bound == "mfma" else 1e9
     roof = {"bound": bound, "kernel": name, "launches_per_step": int(cnt[dom] // args.steps),
             "avg_launch_us": round(avg_s * 1e6, 2), "achieved": round(achieved / scale, 2),
-            "peak": peak / scale, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None}
+            "peak": peak / scale, "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(name)}
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        bd.check(bd.load().gpt2op_copy(dst.data_ptr(), src.data_ptr(), n, torch.cuda.current_stream().cuda_stream),
+                 "copy")
+        torch.cuda.synchronize()
 
     out = {
         "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

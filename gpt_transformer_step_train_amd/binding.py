@@ -24,7 +24,7 @@ EXPORTS = [
     "gpt2_profile_read",
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
-    "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch",
+    "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy",
 ]
 
 
@@ -79,6 +79,7 @@ def load(path=LIB_PATH):
         "gpt2op_encoder_forward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 6),
         "gpt2op_encoder_backward": (ctypes.c_int, [ctypes.c_int] * 6 + [_vp] * 4 + [ctypes.c_int, _vp, _vp, _vp]),
         "gpt2op_encoder_backward_scratch": (_u64, [ctypes.c_int, ctypes.c_int]),
+        "gpt2op_copy": (ctypes.c_int, [_vp, _vp, _u64, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

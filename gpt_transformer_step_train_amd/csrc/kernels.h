@@ -113,6 +113,7 @@ hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float
 hipError_t launch_init_params(const WorkItem* items, int nitems, float* p, uint64_t seed, double std_,
                               hipStream_t s);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
 
 }  // namespace g2

@@ -839,6 +839,12 @@ int gpt2op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t*
 
 uint64_t gpt2op_encoder_backward_scratch(int BT, int C) { return encoder_bwd_partial_floats(BT, C); }
 
+int gpt2op_copy(void* dst, const void* src, uint64_t bytes, void* stream) {
+  if ((bytes % 16) || ((uintptr_t)dst % 16) || ((uintptr_t)src % 16) || (bytes && (!dst || !src)))
+    return fail(GPT2_EINVAL, "copy: pointers and size must be 16-byte aligned");
+  return op_ret(launch_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok, const void* dout,
                             float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys, float* partial, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -182,6 +182,18 @@ hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                   size_t n16) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = src[i];
+}
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  copy_kernel<<<(int)std::min<size_t>(8192, (n16 + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), n16);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, size_t n, float v) {
   for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
 }

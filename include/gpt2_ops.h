@@ -74,6 +74,12 @@ int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, 
                             float* partial, void* stream);
 uint64_t gpt2op_encoder_backward_scratch(int BT, int C);
 
+/* Measurement utility, not part of the training step: dst[0, bytes) = src[0, bytes) with one
+ * streaming kernel (16-byte loads and stores; bytes and both pointers 16-byte aligned, else
+ * GPT2_EINVAL). Reads and writes exactly `bytes` each, so its HBM traffic counters give the scale
+ * that converts the counters of any other kernel into bytes. */
+int gpt2op_copy(void* dst, const void* src, uint64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
