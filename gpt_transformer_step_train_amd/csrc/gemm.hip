@@ -567,11 +567,17 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* const st0 = reinterpret_cast<T*>(smem);
 
-  // tile mapping: XCD-contiguous runs, then grouped row-major order
+  // Block -> (split, tile). The 1-D grid holds splits x tiles blocks padded to a multiple of 8;
+  // blocks are dealt round-robin to the 8 XCDs, so block L is renumbered to give each XCD a
+  // contiguous run of (split, tile) pairs (tiles of one split that share operand rows or columns
+  // then share an L2); padding blocks exit. Inside a split, tiles go in groups of GROUP_M
+  // tile-rows.
   const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
-  const int nt = gridDim.x;
-  int b = blockIdx.x;
-  if ((nt & 7) == 0) b = (b & 7) * (nt >> 3) + (b >> 3);
+  const int ntiles = tiles_m * tiles_n;
+  const int nsplit = cdiv(p.K, k_split);
+  const int bb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (bb >= ntiles * nsplit) return;
+  const int zs = bb / ntiles, b = bb % ntiles;
   const int group = GROUP_M * tiles_n;
   const int first_m = (b / group) * GROUP_M;
   const int gsz = min(tiles_m - first_m, GROUP_M);
@@ -579,7 +585,7 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
   const int tn = (b % group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const int kbeg = blockIdx.z * k_split;
+  const int kbeg = zs * k_split;
   const int kend = min(p.K, kbeg + k_split);
 
   const int tid = threadIdx.x;
@@ -611,7 +617,7 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
   GemmArgs q = p;
   if constexpr (EPI == EPI_F32) {
     if (split_out) {
-      C_f32 = split_out + (size_t)blockIdx.z * p.M * p.N;
+      C_f32 = split_out + (size_t)zs * p.M * p.N;
       ldc = p.N;
       q.accumulate = 0;
     }
@@ -766,7 +772,7 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
     k_split = cdiv(cdiv(a.K, splits), BK) * BK;
     splits = cdiv(a.K, k_split);
   }
-  dim3 grid(tiles, 1, splits);
+  dim3 grid(((long)tiles * splits + 7) & ~7L);
   switch (epi) {
     case EPI_BIAS: launch_cfg<T, BM, BN, AKC, BKC, EPI_BIAS>(grid, a, k_split, nullptr, s); break;
     case EPI_GELU: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU>(grid, a, k_split, nullptr, s); break;
