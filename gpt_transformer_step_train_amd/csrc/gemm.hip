@@ -55,9 +55,6 @@ template <> struct Mma<float> {
   }
 };
 
-#ifndef GEMM_SCHED_HINT
-#define GEMM_SCHED_HINT __builtin_amdgcn_iglp_opt(1)
-#endif
 constexpr int NTHR = 256, WGM = 2, WGN = 2;
 constexpr int GROUP_M = 8;
 constexpr int TKR = 4;  // transposed piece: TKR k-rows x VEC row-contiguous elements
@@ -301,8 +298,6 @@ template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   // k per LDS stage: 64 when both bf16 operands are K-contiguous (direct copies, 64 MFMAs per
   // wave between barriers), else 32 (register staging; half the staging registers)
   static constexpr int BK = sizeof(T) == 2 && AKC && BKC ? 64 : 32;
-  // bf16 K-contiguous products are scheduled with the MFMA / LDS interleave hint
-  static constexpr bool HINT = sizeof(T) == 2 && AKC && BKC;
   using OA = Operand<T, AKC, BM, BK>;
   using OB = Operand<T, BKC, BN, BK>;
   static constexpr int STAGE = OA::ELEMS + OB::ELEMS;  // elements per LDS stage
@@ -501,6 +496,21 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[cb][i], fb[cb][j], acc[i][j]);
     }
+    {
+      // issue order: the reads of step 0, then for each step one read of the next step after
+      // every FM*FN/(FM+FN) MFMAs, so no MFMA waits for a read issued in its own step
+      constexpr int NR = FM * (OA::MODE == 2 ? 2 : 1) + FN * (OB::MODE == 2 ? 2 : 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int st = 0; st + 1 < KS; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR / 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR - NR / 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    }
   };
 
   if constexpr (DIRECT) {
@@ -529,7 +539,7 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
       asm volatile("" ::: "memory");
       if (kt + NS - 1 < nkt) issue(kt + NS - 1);
       compute(Abuf(kt % NS), Bbuf(kt % NS));
-      if constexpr (CF::HINT) GEMM_SCHED_HINT;
+
     }
     __syncthreads();  // the epilogue reuses the LDS
   } else {
@@ -550,7 +560,7 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
         lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * BK, kend);
       }
       compute(Abuf(cur), Bbuf(cur));
-      if constexpr (CF::HINT) GEMM_SCHED_HINT;
+
       if (more) {
         la.store(Abuf(cur ^ 1), m0, p.M, kbeg + (kt + 1) * BK, kend);
         lb.store(Bbuf(cur ^ 1), n0, p.N, kbeg + (kt + 1) * BK, kend);
