@@ -14,7 +14,7 @@
 
 namespace g2 {
 
-constexpr int CE_THREADS = 1024;
+constexpr int CE_THREADS = 512;
 constexpr int CE_WAVES = CE_THREADS / 64;
 
 // dloss_out = 1/(n_valid * accum) (0 when n_valid == 0); nvalid_out = n_valid; err |= 2 on bad target
@@ -36,12 +36,26 @@ __global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __re
   }
 }
 
+// (m, s) pairs in log2 units: s = sum 2^(y - m) over the values seen; m = -inf while empty
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  const float a = m == -INFINITY ? 0.f : s * fast_exp2(m - M);
+  const float b = m2 == -INFINITY ? 0.f : s2 * fast_exp2(m2 - M);
+  m = M;
+  s = a + b;
+}
+
+// One block of 512 threads per row. The row is loaded once into registers (packed), the max and
+// the sum of exponentials are accumulated in one online pass per thread (rescaled once per 8 or 4
+// values), merged across the wave and the 8 waves in a fixed order, then the gradient is written.
+// Blocks of 512 threads with ~13 packed vectors each leave room for several rows per CU, so the
+// loads of one row overlap the arithmetic and stores of another.
 template <typename T, int NVT>
 __global__ __launch_bounds__(CE_THREADS) void ce_kernel(int V, int ld, T* __restrict__ logits,
                                                         const int32_t* __restrict__ targets,
                                                         const float* __restrict__ dloss_p, float* __restrict__ losses) {
   constexpr int VEC = Elt<T>::VEC;
-  __shared__ float red[CE_WAVES];
+  __shared__ float red_m[CE_WAVES], red_s[CE_WAVES];
   __shared__ float xt_sh;
   const int row = blockIdx.x;
   T* x = logits + (size_t)row * ld;
@@ -50,50 +64,65 @@ __global__ __launch_bounds__(CE_THREADS) void ce_kernel(int V, int ld, T* __rest
   const int nvec = ld / VEC;
   if (threadIdx.x == 0) xt_sh = tgt >= 0 ? ld1(x, tgt) : 0.f;
 
-  V16<T> xv[NVT];
-  float mx = -INFINITY;
+  u32x4 raw[NVT];
 #pragma unroll
   for (int j = 0; j < NVT; ++j) {
     const int v = threadIdx.x + j * CE_THREADS;
-    if (v < nvec) {
-      xv[j].load(x + (size_t)v * VEC);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        if (v * VEC + e >= V) xv[j].v[e] = -INFINITY;
-        mx = fmaxf(mx, xv[j].v[e]);
-      }
-    }
+    raw[j] = v < nvec ? *reinterpret_cast<const u32x4*>(x + (size_t)v * VEC) : u32x4{0u, 0u, 0u, 0u};
   }
-  mx = block_max<CE_WAVES>(mx, red);
-  const float mx2 = mx * LOG2E;
-  float se = 0.f;
+  // values in log2 units; columns >= V are -inf
+  auto unpack = [&](int j, float (&y)[VEC]) {
+    V16<T> t;
+    t.unpack(raw[j]);
+    const int c0 = (threadIdx.x + j * CE_THREADS) * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) y[e] = c0 + e < V ? t.v[e] * LOG2E : -INFINITY;
+  };
+  float m = -INFINITY, s = 0.f;
 #pragma unroll
   for (int j = 0; j < NVT; ++j) {
-    const int v = threadIdx.x + j * CE_THREADS;
-    if (v < nvec) {
+    if (threadIdx.x + j * CE_THREADS < nvec) {
+      float y[VEC];
+      unpack(j, y);
+      float vm = y[0];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float p = fast_exp2(xv[j].v[e] * LOG2E - mx2);
-        xv[j].v[e] = p;  // unnormalised probability (0 for padded columns)
-        se += p;
+      for (int e = 1; e < VEC; ++e) vm = fmaxf(vm, y[e]);
+      if (vm != -INFINITY) {
+        const float mn = fmaxf(m, vm);
+        float acc = m == -INFINITY ? 0.f : s * fast_exp2(m - mn);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc += fast_exp2(y[e] - mn);
+        m = mn;
+        s = acc;
       }
     }
   }
-  se = block_sum<CE_WAVES>(se, red);  // includes the barrier that publishes xt_sh
-  const float lse = mx + logf(se);
-  if (threadIdx.x == 0) losses[row] = tgt >= 0 ? lse - xt_sh : 0.f;
+  // merge over the wave: common max, then the rescaled sums
+  const float wm = wave_max(m);
+  float ws = wave_sum(m == -INFINITY ? 0.f : s * fast_exp2(m - wm));
+  if ((threadIdx.x & 63) == 0) {
+    red_m[threadIdx.x >> 6] = wm;
+    red_s[threadIdx.x >> 6] = ws;
+  }
+  __syncthreads();  // also publishes xt_sh
+  float M = red_m[0], S = red_s[0];
+#pragma unroll
+  for (int w = 1; w < CE_WAVES; ++w) lse_merge(M, S, red_m[w], red_s[w]);
+  const float lse2 = M + __log2f(S);  // log2 units
+  if (threadIdx.x == 0) losses[row] = tgt >= 0 ? lse2 / LOG2E - xt_sh : 0.f;
   if (!dloss_p) return;
   const float dl = tgt >= 0 ? *dloss_p : 0.f;
-  const float inv = dl / se;
 #pragma unroll
   for (int j = 0; j < NVT; ++j) {
     const int v = threadIdx.x + j * CE_THREADS;
     if (v < nvec) {
+      float y[VEC];
+      unpack(j, y);
       V16<T> o;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const int col = v * VEC + e;
-        o.v[e] = xv[j].v[e] * inv - (col == tgt ? dl : 0.f);
+        o.v[e] = fast_exp2(y[e] - lse2) * dl - (col == tgt ? dl : 0.f);
       }
       o.store(x + (size_t)v * VEC);
     }
@@ -106,13 +135,14 @@ static hipError_t ce_t(int rows, int V, int ld, void* logits, const int32_t* tar
   constexpr int VEC = Elt<T>::VEC;
   const int nvt = cdiv(ld / VEC, CE_THREADS);
   T* L = reinterpret_cast<T*>(logits);
-  if (nvt <= 1) ce_kernel<T, 1><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
-  else if (nvt <= 2) ce_kernel<T, 2><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
-  else if (nvt <= 4) ce_kernel<T, 4><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
-  else if (nvt <= 8) ce_kernel<T, 8><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
-  else if (nvt <= 16) ce_kernel<T, 16><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+#define CE_CASE(n) \
+  if (nvt <= n) { \
+    ce_kernel<T, n><<<rows, CE_THREADS, 0, s>>>(V, ld, L, targets, dloss, losses); \
+    return hipGetLastError(); \
+  }
+  CE_CASE(1) CE_CASE(2) CE_CASE(4) CE_CASE(8) CE_CASE(13) CE_CASE(16) CE_CASE(25) CE_CASE(32)
+#undef CE_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_count_targets(const int32_t* targets, int rows, int V, int accum, float* dloss, int* nvalid,
