@@ -71,7 +71,7 @@ def load(path=LIB_PATH):
         "gpt2op_gemm": (ctypes.c_int, [ctypes.c_int] * 7 + [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp,
                                                             ctypes.c_int, _vp, _u64, _vp]),
         "gpt2op_layernorm_forward": (ctypes.c_int, [ctypes.c_int] * 3 + [_vp] * 7),
-        "gpt2op_layernorm_backward": (ctypes.c_int, [ctypes.c_int] * 3 + [_vp] * 8 + [ctypes.c_int, _vp, _vp]),
+        "gpt2op_layernorm_backward": (ctypes.c_int, [ctypes.c_int] * 3 + [_vp] * 9 + [ctypes.c_int, _vp, _vp]),
         "gpt2op_layernorm_backward_scratch": (_u64, [ctypes.c_int, ctypes.c_int]),
         "gpt2op_attention_forward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 4),
         "gpt2op_attention_backward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7),

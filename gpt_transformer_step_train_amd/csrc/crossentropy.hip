@@ -14,7 +14,7 @@
 
 namespace g2 {
 
-constexpr int CE_THREADS = 512;
+constexpr int CE_THREADS = 1024;
 constexpr int CE_WAVES = CE_THREADS / 64;
 
 // dloss_out = 1/(n_valid * accum) (0 when n_valid == 0); nvalid_out = n_valid; err |= 2 on bad target
@@ -45,10 +45,10 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   s = a + b;
 }
 
-// One block of 512 threads per row. The row is loaded once into registers (packed), the max and
+// One block of 1024 threads per row. The row is loaded once into registers (packed), the max and
 // the sum of exponentials are accumulated in one online pass per thread (rescaled once per 8 or 4
-// values), merged across the wave and the 8 waves in a fixed order, then the gradient is written.
-// Blocks of 512 threads with ~13 packed vectors each leave room for several rows per CU, so the
+// values), merged across the wave and the 16 waves in a fixed order, then the gradient is written.
+// Blocks of 1024 threads with ~7 packed vectors each leave room for two rows per CU, so the
 // loads of one row overlap the arithmetic and stores of another.
 template <typename T, int NVT>
 __global__ __launch_bounds__(CE_THREADS) void ce_kernel(int V, int ld, T* __restrict__ logits,

@@ -50,9 +50,10 @@ hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float*
 hipError_t launch_layernorm_fwd(DType dt, int rows, int C, const void* x, const void* w, const void* b,
                                 void* y, float* mean, float* rstd, hipStream_t s);
 // dres[row] += dx (add = 1) or = dx (add = 0); dw/db (+)= column sums (two-stage, deterministic)
+// dsum (may be null): column sums of the updated dres rows (= or += per accumulate)
 hipError_t launch_layernorm_bwd(DType dt, int rows, int C, const void* dy, const void* x, const void* w,
                                 const float* mean, const float* rstd, void* dres, int add, float* dw, float* db,
-                                int accumulate, float* partial, size_t partial_floats, hipStream_t s);
+                                float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s);
 size_t layernorm_bwd_partial_floats(int rows, int C);
 
 // Encoder

@@ -73,49 +73,76 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
 
 constexpr int LNB_BLOCKS = 1024;
 
-template <typename T, int NV>
+// Raw (packed) inputs of one row of the backward, held in registers so that the loads of the next
+// row are in flight while this one is processed.
+template <typename T, int NV> struct LnRow {
+  u32x4 dy[NV], x[NV], dr[NV];
+  float mu, rs;
+};
+
+// dx of every row (into dres: = or += dx), and per-block column partials of
+//   dw = sum dy * xhat,  db = sum dy,  and (when dsum) the sum of the updated dres rows
+// (the bias gradient of the linear layer whose output feeds this residual stream).
+// Block = 4 waves; wave wv takes rows r0 + wv, r0 + wv + 4, ...; partial layout [block][3][C].
+template <typename T, int NV, bool PF>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_per_block,
                                                      const T* __restrict__ dy, const T* __restrict__ x,
                                                      const T* __restrict__ w, const float* __restrict__ mean,
                                                      const float* __restrict__ rstd, T* __restrict__ dres,
-                                                     int add, float* __restrict__ partial) {
+                                                     int add, int dsum, float* __restrict__ partial) {
   constexpr int VEC = Elt<T>::VEC;
-  extern __shared__ float red[];  // [4][2*C]
+  extern __shared__ float red[];  // [4][C]
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nvec = C / VEC;
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(rows, r0 + rows_per_block);
 
-  float dw_acc[NV][VEC], db_acc[NV][VEC];
-  V16<T> wvec[NV];
+  float acc[3][NV][VEC];  // dw, db, dres sums
+  float wf[NV][VEC];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) dw_acc[j][e] = db_acc[j][e] = 0.f;
     const int v = lane + 64 * j;
-    if (v < nvec) wvec[j].load(w + v * VEC);
+    V16<T> t;
+    if (v < nvec) t.load(w + v * VEC);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      wf[j][e] = v < nvec ? t.v[e] : 0.f;
+      acc[0][j][e] = acc[1][j][e] = acc[2][j][e] = 0.f;
+    }
   }
-
-  for (int row = r0 + wv; row < r1; row += 4) {
-    const float mu = mean[row], rs = rstd[row];
-    V16<T> dyv[NV], xv[NV];
-    float sg = 0.f, sgx = 0.f;
+  auto load_row = [&](int row, LnRow<T, NV>& d) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int v = lane + 64 * j;
       if (v < nvec) {
-        dyv[j].load(dy + (size_t)row * C + v * VEC);
-        xv[j].load(x + (size_t)row * C + v * VEC);
+        const size_t o = (size_t)row * C + v * VEC;
+        d.dy[j] = *reinterpret_cast<const u32x4*>(dy + o);
+        d.x[j] = *reinterpret_cast<const u32x4*>(x + o);
+        if (add) d.dr[j] = *reinterpret_cast<const u32x4*>(dres + o);
+      }
+    }
+    d.mu = mean[row];
+    d.rs = rstd[row];
+  };
+  auto process = [&](int row, const LnRow<T, NV>& d) {
+    float dyf[NV][VEC], xh[NV][VEC];
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (lane + 64 * j < nvec) {
+        V16<T> a, b;
+        a.unpack(d.dy[j]);
+        b.unpack(d.x[j]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float xh = (xv[j].v[e] - mu) * rs;
-          xv[j].v[e] = xh;  // keep xhat
-          const float g = dyv[j].v[e] * wvec[j].v[e];
+          dyf[j][e] = a.v[e];
+          xh[j][e] = (b.v[e] - d.mu) * d.rs;
+          const float g = a.v[e] * wf[j][e];
           sg += g;
-          sgx += g * xh;
-          dw_acc[j][e] += dyv[j].v[e] * xh;
-          db_acc[j][e] += dyv[j].v[e];
+          sgx += g * xh[j][e];
+          acc[0][j][e] += a.v[e] * xh[j][e];
+          acc[1][j][e] += a.v[e];
         }
       }
     }
@@ -125,48 +152,66 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_p
     for (int j = 0; j < NV; ++j) {
       const int v = lane + 64 * j;
       if (v < nvec) {
-        T* dr = dres + (size_t)row * C + v * VEC;
         V16<T> o;
-        if (add) o.load(dr);
+        if (add) o.unpack(d.dr[j]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float g = dyv[j].v[e] * wvec[j].v[e];
-          const float dx = rs * (g - mg - xv[j].v[e] * mgx);
+          const float dx = d.rs * (dyf[j][e] * wf[j][e] - mg - xh[j][e] * mgx);
           o.v[e] = add ? o.v[e] + dx : dx;
+          acc[2][j][e] += o.v[e];
         }
-        o.store(dr);
+        o.store(dres + (size_t)row * C + v * VEC);
       }
     }
-  }
-  // combine the 4 waves' column partials in LDS, then write this block's partial row
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = lane + 64 * j;
-    if (v < nvec) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        red[wv * 2 * C + v * VEC + e] = dw_acc[j][e];
-        red[wv * 2 * C + C + v * VEC + e] = db_acc[j][e];
-      }
+  };
+  int row = r0 + wv;
+  if constexpr (PF) {
+    LnRow<T, NV> cur, nxt;
+    if (row < r1) load_row(row, cur);
+    for (; row < r1; row += 4) {
+      if (row + 4 < r1) load_row(row + 4, nxt);
+      process(row, cur);
+      cur = nxt;
+    }
+  } else {
+    for (; row < r1; row += 4) {
+      LnRow<T, NV> cur;
+      load_row(row, cur);
+      process(row, cur);
     }
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < 2 * C; c += 256) {
-    const float s = (red[c] + red[2 * C + c]) + (red[4 * C + c] + red[6 * C + c]);
-    partial[(size_t)blockIdx.x * 2 * C + c] = s;
+  // combine the 4 waves' column partials in LDS, one quantity at a time, and write this
+  // block's partial rows
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    if (q == 2 && !dsum) break;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = lane + 64 * j;
+      if (v < nvec) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) red[wv * C + v * VEC + e] = acc[q][j][e];
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += 256) {
+      const float sum = (red[c] + red[C + c]) + (red[2 * C + c] + red[3 * C + c]);
+      partial[((size_t)blockIdx.x * 3 + q) * C + c] = sum;
+    }
+    __syncthreads();
   }
 }
 
-// grid (cdiv(C, 32), 2): y = 0 -> dw, y = 1 -> db
+// grid (cdiv(C, 32), 3): y = 0 -> dw, 1 -> db, 2 -> dres column sums
 __global__ __launch_bounds__(RP_THREADS) void ln_bwd_finish(const float* __restrict__ partial, int nblocks, int C,
                                                      float* __restrict__ dw, float* __restrict__ db,
-                                                     int accumulate) {
-  float* out = blockIdx.y == 0 ? dw : db;
+                                                     float* __restrict__ dsum, int accumulate) {
+  float* out = blockIdx.y == 0 ? dw : blockIdx.y == 1 ? db : dsum;
   if (!out) return;
-  reduce_partials_block(partial + (size_t)blockIdx.y * C, nblocks, 2L * C, C, out, accumulate);
+  reduce_partials_block(partial + (size_t)blockIdx.y * C, nblocks, 3L * C, C, out, accumulate);
 }
 
-size_t layernorm_bwd_partial_floats(int rows, int C) { return (size_t)LNB_BLOCKS * 2 * C; }
+size_t layernorm_bwd_partial_floats(int rows, int C) { return (size_t)LNB_BLOCKS * 3 * C; }
 
 template <typename T>
 static hipError_t ln_fwd_t(int rows, int C, const void* x, const void* w, const void* b, void* y, float* mean,
@@ -195,35 +240,39 @@ hipError_t launch_layernorm_fwd(DType dt, int rows, int C, const void* x, const 
 
 template <typename T>
 static hipError_t ln_bwd_t(int rows, int C, const void* dy, const void* x, const void* w, const float* mean,
-                           const float* rstd, void* dres, int add, float* dw, float* db, int accumulate,
-                           float* partial, hipStream_t s) {
+                           const float* rstd, void* dres, int add, float* dw, float* db, float* dsum,
+                           int accumulate, float* partial, hipStream_t s) {
   constexpr int VEC = Elt<T>::VEC;
   const int nv = cdiv(C / VEC, 64);
   const int rpb = cdiv(rows, LNB_BLOCKS);
   const int nb = rows > 0 ? cdiv(rows, rpb) : 0;
-  const size_t shm = (size_t)4 * 2 * C * sizeof(float);
+  const size_t shm = (size_t)4 * C * sizeof(float);
   auto DY = reinterpret_cast<const T*>(dy);
   auto X = reinterpret_cast<const T*>(x);
   auto W = reinterpret_cast<const T*>(w);
   auto DR = reinterpret_cast<T*>(dres);
+  const int ds = dsum != nullptr;
   if (nb > 0) {
-    if (nv <= 1) ln_bwd_kernel<T, 1><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, partial);
-    else if (nv <= 2) ln_bwd_kernel<T, 2><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, partial);
-    else if (nv <= 4) ln_bwd_kernel<T, 4><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, partial);
-    else if (nv <= 8) ln_bwd_kernel<T, 8><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, partial);
+#define LNB(n, pf) ln_bwd_kernel<T, n, pf><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, ds, partial)
+    if (nv <= 1) LNB(1, true);
+    else if (nv <= 2) LNB(2, true);
+    else if (nv <= 4) LNB(4, false);
+    else if (nv <= 8) LNB(8, false);
     else return hipErrorInvalidValue;
+#undef LNB
   }
-  ln_bwd_finish<<<dim3(cdiv(C, 32), 2), RP_THREADS, 0, s>>>(partial, nb, C, dw, db, accumulate);
+  ln_bwd_finish<<<dim3(cdiv(C, 32), 3), RP_THREADS, 0, s>>>(partial, nb, C, dw, db, dsum, accumulate);
   return hipGetLastError();
 }
 
 hipError_t launch_layernorm_bwd(DType dt, int rows, int C, const void* dy, const void* x, const void* w,
                                 const float* mean, const float* rstd, void* dres, int add, float* dw, float* db,
-                                int accumulate, float* partial, size_t partial_floats, hipStream_t s) {
-  if ((size_t)LNB_BLOCKS * 2 * C > partial_floats) return hipErrorInvalidValue;
-  if ((size_t)4 * 2 * C * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
-  return dt == DT_BF16 ? ln_bwd_t<bf16>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, accumulate, partial, s)
-                       : ln_bwd_t<float>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, accumulate, partial, s);
+                                float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s) {
+  if ((size_t)LNB_BLOCKS * 3 * C > partial_floats) return hipErrorInvalidValue;
+  if ((size_t)4 * C * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
+  return dt == DT_BF16
+             ? ln_bwd_t<bf16>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, dsum, accumulate, partial, s)
+             : ln_bwd_t<float>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, dsum, accumulate, partial, s);
 }
 
 }  // namespace g2

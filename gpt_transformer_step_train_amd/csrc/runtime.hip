@@ -439,8 +439,10 @@ int backward_impl() {
   const char* xlast = L > 0 ? g.la[L - 1].res2 : g.encoded;
   {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
+      // the column sums of the dres it writes are the bias gradient of the last fcproj
+      float* dsum = (lb && L > 0) ? G(g.lo[L - 1].fcprojb) : nullptr;
       HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xlast, W(g.o_lnfw), g.lnf_mean, g.lnf_rstd, g.dres, 0,
-                              G(g.o_lnfw), G(g.o_lnfb), acc, sc, sf, s));
+                                  G(g.o_lnfw), G(g.o_lnfb), dsum, acc, sc, sf, s));
     }
   for (int l = L - 1; l >= 0; --l) {
     const LayerOff& o = g.lo[l];
@@ -457,10 +459,7 @@ int backward_impl() {
       RUN(gemm(false, false, EPI_F32, C, 4 * C, BT, g.dres, C, a.fchg, 4 * C, G(o.fcprojw), 4 * C, nullptr, nullptr,
              0, nullptr, acc, true));
     }
-    {
-      ProfScope ps_(GPT2_K_BIAS_GRAD);
-      if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.fcprojb), acc, sc, sf, s));
-    }
+    // (the fcproj bias gradient, the column sums of dres, came with the LayerNorm backward above)
     // fc: z = ln2 Wfc^T + b (fch = gelu'(z), fchg = gelu(z))
     {
       ProfScope ps_(GPT2_K_GEMM_FC_DX);
@@ -477,8 +476,9 @@ int backward_impl() {
     }
     {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
+      // + column sums of the updated dres = the attproj bias gradient
       HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, a.res1, W(o.ln2w), a.ln2_mean, a.ln2_rstd, g.dres, 1,
-                                G(o.ln2w), G(o.ln2b), acc, sc, sf, s));
+                                  G(o.ln2w), G(o.ln2b), lb ? G(o.attprojb) : nullptr, acc, sc, sf, s));
     }
     // attproj: res1 = xin + atty Wproj^T + b
     {
@@ -489,10 +489,6 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_GEMM_ATTPROJ_DW);
       RUN(gemm(false, false, EPI_F32, C, C, BT, g.dres, C, a.atty, C, G(o.attprojw), C, nullptr, nullptr, 0, nullptr,
              acc, true));
-    }
-    {
-      ProfScope ps_(GPT2_K_BIAS_GRAD);
-      if (lb) HIPCHK(launch_colsum(g.dt, g.dres, C, BT, C, G(o.attprojb), acc, sc, sf, s));
     }
     {
       ProfScope ps_(GPT2_K_ATTENTION_BWD_PRE);
@@ -525,8 +521,10 @@ int backward_impl() {
     }
     {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
-      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, g.dres, 1, G(o.ln1w),
-                                G(o.ln1b), acc, sc, sf, s));
+      // + column sums of the updated dres = the fcproj bias gradient of the layer below
+      float* dsum = (lb && l > 0) ? G(g.lo[l - 1].fcprojb) : nullptr;
+      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, g.dres, 1,
+                                  G(o.ln1w), G(o.ln1b), dsum, acc, sc, sf, s));
     }
   }
   HIPCHK(hipStreamWaitEvent(s, g.ev_sorted, 0));
@@ -809,10 +807,11 @@ int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const vo
 uint64_t gpt2op_layernorm_backward_scratch(int rows, int C) { return layernorm_bwd_partial_floats(rows, C); }
 
 int gpt2op_layernorm_backward(int dtype, int rows, int C, const void* dy, const void* x, const void* w,
-                              const float* mean, const float* rstd, void* dres, float* dw, float* db, int accumulate,
-                              float* partial, void* stream) {
-  return op_ret(launch_layernorm_bwd(to_dt(dtype), rows, C, dy, x, w, mean, rstd, dres, 1, dw, db, accumulate, partial,
-                                     layernorm_bwd_partial_floats(rows, C), reinterpret_cast<hipStream_t>(stream)));
+                              const float* mean, const float* rstd, void* dres, float* dw, float* db, float* dsum,
+                              int accumulate, float* partial, void* stream) {
+  return op_ret(launch_layernorm_bwd(to_dt(dtype), rows, C, dy, x, w, mean, rstd, dres, 1, dw, db, dsum, accumulate,
+                                     partial, layernorm_bwd_partial_floats(rows, C),
+                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,

@@ -42,9 +42,11 @@ int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, in
 int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,
                              float* mean, float* rstd, void* stream);
 /* dres += dx; dw, db (float [C]) = or += column sums (accumulate). db may be NULL.
+ * dsum (float [C], may be NULL) = or += the column sums of the updated dres (the bias gradient of
+ * the linear layer whose output is added to this residual stream).
  * partial: float scratch of gpt2op_layernorm_backward_scratch(rows, C) elements. */
 int gpt2op_layernorm_backward(int dtype, int rows, int C, const void* dy, const void* x, const void* w,
-                              const float* mean, const float* rstd, void* dres, float* dw, float* db,
+                              const float* mean, const float* rstd, void* dres, float* dw, float* db, float* dsum,
                               int accumulate, float* partial, void* stream);
 uint64_t gpt2op_layernorm_backward_scratch(int rows, int C);
 

@@ -242,10 +242,11 @@ def test_layernorm_forward_backward(dt, rows, C, has_b):
     dw = torch.full((C,), 0.25, dtype=torch.float32, device="cuda")
     db = torch.full((C,), -0.5, dtype=torch.float32, device="cuda")
     part = torch.empty(lib.gpt2op_layernorm_backward_scratch(rows, C), dtype=torch.float32, device="cuda")
+    dsum = torch.full((C,), 1.5, dtype=torch.float32, device="cuda")
     dres_before = h64(dres)
     rc = lib.gpt2op_layernorm_backward(dt, rows, C, dyd.data_ptr(), xd.data_ptr(), wd.data_ptr(), mean.data_ptr(),
-                                       rstd.data_ptr(), dres.data_ptr(), dw.data_ptr(), db.data_ptr(), 1,
-                                       part.data_ptr(), stream())
+                                       rstd.data_ptr(), dres.data_ptr(), dw.data_ptr(), db.data_ptr(),
+                                       dsum.data_ptr(), 1, part.data_ptr(), stream())
     assert rc == 0
     torch.cuda.synchronize()
     x64, w64, b64 = h64(xd), h64(wd), h64(bdv) if has_b else None
@@ -258,6 +259,8 @@ def test_layernorm_forward_backward(dt, rows, C, has_b):
     want = dx if dt == bd.GPT2_FP32 else dres_before + dx
     assert rel(got, want) <= tol(dt, 5e-5)
     assert rel(dw.cpu().numpy(), dwr + 0.25) <= 5e-5
+    # column sums of the updated dres rows (taken before their rounding to the storage type)
+    assert rel(dsum.cpu().numpy(), (dres_before + dx).sum(0) + 1.5) <= tol(dt, 5e-5)
     assert rel(db.cpu().numpy(), dbr - 0.5) <= 5e-5
 
 
