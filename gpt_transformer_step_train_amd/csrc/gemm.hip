@@ -55,7 +55,9 @@ template <> struct Mma<float> {
   }
 };
 
-constexpr int NTHR = 256, WGM = 2, WGN = 2;
+#ifndef GEMM_BIG_WAVES
+#define GEMM_BIG_WAVES 8
+#endif
 constexpr int GROUP_M = 8;
 constexpr int TKR = 4;  // transposed piece: TKR k-rows x VEC row-contiguous elements
 
@@ -79,7 +81,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Interior tiles of modes 0 and 2 are copied global -> LDS with global_load_lds_dwordx4 (lane l
 // of a wave lands at LDS base + 16 l, so each lane fetches the global chunk that belongs there);
 // edge tiles and mode 1 go through registers, with out-of-range elements zeroed.
-template <typename T, bool KC, int ROWS, int BK_> struct Operand {
+template <typename T, bool KC, int ROWS, int BK_, int NTHR> struct Operand {
   static constexpr int VEC = Elt<T>::VEC;
   static constexpr int BK = BK_;
   static constexpr int MODE = KC ? 0 : (sizeof(T) == 2 ? 2 : 1);
@@ -293,18 +295,21 @@ template <typename T, bool KC, int ROWS, int BK_> struct Operand {
 
 template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
+  // waves per block, in a 2 x (NW/2) grid over the tile
+  static constexpr int NW = (sizeof(T) == 2 && BM == 256 && BN == 256) ? GEMM_BIG_WAVES : 4;
+  static constexpr int NTHR = 64 * NW, WGM = 2, WGN = NW / 2;
   static constexpr int TM = BM / WGM, TN = BN / WGN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   // k per LDS stage: 64 when both bf16 operands are K-contiguous (direct copies, 64 MFMAs per
   // wave between barriers), else 32 (register staging; half the staging registers)
   static constexpr int BK = sizeof(T) == 2 && AKC && BKC ? 64 : 32;
-  using OA = Operand<T, AKC, BM, BK>;
-  using OB = Operand<T, BKC, BN, BK>;
+  using OA = Operand<T, AKC, BM, BK, NTHR>;
+  using OB = Operand<T, BKC, BN, BK, NTHR>;
   static constexpr int STAGE = OA::ELEMS + OB::ELEMS;  // elements per LDS stage
   static constexpr int NS = 2;  // LDS stages
   static constexpr int EPI_LD = TN + 4;                 // epilogue staging pitch (floats)
   static constexpr size_t OPS_BYTES = (size_t)NS * STAGE * sizeof(T);
-  static constexpr size_t EPI_BYTES = (size_t)4 * 32 * EPI_LD * 4;
+  static constexpr size_t EPI_BYTES = (size_t)NW * 32 * EPI_LD * 4;
   static constexpr size_t LDS_BYTES = OPS_BYTES > EPI_BYTES ? OPS_BYTES : EPI_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
@@ -442,7 +447,7 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
 // tile). Otherwise the tiles go through registers.
 template <typename T, int BM, int BN, bool AKC, bool BKC, bool DIRECT>
 __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0, int kbeg, int kend, T* st0,
-                                              f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+                                              f32x16 (&acc)[Cfg<T, BM, BN, AKC, BKC>::FM][Cfg<T, BM, BN, AKC, BKC>::FN]) {
   using CF = Cfg<T, BM, BN, AKC, BKC>;
   using MM = Mma<T>;
   using OA = typename CF::OA;
@@ -456,7 +461,7 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int wm = w / WGN, wn = w % WGN;
+  const int wm = w / CF::WGN, wn = w % CF::WGN;
 
   const int arow = wm * TM + (lane & 31);
   const int brow = wn * TN + (lane & 31);
@@ -571,7 +576,8 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
 }
 
 template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, float* split_out) {
+__global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(GemmArgs p, int k_split,
+                                                                               float* split_out) {
   using CF = Cfg<T, BM, BN, AKC, BKC>;
   constexpr int BK = CF::BK, TM = CF::TM, TN = CF::TN, FM = CF::FM, FN = CF::FN;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -601,7 +607,7 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs p, int k_split, flo
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wm = w / WGN, wn = w % WGN;
+  const int wm = w / CF::WGN, wn = w % CF::WGN;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -768,7 +774,7 @@ static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, 
                               (int)CF::LDS_BYTES);
     attr = true;
   }
-  kern<<<grid, NTHR, CF::LDS_BYTES, s>>>(a, k_split, split);
+  kern<<<grid, CF::NTHR, CF::LDS_BYTES, s>>>(a, k_split, split);
 }
 
 template <typename T, int BM, int BN, bool AKC, bool BKC>
