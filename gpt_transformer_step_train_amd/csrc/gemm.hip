@@ -732,10 +732,13 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
 
 constexpr int NCU = 256;
 
-static bool use_big(DType dt, int M, int N) {
+// The 256x256 tile (8 waves) wins once the grid fills at least half of the CUs for the
+// K-contiguous products (direct copies); with a row-contiguous operand the 128x128 tile (several
+// blocks per CU) stays ahead until about 1.5 rounds of the CUs.
+static bool use_big(DType dt, bool kc_both, int M, int N) {
   if (dt != DT_BF16) return false;
   const long t = (long)cdiv(M, 256) * cdiv(N, 256);
-  return t >= 384;
+  return t >= (kc_both ? 128 : 384);
 }
 
 #ifndef GEMM_DW_BIG
@@ -812,9 +815,9 @@ template <typename T, bool AKC, bool BKC>
 static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
   // split-K weight gradients (their M x N is small)
   if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2) return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
-  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.M, a.N))
+  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N))
     return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
-  if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.M, a.N))
+  if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N))
     return launch_t<T, 256, 256, AKC, BKC>(epi, a, nullptr, 0, s);
   return launch_t<T, 128, 128, AKC, BKC>(epi, a, scratch, sf, s);
 }
