@@ -26,13 +26,24 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
   if (row >= rows) return;
   const int nvec = C / VEC;
   const T* xr = x + (size_t)row * C;
+  // the row, the weight and the bias are all requested before the first reduction
+  u32x4 xraw[NV], wraw[NV], braw[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = lane + 64 * j;
+    if (v < nvec) {
+      xraw[j] = *reinterpret_cast<const u32x4*>(xr + v * VEC);
+      wraw[j] = *reinterpret_cast<const u32x4*>(w + v * VEC);
+      if (b) braw[j] = *reinterpret_cast<const u32x4*>(b + v * VEC);
+    }
+  }
   V16<T> xv[NV];
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = lane + 64 * j;
     if (v < nvec) {
-      xv[j].load(xr + v * VEC);
+      xv[j].unpack(xraw[j]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s += xv[j].v[e];
     }
@@ -58,8 +69,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
     const int v = lane + 64 * j;
     if (v < nvec) {
       V16<T> wv, bv, o;
-      wv.load(w + v * VEC);
-      if (b) bv.load(b + v * VEC);
+      wv.unpack(wraw[j]);
+      if (b) bv.unpack(braw[j]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o.v[e] = (xv[j].v[e] - mu) * rs * wv.v[e] + (b ? bv.v[e] : 0.f);
       o.store(yr + v * VEC);

@@ -85,22 +85,51 @@ __global__ __launch_bounds__(ADAM_T) void adamw_kernel(const WorkItem* __restric
   const float sc = *scale_p;
   const float wd = it.kind == 1 ? a.wd : 0.f;
   const size_t base = it.off;
-  for (int j = threadIdx.x * 4; j < (int)it.len; j += ADAM_T * 4) {
+  auto step4 = [&](f32x4& pv, const f32x4& gv, f32x4& mv, f32x4& vv) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gg = gv[e] * sc;
+      mv[e] = a.b1 * mv[e] + (1.f - a.b1) * gg;
+      vv[e] = a.b2 * vv[e] + (1.f - a.b2) * gg * gg;
+      const float mh = mv[e] * a.bc1;
+      const float vh = vv[e] * a.bc2;
+      pv[e] = pv[e] - a.lr * (mh / (sqrtf(vh) + a.eps) + wd * pv[e]);
+    }
+  };
+  // U vectors of 4 per thread and pass: all U x 4 loads are in flight before any arithmetic
+  constexpr int U = 4;
+  const int full = (int)it.len / (ADAM_T * 4 * U) * (ADAM_T * 4 * U);
+  for (int j0 = 0; j0 < full; j0 += ADAM_T * 4 * U) {
+    f32x4 pv[U], gv[U], mv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + j0 + (u * ADAM_T + threadIdx.x) * 4;
+      pv[u] = *reinterpret_cast<const f32x4*>(p + i);
+      gv[u] = *reinterpret_cast<const f32x4*>(g + i);
+      mv[u] = *reinterpret_cast<const f32x4*>(m + i);
+      vv[u] = *reinterpret_cast<const f32x4*>(v + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + j0 + (u * ADAM_T + threadIdx.x) * 4;
+      step4(pv[u], gv[u], mv[u], vv[u]);
+      *reinterpret_cast<f32x4*>(p + i) = pv[u];
+      *reinterpret_cast<f32x4*>(m + i) = mv[u];
+      *reinterpret_cast<f32x4*>(v + i) = vv[u];
+      if (shadow) {
+        u32x2 sv = {pack2bf(pv[u][0], pv[u][1]), pack2bf(pv[u][2], pv[u][3])};
+        *reinterpret_cast<u32x2*>(shadow + i) = sv;
+      }
+    }
+  }
+  for (int j = full + threadIdx.x * 4; j < (int)it.len; j += ADAM_T * 4) {
     const size_t i = base + j;
     if (j + 4 <= (int)it.len) {
       f32x4 pv = *reinterpret_cast<const f32x4*>(p + i);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(g + i);
       f32x4 mv = *reinterpret_cast<const f32x4*>(m + i);
       f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float gg = gv[e] * sc;
-        mv[e] = a.b1 * mv[e] + (1.f - a.b1) * gg;
-        vv[e] = a.b2 * vv[e] + (1.f - a.b2) * gg * gg;
-        const float mh = mv[e] * a.bc1;
-        const float vh = vv[e] * a.bc2;
-        pv[e] = pv[e] - a.lr * (mh / (sqrtf(vh) + a.eps) + wd * pv[e]);
-      }
+      step4(pv, gv, mv, vv);
       *reinterpret_cast<f32x4*>(p + i) = pv;
       *reinterpret_cast<f32x4*>(m + i) = mv;
       *reinterpret_cast<f32x4*>(v + i) = vv;
