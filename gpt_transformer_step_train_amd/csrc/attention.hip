@@ -354,36 +354,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
     pc.store_rows(is_k ? Ks : Vs, p);
     __syncthreads();
     if (kt + 1 < ntiles) load_tile(kt + 1);
+    // both 32-key halves of the tile at once: two independent S chains, one max, one rescale
+    const int kb0 = kt * KT;
+    if (kb0 <= qw0 + 31) {  // else the whole tile is in the future of this wave's queries
+      f32x16 st[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int kb = kt * KT + sb * 32;
-      if (kb > qw0 + 31) continue;  // entirely in the future of this wave's queries
-      f32x16 st = zero16();
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) st = mfma(lds_frag16(Ks + (sb * 32 + l32) * LDP + 16 * s + 8 * g), qf[s], st);
-      float sc[16];
-      float mloc = -INFINITY;
-      if (kb + 31 > qw0) {  // diagonal sub-block: mask keys after the query
+        for (int sb = 0; sb < 2; ++sb)
+          st[sb] = mfma(lds_frag16(Ks + (sb * 32 + l32) * LDP + 16 * s + 8 * g), qf[s], st[sb]);
+      float sc[32];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + acc_row(i, g);
-          sc[i] = key <= myq ? st[i] * c2 : -INFINITY;
-          mloc = fmaxf(mloc, sc[i]);
-        }
-      } else {
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = st[0][i];
+        sc[16 + i] = st[1][i];
+      }
+      if (kb0 + 63 > qw0) {  // diagonal tile: mask keys after the query
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sc[i] = st[i] * c2;
-          mloc = fmaxf(mloc, sc[i]);
+        for (int i = 0; i < 32; ++i) {
+          const int key = kb0 + (i >> 4) * 32 + acc_row(i & 15, g);
+          if (key > myq) sc[i] = -INFINITY;
         }
       }
+      float mloc = sc[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) mloc = fmaxf(mloc, sc[i]);
       mloc = pair_max(mloc);
-      const float m_new = fmaxf(m_run, mloc);
+      const float m_new = fmaxf(m_run, mloc * c2);  // scaled, log2 units
       const float corr = fast_exp2(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sc[i] = fast_exp2(sc[i] - m_new);
+      for (int i = 0; i < 32; ++i) {
+        sc[i] = fast_exp2(fmaf(sc[i], c2, -m_new));
         psum += sc[i];
       }
       l_run = l_run * corr + psum;
@@ -394,11 +396,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
         for (int i = 0; i < 16; ++i) o[db][i] *= corr;
       // O^T += V^T P^T : A = V^T (rows d, k = keys), B = P^T (k = keys, columns = queries)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pf = pack_frag(sc + 8 * ks);
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) o[db] = mfma(tr_frag(Vs, sb * 32 + 16 * ks, db * 32, lane), pf, o[db]);
-      }
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 pf = pack_frag(sc + 16 * sb + 8 * ks);
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            o[db] = mfma(tr_frag(Vs, sb * 32 + 16 * ks, db * 32, lane), pf, o[db]);
+        }
     }
     __syncthreads();
   }
