@@ -59,6 +59,7 @@ template <> struct Mma<float> {
 #define GEMM_BIG_WAVES 8
 #endif
 constexpr int GROUP_M = 8;
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int TKR = 4;  // transposed piece: TKR k-rows x VEC row-contiguous elements
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -295,9 +296,11 @@ template <typename T, bool KC, int ROWS, int BK_, int NTHR> struct Operand {
 
 template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
-  // waves per block, in a 2 x (NW/2) grid over the tile
-  static constexpr int NW = (sizeof(T) == 2 && BM == 256 && BN == 256) ? GEMM_BIG_WAVES : 4;
-  static constexpr int NTHR = 64 * NW, WGM = 2, WGN = NW / 2;
+  // waves per block, in a WGM x WGN grid over the tile: 2 x (NW/2), except 256 x 192 (4 x 2,
+  // 64 x 96 per wave)
+  static constexpr bool BIG = sizeof(T) == 2 && BM == 256 && (BN == 256 || BN == 192);
+  static constexpr int NW = BIG ? GEMM_BIG_WAVES : 4;
+  static constexpr int NTHR = 64 * NW, WGM = BN == 192 ? 4 : 2, WGN = NW / WGM;
   static constexpr int TM = BM / WGM, TN = BN / WGN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   // k per LDS stage: 64 when both bf16 operands are K-contiguous (direct copies, 64 MFMAs per
@@ -642,28 +645,34 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
   const int g = lane >> 5, l32 = lane & 31;
   constexpr int CPR = TN / 8;             // 8-column chunks per staged row
   constexpr int NIT = (32 * CPR) / 64;    // chunks per lane per slab
-  static_assert(64 % CPR == 0, "a lane keeps its column chunk across a slab");
-  const int cc = (lane % CPR) * 8;
-  const int col = n0 + wn * TN + cc;
-  float bv[8];
+  static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
+  // chunk it * 64 + lane of a slab: row / CPR, column chunk % CPR; a lane's column chunk repeats
+  // every BP chunks (1 when CPR divides 64)
+  constexpr int BP = CPR / gcd_c(64, CPR);
+  auto ccol = [&](int it) { return ((it * 64 + lane) % CPR) * 8; };
+  float bv[BP][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) bv[e] = 0.f;
-  if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID || EPI == EPI_GELU_GRAD) {
-    if (p.bias && col < p.N) {
-      const T* bias = reinterpret_cast<const T*>(p.bias) + col;
-      if (col + 8 <= p.N) {
-        constexpr int VEC = Elt<T>::VEC;
+  for (int bp = 0; bp < BP; ++bp) {
 #pragma unroll
-        for (int h = 0; h < 8 / VEC; ++h) {
-          V16<T> t;
-          t.load(bias + h * VEC);
+    for (int e = 0; e < 8; ++e) bv[bp][e] = 0.f;
+    const int col = n0 + wn * TN + ccol(bp);
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID || EPI == EPI_GELU_GRAD) {
+      if (p.bias && col < p.N) {
+        const T* bias = reinterpret_cast<const T*>(p.bias) + col;
+        if (col + 8 <= p.N) {
+          constexpr int VEC = Elt<T>::VEC;
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) bv[h * VEC + e] = t.v[e];
+          for (int h = 0; h < 8 / VEC; ++h) {
+            V16<T> t;
+            t.load(bias + h * VEC);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) bv[bp][h * VEC + e] = t.v[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) bv[bp][e] = ld1(bias, e);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (col + e < p.N) bv[e] = ld1(bias, e);
       }
     }
   }
@@ -683,6 +692,7 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int row = row0 + (it * 64 + lane) / CPR;
+      const int col = n0 + wn * TN + ccol(it);
       if (row < p.M && col < p.N) epi_fetch8<T, EPI>(q, C_f32, ldc, row, col, xo[it]);
     }
   };
@@ -703,11 +713,12 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
     for (int it = 0; it < NIT; ++it) {
       const int rr = (it * 64 + lane) / CPR;
       const int row = row0 + rr;
+      const int cc = ccol(it), col = n0 + wn * TN + cc;
       if (row < p.M && col < p.N) {
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc + 4);
         const float a8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv, xs[ALL_AT_ONCE ? i : 0][it]);
+        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv[it % BP], xs[ALL_AT_ONCE ? i : 0][it]);
       }
     }
     wave_sync();
@@ -811,12 +822,23 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
   return hipGetLastError();
 }
 
+// Fraction of the CU slots busy over the rounds a grid of this many single-block-per-CU tiles takes.
+static double round_fill(long tiles) { return (double)tiles / (double)(cdiv((int)tiles, NCU) * NCU); }
+
 template <typename T, bool AKC, bool BKC>
 static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
   // split-K weight gradients (their M x N is small)
   if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2) return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
-  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N))
+  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N)) {
+    // K-contiguous products whose 256-wide column tiles leave CUs idle in the last round
+    // (N = 768: 192 tiles per 16384 rows) take 192-wide column tiles when those fill the rounds
+    // clearly better
+    if constexpr (AKC && BKC && sizeof(T) == 2) {
+      const long t256 = (long)cdiv(a.M, 256) * cdiv(a.N, 256), t192 = (long)cdiv(a.M, 256) * cdiv(a.N, 192);
+      if (round_fill(t192) > round_fill(t256) + 0.05) return launch_t<T, 256, 192, AKC, BKC>(epi, a, scratch, sf, s);
+    }
     return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
+  }
   if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N))
     return launch_t<T, 256, 256, AKC, BKC>(epi, a, nullptr, 0, s);
   return launch_t<T, 128, 128, AKC, BKC>(epi, a, scratch, sf, s);

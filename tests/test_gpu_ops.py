@@ -99,8 +99,20 @@ def test_gemm_bf16_256_tile_path(layout, epi, K):
     """Shapes with >= 384 tiles of 256 x 256 take the large-tile kernel; ragged M and N. With K a
     multiple of 64 the interior tiles take the direct global -> LDS copies, the edge tiles the
     register path; with K = 72 every tile has a ragged K tail."""
+    check_big_gemm(layout, epi, K, 4100, 6392)
+
+
+@pytest.mark.parametrize("K", [72, 192])
+@pytest.mark.parametrize("epi", [bd.EPI_BIAS, bd.EPI_GELU, bd.EPI_RESID, bd.EPI_GELU_GRAD, bd.EPI_MUL])
+def test_gemm_bf16_256x192_tile_path(epi, K):
+    """K-contiguous products where 192-wide column tiles fill the CU rounds better than 256-wide
+    ones (here 17 x 12 = 204 tiles against 17 x 9 = 153) take the 256 x 192 kernel: ragged M and
+    N, direct copies and register-path edge tiles, ragged K tail with K = 72."""
+    check_big_gemm((1, 1), epi, K, 4100, 2300)
+
+
+def check_big_gemm(layout, epi, K, M, N):
     akc, bkc = layout
-    M, N = 4100, 6392
     rng = np.random.default_rng(epi * 10 + akc * 2 + bkc)
     A, Bm = rng.normal(0, 1, (M, K)), rng.normal(0, 1, (N, K))
     bias = rng.normal(0, 1, N)
