@@ -187,7 +187,8 @@ KERNEL_CLASSES = ["encoder_fwd", "layernorm_fwd", "gemm_qkv", "attention_fwd", "
                   "gemm_fcproj", "gemm_classifier", "cross_entropy", "gemm_classifier_dx", "gemm_classifier_dw",
                   "layernorm_bwd", "gemm_fcproj_dx", "gemm_fcproj_dw", "bias_grad", "gemm_fc_dx", "gemm_fc_dw",
                   "gemm_attproj_dx", "gemm_attproj_dw", "attention_bwd", "gemm_qkv_dx", "gemm_qkv_dw",
-                  "encoder_bwd", "grad_norm", "adamw", "attention_bwd_q", "attention_bwd_pre"]
+                  "encoder_bwd", "grad_norm", "adamw", "attention_bwd_q", "attention_bwd_pre",
+                  "weight_transpose"]
 
 
 def gpt2_profile_enable(mask):

@@ -114,6 +114,15 @@ hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float
 hipError_t launch_init_params(const WorkItem* items, int nitems, float* p, uint64_t seed, double std_,
                               hipStream_t s);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
+// Transposed bf16 copy of a weight matrix: dst[dst_off + c * ldd + r] = src[src_off + r * cols + c],
+// r < rows, c < cols. tile0: the first 64 x 64 tile of this matrix in the launch's tile numbering.
+struct TransItem {
+  uint64_t src_off, dst_off;
+  int32_t rows, cols, ldd, tile0;
+};
+inline int trans_tiles(int rows, int cols) { return ((rows + 63) / 64) * ((cols + 63) / 64); }
+hipError_t launch_transpose_bf16(const TransItem* items, int nitems, int ntiles, const uint16_t* src, uint16_t* dst,
+                                 hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
 

@@ -50,6 +50,13 @@ struct Model {
   // device pointers inside the workspace
   float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
   uint16_t* shadow = nullptr;
+  // bf16 runs: transposed copies of the weight matrices (layer matrices at their parameter
+  // offsets in shadow_t, the token embedding as C x ldl in wte_t) for the input-gradient products,
+  // which then read both operands K-contiguous
+  uint16_t *shadow_t = nullptr, *wte_t = nullptr;
+  std::vector<TransItem> tr_host;
+  TransItem* tr_items = nullptr;
+  int tr_tiles = 0;
   WorkItem* items = nullptr;
   char* encoded = nullptr;
   std::vector<LayerAct> la;
@@ -227,6 +234,11 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
   M->m = (float*)take(N * 4);
   M->v = (float*)take(N * 4);
   M->shadow = c->precision == GPT2_BF16 ? (uint16_t*)take(N * 2) : nullptr;
+  if (c->precision == GPT2_BF16) {
+    M->shadow_t = (uint16_t*)take(N * 2);
+    M->wte_t = (uint16_t*)take(C * ldl * 2);
+    M->tr_items = (TransItem*)take((1 + 4 * L) * sizeof(TransItem));
+  }
   M->items = (WorkItem*)take(nitems * sizeof(WorkItem));
   M->encoded = take(BT * C * es);
   M->la.resize(L);
@@ -313,6 +325,40 @@ const void* W(size_t off) {
   return g.params + off;
 }
 float* G(size_t off) { return off == NONE ? nullptr : g.grads + off; }
+// transposed bf16 copy of a layer weight matrix (bf16 runs only)
+const void* WT(size_t off) { return g.shadow_t + off; }
+
+// The transposed copies: the token embedding [Vp, C] -> [C, ldl], each layer's qkvw [3C, C],
+// attprojw [C, C], fcw [4C, C] and fcprojw [C, 4C] -> their transposes at the same offsets.
+void make_trans_items() {
+  g.tr_host.clear();
+  g.tr_tiles = 0;
+  auto add = [&](size_t src_off, size_t dst_off, int rows, int cols, int ldd) {
+    TransItem t{};
+    t.src_off = src_off;
+    t.dst_off = dst_off;
+    t.rows = rows;
+    t.cols = cols;
+    t.ldd = ldd;
+    t.tile0 = g.tr_tiles;
+    g.tr_tiles += trans_tiles(rows, cols);
+    g.tr_host.push_back(t);
+  };
+  const int C = g.C;
+  add(g.o_wte, (size_t)(g.wte_t - g.shadow_t), g.Vp, C, g.ldl);
+  for (int l = 0; l < g.L; ++l) {
+    const LayerOff& o = g.lo[l];
+    add(o.qkvw, o.qkvw, 3 * C, C, 3 * C);
+    add(o.attprojw, o.attprojw, C, C, C);
+    add(o.fcw, o.fcw, 4 * C, C, 4 * C);
+    add(o.fcprojw, o.fcprojw, C, 4 * C, C);
+  }
+}
+hipError_t refresh_transposed() {
+  if (!g.shadow_t) return hipSuccess;
+  ProfScope ps_(GPT2_K_WEIGHT_TRANSPOSE);
+  return launch_transpose_bf16(g.tr_items, (int)g.tr_host.size(), g.tr_tiles, g.shadow, g.shadow_t, g.stream);
+}
 
 int gemm(bool akc, bool bkc, Epi epi, int M, int N, int K, const void* A, long lda, const void* Bp, long ldb,
          void* Cp, long ldc, const void* bias = nullptr, const void* aux = nullptr, long ldaux = 0,
@@ -429,7 +475,8 @@ int backward_impl() {
   // classifier (tied wte): dz = dlogits wte ; dwte (+)= dlogits^T z
   {
       ProfScope ps_(GPT2_K_GEMM_CLASSIFIER_DX);
-      RUN(gemm(true, false, EPI_BIAS, BT, C, g.Vp, g.logits, g.ldl, W(g.o_wte), C, g.dbuf2, C));
+      if (g.wte_t) RUN(gemm(true, true, EPI_BIAS, BT, C, g.Vp, g.logits, g.ldl, g.wte_t, g.ldl, g.dbuf2, C));
+      else RUN(gemm(true, false, EPI_BIAS, BT, C, g.Vp, g.logits, g.ldl, W(g.o_wte), C, g.dbuf2, C));
     }
   {
       ProfScope ps_(GPT2_K_GEMM_CLASSIFIER_DW);
@@ -451,8 +498,12 @@ int backward_impl() {
     // fcproj: res2 = res1 + gelu(z) Wfcproj^T + b ; dz = (dres Wfcproj) * gelu'(z)
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DX);
-      RUN(gemm(true, false, EPI_MUL, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
-               4 * C));
+      if (g.shadow_t)
+        RUN(gemm(true, true, EPI_MUL, BT, 4 * C, C, g.dres, C, WT(o.fcprojw), C, g.dbuf1, 4 * C, nullptr, a.fch,
+                 4 * C));
+      else
+        RUN(gemm(true, false, EPI_MUL, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
+                 4 * C));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DW);
@@ -463,7 +514,8 @@ int backward_impl() {
     // fc: z = ln2 Wfc^T + b (fch = gelu'(z), fchg = gelu(z))
     {
       ProfScope ps_(GPT2_K_GEMM_FC_DX);
-      RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
+      if (g.shadow_t) RUN(gemm(true, true, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, WT(o.fcw), 4 * C, g.dbuf2, C));
+      else RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FC_DW);
@@ -483,7 +535,8 @@ int backward_impl() {
     // attproj: res1 = xin + atty Wproj^T + b
     {
       ProfScope ps_(GPT2_K_GEMM_ATTPROJ_DX);
-      RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
+      if (g.shadow_t) RUN(gemm(true, true, EPI_BIAS, BT, C, C, g.dres, C, WT(o.attprojw), C, g.dbuf2, C));
+      else RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_ATTPROJ_DW);
@@ -508,7 +561,8 @@ int backward_impl() {
     // qkv = ln1 Wqkv^T + b
     {
       ProfScope ps_(GPT2_K_GEMM_QKV_DX);
-      RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
+      if (g.shadow_t) RUN(gemm(true, true, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, WT(o.qkvw), 3 * C, g.dbuf2, C));
+      else RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_QKV_DW);
@@ -600,6 +654,12 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed) {
   HIPCHK(launch_fill_f32(g.v, g.N, 0.f, g.stream));
   HIPCHK(launch_fill_f32(g.grads, g.N, 0.f, g.stream));
   if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
+  if (g.shadow_t) {
+    make_trans_items();
+    HIPCHK(hipMemcpyAsync(g.tr_items, g.tr_host.data(), g.tr_host.size() * sizeof(TransItem), hipMemcpyHostToDevice,
+                          g.stream));
+    HIPCHK(refresh_transposed());
+  }
   HIPCHK(hipStreamSynchronize(g.stream));
   g.ready = true;
   return ok();
@@ -661,6 +721,7 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
       HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale, g.norm2,
                       a, s));
     }
+  HIPCHK(refresh_transposed());
   g.micro = 0;
   return ok();
 }
@@ -730,6 +791,7 @@ int gpt2_set_params(const float* src, uint64_t n) {
   if (!src || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
   HIPCHK(hipMemcpyAsync(g.params, src, n * 4, hipMemcpyHostToDevice, g.stream));
   if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
+  HIPCHK(refresh_transposed());
   HIPCHK(hipStreamSynchronize(g.stream));
   return ok();
 }

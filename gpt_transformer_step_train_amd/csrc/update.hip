@@ -211,6 +211,69 @@ hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t
   return hipGetLastError();
 }
 
+// One block per 64 x 64 tile: 16-byte row vectors of the source into LDS, 16-byte row vectors of
+// the copy out of it (each gathered from 8 LDS rows).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const TransItem* __restrict__ items, int nitems,
+                                                             const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst) {
+  constexpr int P = 72;  // LDS row pitch (elements): 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
+  int i = nitems - 1;
+  while (i > 0 && items[i].tile0 > (int)blockIdx.x) --i;
+  const TransItem it = items[i];
+  const int t = (int)blockIdx.x - it.tile0;
+  const int tcols = (it.cols + 63) / 64;
+  const int r0 = (t / tcols) * 64, c0 = (t % tcols) * 64;
+  const uint16_t* s = src + it.src_off;
+  uint16_t* d = dst + it.dst_off;
+  const bool svec = ((it.src_off | (uint64_t)it.cols) & 7) == 0;
+  const bool dvec = ((it.dst_off | (uint64_t)it.ldd) & 7) == 0;
+  for (int v = threadIdx.x; v < 512; v += 256) {
+    const int r = v >> 3, c = (v & 7) * 8;
+    const int gr = r0 + r, gc = c0 + c;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (gr < it.rows) {
+      const uint16_t* row = s + (size_t)gr * it.cols;
+      if (svec && gc + 8 <= it.cols) {
+        x = *reinterpret_cast<const u32x4*>(row + gc);
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = gc + k < it.cols ? row[gc + k] : (uint16_t)0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = (uint32_t)e[2 * k] | ((uint32_t)e[2 * k + 1] << 16);
+      }
+    }
+    *reinterpret_cast<u32x4*>(tile + r * P + c) = x;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < 512; v += 256) {
+    const int c = v >> 3, r = (v & 7) * 8;  // row c of the copy, source rows r .. r + 7
+    const int gc = c0 + c, gr = r0 + r;
+    if (gc >= it.cols || gr >= it.rows) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = tile[(r + k) * P + c];
+    uint16_t* out = d + (size_t)gc * it.ldd + gr;
+    if (dvec && gr + 8 <= it.rows) {
+      u32x4 x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = (uint32_t)e[2 * k] | ((uint32_t)e[2 * k + 1] << 16);
+      *reinterpret_cast<u32x4*>(out) = x;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (gr + k < it.rows) out[k] = e[k];
+    }
+  }
+}
+hipError_t launch_transpose_bf16(const TransItem* items, int nitems, int ntiles, const uint16_t* src, uint16_t* dst,
+                                 hipStream_t s) {
+  if (nitems <= 0 || ntiles <= 0) return hipSuccess;
+  transpose_bf16_kernel<<<ntiles, 256, 0, s>>>(items, nitems, src, dst);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
                                                    size_t n16) {
   for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = src[i];

@@ -132,7 +132,8 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_ADAMW 24
 #define GPT2_K_ATTENTION_BWD_Q 25    /* dQ                                    */
 #define GPT2_K_ATTENTION_BWD_PRE 26  /* D = rowsum(dO * O) per query          */
-#define GPT2_K_COUNT 27
+#define GPT2_K_WEIGHT_TRANSPOSE 27  /* bf16 weight matrices -> transposed copies */
+#define GPT2_K_COUNT 28
 int gpt2_profile_enable(uint32_t mask);
 int gpt2_profile_read(float* ms, int32_t* launches, int32_t n);
 
