@@ -7,18 +7,19 @@
 // run in the GEMM epilogue instead of separate passes over HBM.
 //
 // Design (CDNA4, wave64):
-//  * Two block tiles, both with 4 waves in a 2x2 grid: 256x256 (128x128 per wave = 4x4 MFMA
-//    32x32 blocks, 256 accumulator registers) for the wide products, 128x128 (64x64 per wave)
-//    for N = C products and split-K weight gradients, chosen per shape so the grid covers the
-//    256 CUs in whole rounds. bf16: v_mfma_f32_32x32x16_bf16; fp32: v_mfma_f32_32x32x2f32.
-//  * K-contiguous bf16 products (the forward GEMMs) stage 64 of K per tile; their interior tiles
-//    are copied global -> LDS directly (global_load_lds_dwordx4: no staging registers, no LDS
-//    write instructions) into [row][k] rows whose 16-byte chunks are XOR-swizzled so that the
-//    MFMA fragment reads are free of bank conflicts.
-//  * Products with a row-contiguous operand (input and weight gradients) stage 32 of K per tile
-//    through registers; the row-contiguous side stays [k][row] in LDS and its MFMA fragments are
-//    read with the gfx950 transpose load ds_read_b64_tr_b16. (Those reads are kept away from
-//    direct copies: the compiler makes each of them wait for every copy in flight.)
+//  * Block tiles: 256x256 with 8 waves (2 per SIMD, 128x64 each = 4x2 MFMA 32x32 blocks) for
+//    the large bf16 products and the split-K weight gradients; 256x192 with 8 waves (64x96 each)
+//    where 192-wide column tiles fill the rounds of 256 CUs better (N = 768, 2304); 128x128 with
+//    4 waves (64x64 each) for small grids and fp32. bf16: v_mfma_f32_32x32x16_bf16; fp32:
+//    v_mfma_f32_32x32x2f32.
+//  * bf16 products stage 64 of K per tile; interior tiles are copied global -> LDS directly
+//    (global_load_lds_dwordx4: no staging registers, no LDS write instructions). A K-contiguous
+//    operand lands as [row][k] rows whose 16-byte chunks are XOR-swizzled so that the MFMA
+//    fragment reads are free of bank conflicts; a row-contiguous one (the weight gradients) stays
+//    [k][row] and its MFMA fragments are read with the gfx950 transpose load ds_read_b64_tr_b16.
+//    The copies into one stage and the reads of another are issued through distinct restrict
+//    pointers: without that the compiler makes every transpose read wait for all copies in
+//    flight. Edge tiles and fp32 go through registers.
 //  * Double-buffered LDS, one barrier per tile; operand fragments double-buffered in registers
 //    so the LDS reads of one k-step overlap the MFMAs of the previous one.
 //  * Epilogue through LDS: each wave parks 32 rows of fp32 accumulators in LDS and reads them back
@@ -86,9 +87,8 @@ template <typename T, bool KC, int ROWS, int BK_, int NTHR> struct Operand {
   static constexpr int VEC = Elt<T>::VEC;
   static constexpr int BK = BK_;
   static constexpr int MODE = KC ? 0 : (sizeof(T) == 2 ? 2 : 1);
-  // interior tiles can be copied global -> LDS (mode 2 is not: the compiler waits for every
-  // pending global -> LDS copy before each ds_read_b64_tr_b16, which would serialise the pipeline)
-  static constexpr bool DIRECT = MODE == 0;
+  // interior tiles can be copied global -> LDS
+  static constexpr bool DIRECT = MODE == 0 || MODE == 2;
   static constexpr int LD = MODE == 0 ? BK : BK + VEC;  // [row][k] pitch (elements), modes 0 / 1
   // mode 2 geometry
   static constexpr int RB = 512 / ROWS;             // k-rows per 1024-byte block
@@ -303,9 +303,9 @@ template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   static constexpr int NTHR = 64 * NW, WGM = BN == 192 ? 4 : 2, WGN = NW / WGM;
   static constexpr int TM = BM / WGM, TN = BN / WGN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  // k per LDS stage: 64 when both bf16 operands are K-contiguous (direct copies, 64 MFMAs per
-  // wave between barriers), else 32 (register staging; half the staging registers)
-  static constexpr int BK = sizeof(T) == 2 && AKC && BKC ? 64 : 32;
+  // k per LDS stage: 64 for bf16 (direct copies, 4 k-steps of MFMAs per wave between barriers),
+  // 32 for fp32 (register staging)
+  static constexpr int BK = sizeof(T) == 2 ? 64 : 32;
   using OA = Operand<T, AKC, BM, BK, NTHR>;
   using OB = Operand<T, BKC, BN, BK, NTHR>;
   static constexpr int STAGE = OA::ELEMS + OB::ELEMS;  // elements per LDS stage
@@ -545,8 +545,18 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (kt + NS - 1 < nkt) issue(kt + NS - 1);
-      compute(Abuf(kt % NS), Bbuf(kt % NS));
+      // the copies into one stage and the fragment reads of another go through distinct restrict
+      // pointers, so the compiler's wait analysis can tell them apart
+      auto body = [&](const T* __restrict__ ra, const T* __restrict__ rb, T* __restrict__ da, T* __restrict__ db,
+                      int t) {
+        if (t < nkt) {
+          OA::issue_direct(A, p.lda, m0, kbeg + t * BK, da);
+          OB::issue_direct(B, p.ldb, n0, kbeg + t * BK, db);
+        }
+        compute(ra, rb);
+      };
+      const int tn = kt + NS - 1;
+      body(Abuf(kt % NS), Bbuf(kt % NS), Abuf(tn % NS), Bbuf(tn % NS), tn);
 
     }
     __syncthreads();  // the epilogue reuses the LDS
