@@ -24,7 +24,7 @@ EXPORTS = [
     "gpt2_profile_read",
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
-    "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy",
+    "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
 ]
 
 
@@ -70,6 +70,8 @@ def load(path=LIB_PATH):
         "gpt2_profile_read": (ctypes.c_int, [_vp, _vp, _i32]),
         "gpt2op_gemm": (ctypes.c_int, [ctypes.c_int] * 7 + [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp,
                                                             ctypes.c_int, _vp, _u64, _vp]),
+        "gpt2op_gemm_colsum": (ctypes.c_int, [ctypes.c_int] * 7 + [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
+                                                                   _vp, _vp, ctypes.c_int, _vp, _u64, _vp]),
         "gpt2op_layernorm_forward": (ctypes.c_int, [ctypes.c_int] * 3 + [_vp] * 7),
         "gpt2op_layernorm_backward": (ctypes.c_int, [ctypes.c_int] * 3 + [_vp] * 9 + [ctypes.c_int, _vp, _vp]),
         "gpt2op_layernorm_backward_scratch": (_u64, [ctypes.c_int, ctypes.c_int]),

@@ -366,7 +366,8 @@ __device__ __forceinline__ void epi_fetch8(const GemmArgs& p, const float* C_f32
 // the chunk is whole, element by element at the right edge). bv: bias of the 8 columns.
 template <typename T, int EPI>
 __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long ldc, int row, int col,
-                                           const float (&a)[8], const float (&bv)[8], const EpiX<T, EPI>& x) {
+                                           const float (&a)[8], const float (&bv)[8], const EpiX<T, EPI>& x,
+                                           bool csum, float (&cs)[8]) {
   const bool full = col + 8 <= p.N;
   if constexpr (EPI == EPI_F32) {
     float* dst = C_f32 + (size_t)row * ldc + col;
@@ -412,6 +413,11 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& p, float* C_f32, long
       else if constexpr (EPI == EPI_RESID) o[e] = xv[e] + (a[e] + bv[e]);
       else if constexpr (EPI == EPI_MUL) o[e] = a[e] * xv[e];
       else o[e] = a[e] * gelu_bwd(xv[e]);
+    }
+    if (csum) {  // column sums of the values as stored
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < p.N) cs[e] += sizeof(T) == 2 ? bf2f(f2bf(o[e])) : o[e];
     }
     T* dst = reinterpret_cast<T*>(p.C) + (size_t)row * ldc + col;
     if (full) {
@@ -651,6 +657,13 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
       q.accumulate = 0;
     }
   }
+  // column sums of the output (non-fp32 epilogues): split_out then holds the partial sums, one row
+  // per (tile row, wave row); a lane's column chunk must be the same for all of its rows
+  constexpr bool CSUM_OK = EPI != EPI_F32 && 64 % (TN / 8) == 0;
+  const bool csum = CSUM_OK && split_out != nullptr;
+  float cs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cs[e] = 0.f;
   float* stage = reinterpret_cast<float*>(smem) + w * 32 * CF::EPI_LD;
   const int g = lane >> 5, l32 = lane & 31;
   constexpr int CPR = TN / 8;             // 8-column chunks per staged row
@@ -728,10 +741,26 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + rr * CF::EPI_LD + cc + 4);
         const float a8[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv[it % BP], xs[ALL_AT_ONCE ? i : 0][it]);
+        epi_store8<T, EPI>(q, C_f32, ldc, row, col, a8, bv[it % BP], xs[ALL_AT_ONCE ? i : 0][it], csum, cs);
       }
     }
     wave_sync();
+  }
+  if constexpr (CSUM_OK) {
+    if (csum) {
+      // lanes l, l + CPR, l + 2 CPR, ... hold the same columns: fixed-order butterfly over them
+#pragma unroll
+      for (int msk = CPR; msk < 64; msk <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] += __shfl_xor(cs[e], msk);
+      const int col = n0 + wn * TN + ccol(0);
+      if (lane < CPR && col < p.N) {
+        float* dst = split_out + (size_t)(tm * CF::WGM + wm) * p.N + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < p.N) dst[e] = cs[e];
+      }
+    }
   }
 }
 
@@ -749,125 +778,6 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
     for (int z = 0; z < splits; ++z) s += part[(size_t)z * n + i];
     dst[i] = s;
   }
-}
-
-constexpr int NCU = 256;
-
-// The 256x256 tile (8 waves) wins once the grid fills at least half of the CUs for the
-// K-contiguous products (direct copies); with a row-contiguous operand the 128x128 tile (several
-// blocks per CU) stays ahead until about 1.5 rounds of the CUs.
-static bool use_big(DType dt, bool kc_both, int M, int N) {
-  if (dt != DT_BF16) return false;
-  const long t = (long)cdiv(M, 256) * cdiv(N, 256);
-  return t >= (kc_both ? 128 : 384);
-}
-
-#ifndef GEMM_DW_BIG
-#define GEMM_DW_BIG 1
-#endif
-// Split-K factor for the fp32 weight-gradient products. The blocks run in ceil(tiles s / NCU)
-// rounds of K / s each, and every split adds an fp32 partial of M x N that is written and read
-// back once; pick the s that minimises that time (K per split >= 512, partials within scratch).
-int gemm_splits_t(int M, int N, int K, size_t scratch_floats, int tile) {
-  const long tiles = (long)cdiv(M, tile) * cdiv(N, tile);
-  // per-CU MFMA rate and HBM rate as seen by these kernels (order of magnitude is enough)
-  const double cu_flops = 1.8e12, hbm = 5.0e12;
-  const double tile_flops_per_k = 2.0 * tile * tile;
-  int best = 1;
-  double best_t = 1e30;
-  for (int s = 1; s <= 32; ++s) {
-    if (s > 1 && ((long)K / s < 512 || (size_t)s * M * N > scratch_floats)) break;
-    const double rounds = (double)((tiles * s + NCU - 1) / NCU);
-    const double t = rounds * tile_flops_per_k * ((double)K / s) / cu_flops + (s > 1 ? s * 8.0 * M * N / hbm : 0.0);
-    if (t < best_t * 0.995) {
-      best_t = t;
-      best = s;
-    }
-  }
-  return best;
-}
-int gemm_splits(int M, int N, int K, size_t scratch_floats) { return gemm_splits_t(M, N, K, scratch_floats, 128); }
-
-template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
-static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, hipStream_t s) {
-  using CF = Cfg<T, BM, BN, AKC, BKC>;
-  static bool attr = false;
-  auto kern = gemm_kernel<T, BM, BN, AKC, BKC, EPI>;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)CF::LDS_BYTES);
-    attr = true;
-  }
-  kern<<<grid, CF::NTHR, CF::LDS_BYTES, s>>>(a, k_split, split);
-}
-
-template <typename T, int BM, int BN, bool AKC, bool BKC>
-static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t scratch_floats, hipStream_t s) {
-  const int tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
-  int splits = 1;
-  if (epi == EPI_F32 && scratch) splits = gemm_splits_t(a.M, a.N, a.K, scratch_floats, BM);
-  int k_split = a.K;
-  if (splits > 1) {
-    constexpr int BK = Cfg<T, BM, BN, AKC, BKC>::BK;
-    k_split = cdiv(cdiv(a.K, splits), BK) * BK;
-    splits = cdiv(a.K, k_split);
-  }
-  dim3 grid(((long)tiles * splits + 7) & ~7L);
-  switch (epi) {
-    case EPI_BIAS: launch_cfg<T, BM, BN, AKC, BKC, EPI_BIAS>(grid, a, k_split, nullptr, s); break;
-    case EPI_GELU: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU>(grid, a, k_split, nullptr, s); break;
-    case EPI_RESID: launch_cfg<T, BM, BN, AKC, BKC, EPI_RESID>(grid, a, k_split, nullptr, s); break;
-    case EPI_GELU_BWD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_BWD>(grid, a, k_split, nullptr, s); break;
-    case EPI_GELU_GRAD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_GRAD>(grid, a, k_split, nullptr, s); break;
-    case EPI_MUL: launch_cfg<T, BM, BN, AKC, BKC, EPI_MUL>(grid, a, k_split, nullptr, s); break;
-    case EPI_F32:
-      launch_cfg<T, BM, BN, AKC, BKC, EPI_F32>(grid, a, k_split, splits > 1 ? scratch : nullptr, s);
-      if (splits > 1) {
-        const size_t n = (size_t)a.M * a.N;
-        const int blocks = (int)std::min<size_t>(4096, (n / 4 + 255) / 256 + 1);
-        splitk_reduce<<<blocks, 256, 0, s>>>(scratch, splits, n, reinterpret_cast<float*>(a.C), a.accumulate);
-      }
-      break;
-  }
-  return hipGetLastError();
-}
-
-// Fraction of the CU slots busy over the rounds a grid of this many single-block-per-CU tiles takes.
-static double round_fill(long tiles) { return (double)tiles / (double)(cdiv((int)tiles, NCU) * NCU); }
-
-template <typename T, bool AKC, bool BKC>
-static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
-  // split-K weight gradients (their M x N is small)
-  if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2) return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
-  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N)) {
-    // K-contiguous products whose 256-wide column tiles leave CUs idle in the last round
-    // (N = 768: 192 tiles per 16384 rows) take 192-wide column tiles when those fill the rounds
-    // clearly better
-    if constexpr (AKC && BKC && sizeof(T) == 2) {
-      const long t256 = (long)cdiv(a.M, 256) * cdiv(a.N, 256), t192 = (long)cdiv(a.M, 256) * cdiv(a.N, 192);
-      if (round_fill(t192) > round_fill(t256) + 0.05) return launch_t<T, 256, 192, AKC, BKC>(epi, a, scratch, sf, s);
-    }
-    return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
-  }
-  if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N))
-    return launch_t<T, 256, 256, AKC, BKC>(epi, a, nullptr, 0, s);
-  return launch_t<T, 128, 128, AKC, BKC>(epi, a, scratch, sf, s);
-}
-
-hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& a, float* scratch,
-                       size_t scratch_floats, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (epi == EPI_F32 && scratch && a.ldc != a.N) scratch = nullptr;
-  if (dt == DT_BF16) {
-    if (a_kc && b_kc) return launch_sel<bf16, true, true>(epi, a, scratch, scratch_floats, s);
-    if (a_kc && !b_kc) return launch_sel<bf16, true, false>(epi, a, scratch, scratch_floats, s);
-    if (!a_kc && !b_kc) return launch_sel<bf16, false, false>(epi, a, scratch, scratch_floats, s);
-    return launch_sel<bf16, false, true>(epi, a, scratch, scratch_floats, s);
-  }
-  if (a_kc && b_kc) return launch_t<float, 128, 128, true, true>(epi, a, scratch, scratch_floats, s);
-  if (a_kc && !b_kc) return launch_t<float, 128, 128, true, false>(epi, a, scratch, scratch_floats, s);
-  if (!a_kc && !b_kc) return launch_t<float, 128, 128, false, false>(epi, a, scratch, scratch_floats, s);
-  return launch_t<float, 128, 128, false, true>(epi, a, scratch, scratch_floats, s);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -932,6 +842,140 @@ hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float*
   }
   colsum_finish<<<cdiv(N, 32), RP_THREADS, 0, s>>>(partial, M > 0 ? ny : 0, N, db, accumulate);
   return hipGetLastError();
+}
+
+
+constexpr int NCU = 256;
+
+// The 256x256 tile (8 waves) wins once the grid fills at least half of the CUs for the
+// K-contiguous products (direct copies); with a row-contiguous operand the 128x128 tile (several
+// blocks per CU) stays ahead until about 1.5 rounds of the CUs.
+static bool use_big(DType dt, bool kc_both, int M, int N) {
+  if (dt != DT_BF16) return false;
+  const long t = (long)cdiv(M, 256) * cdiv(N, 256);
+  return t >= (kc_both ? 128 : 384);
+}
+
+#ifndef GEMM_DW_BIG
+#define GEMM_DW_BIG 1
+#endif
+// Split-K factor for the fp32 weight-gradient products. The blocks run in ceil(tiles s / NCU)
+// rounds of K / s each, and every split adds an fp32 partial of M x N that is written and read
+// back once; pick the s that minimises that time (K per split >= 512, partials within scratch).
+int gemm_splits_t(int M, int N, int K, size_t scratch_floats, int tile) {
+  const long tiles = (long)cdiv(M, tile) * cdiv(N, tile);
+  // per-CU MFMA rate and HBM rate as seen by these kernels (order of magnitude is enough)
+  const double cu_flops = 1.8e12, hbm = 5.0e12;
+  const double tile_flops_per_k = 2.0 * tile * tile;
+  int best = 1;
+  double best_t = 1e30;
+  for (int s = 1; s <= 32; ++s) {
+    if (s > 1 && ((long)K / s < 512 || (size_t)s * M * N > scratch_floats)) break;
+    const double rounds = (double)((tiles * s + NCU - 1) / NCU);
+    const double t = rounds * tile_flops_per_k * ((double)K / s) / cu_flops + (s > 1 ? s * 8.0 * M * N / hbm : 0.0);
+    if (t < best_t * 0.995) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
+}
+int gemm_splits(int M, int N, int K, size_t scratch_floats) { return gemm_splits_t(M, N, K, scratch_floats, 128); }
+
+template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
+static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, hipStream_t s) {
+  using CF = Cfg<T, BM, BN, AKC, BKC>;
+  static bool attr = false;
+  auto kern = gemm_kernel<T, BM, BN, AKC, BKC, EPI>;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)CF::LDS_BYTES);
+    attr = true;
+  }
+  kern<<<grid, CF::NTHR, CF::LDS_BYTES, s>>>(a, k_split, split);
+}
+
+template <typename T, int BM, int BN, bool AKC, bool BKC>
+static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t scratch_floats, hipStream_t s) {
+  const int tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
+  int splits = 1;
+  if (epi == EPI_F32 && scratch) splits = gemm_splits_t(a.M, a.N, a.K, scratch_floats, BM);
+  int k_split = a.K;
+  if (splits > 1) {
+    constexpr int BK = Cfg<T, BM, BN, AKC, BKC>::BK;
+    k_split = cdiv(cdiv(a.K, splits), BK) * BK;
+    splits = cdiv(a.K, k_split);
+  }
+  dim3 grid(((long)tiles * splits + 7) & ~7L);
+  // column sums fused into the epilogue when a lane keeps one column chunk (and the partials fit);
+  // otherwise a separate pass over the stored C
+  using CF = Cfg<T, BM, BN, AKC, BKC>;
+  const int cs_rows = cdiv(a.M, BM) * CF::WGM;
+  const bool cs_fused = epi != EPI_F32 && a.colsum && 64 % (CF::TN / 8) == 0 && scratch &&
+                        (size_t)cs_rows * a.N <= scratch_floats;
+  float* csp = cs_fused ? scratch : nullptr;
+  switch (epi) {
+    case EPI_BIAS: launch_cfg<T, BM, BN, AKC, BKC, EPI_BIAS>(grid, a, k_split, csp, s); break;
+    case EPI_GELU: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU>(grid, a, k_split, csp, s); break;
+    case EPI_RESID: launch_cfg<T, BM, BN, AKC, BKC, EPI_RESID>(grid, a, k_split, csp, s); break;
+    case EPI_GELU_BWD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_BWD>(grid, a, k_split, csp, s); break;
+    case EPI_GELU_GRAD: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU_GRAD>(grid, a, k_split, csp, s); break;
+    case EPI_MUL: launch_cfg<T, BM, BN, AKC, BKC, EPI_MUL>(grid, a, k_split, csp, s); break;
+    case EPI_F32:
+      launch_cfg<T, BM, BN, AKC, BKC, EPI_F32>(grid, a, k_split, splits > 1 ? scratch : nullptr, s);
+      if (splits > 1) {
+        const size_t n = (size_t)a.M * a.N;
+        const int blocks = (int)std::min<size_t>(4096, (n / 4 + 255) / 256 + 1);
+        splitk_reduce<<<blocks, 256, 0, s>>>(scratch, splits, n, reinterpret_cast<float*>(a.C), a.accumulate);
+      }
+      break;
+  }
+  if (epi != EPI_F32 && a.colsum) {
+    if (cs_fused)
+      colsum_finish<<<cdiv(a.N, 32), RP_THREADS, 0, s>>>(scratch, cs_rows, a.N, a.colsum, a.colsum_accumulate);
+    else
+      return launch_colsum(sizeof(T) == 2 ? DT_BF16 : DT_F32, a.C, a.ldc, a.M, a.N, a.colsum, a.colsum_accumulate,
+                           scratch, scratch_floats, s);
+  }
+  return hipGetLastError();
+}
+
+// Fraction of the CU slots busy over the rounds a grid of this many single-block-per-CU tiles takes.
+static double round_fill(long tiles) { return (double)tiles / (double)(cdiv((int)tiles, NCU) * NCU); }
+
+template <typename T, bool AKC, bool BKC>
+static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
+  // split-K weight gradients (their M x N is small)
+  if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2) return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
+  if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N)) {
+    // K-contiguous products whose 256-wide column tiles leave CUs idle in the last round
+    // (N = 768: 192 tiles per 16384 rows) take 192-wide column tiles when those fill the rounds
+    // clearly better
+    if constexpr (AKC && BKC && sizeof(T) == 2) {
+      const long t256 = (long)cdiv(a.M, 256) * cdiv(a.N, 256), t192 = (long)cdiv(a.M, 256) * cdiv(a.N, 192);
+      if (round_fill(t192) > round_fill(t256) + 0.05) return launch_t<T, 256, 192, AKC, BKC>(epi, a, scratch, sf, s);
+    }
+    return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
+  }
+  if (epi == EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N))
+    return launch_t<T, 256, 256, AKC, BKC>(epi, a, nullptr, 0, s);
+  return launch_t<T, 128, 128, AKC, BKC>(epi, a, scratch, sf, s);
+}
+
+hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& a, float* scratch,
+                       size_t scratch_floats, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (epi == EPI_F32 && scratch && a.ldc != a.N) scratch = nullptr;
+  if (dt == DT_BF16) {
+    if (a_kc && b_kc) return launch_sel<bf16, true, true>(epi, a, scratch, scratch_floats, s);
+    if (a_kc && !b_kc) return launch_sel<bf16, true, false>(epi, a, scratch, scratch_floats, s);
+    if (!a_kc && !b_kc) return launch_sel<bf16, false, false>(epi, a, scratch, scratch_floats, s);
+    return launch_sel<bf16, false, true>(epi, a, scratch, scratch_floats, s);
+  }
+  if (a_kc && b_kc) return launch_t<float, 128, 128, true, true>(epi, a, scratch, scratch_floats, s);
+  if (a_kc && !b_kc) return launch_t<float, 128, 128, true, false>(epi, a, scratch, scratch_floats, s);
+  if (!a_kc && !b_kc) return launch_t<float, 128, 128, false, false>(epi, a, scratch, scratch_floats, s);
+  return launch_t<float, 128, 128, false, true>(epi, a, scratch, scratch_floats, s);
 }
 
 }  // namespace g2

@@ -34,9 +34,14 @@ struct GemmArgs {
   long ldaux;
   void* C2;          // second output (EPI_GELU), same ldc
   int accumulate;    // EPI_F32 only
+  // non-EPI_F32 epilogues: when set, colsum[n] (+)= sum over m of the stored C[m][n] (the bias
+  // gradient of a layer whose input gradient this product writes); partials go through scratch
+  float* colsum;
+  int colsum_accumulate;
 };
 
 // split-K: for EPI_F32 only; `scratch` must hold splits*M*N floats (nullptr => no split).
+// Column sums (GemmArgs::colsum): `scratch` must hold (M/128 rounded up) * 2 * N floats.
 hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& a, float* scratch,
                        size_t scratch_floats, hipStream_t s);
 // Choose the number of K splits for an EPI_F32 GEMM (1 = none).

@@ -271,7 +271,7 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
   size_t sf = std::max<size_t>(8 * 4 * C * C, (size_t)ldl * C * 3);  // split-K partials of the dW GEMMs
   sf = std::max(sf, layernorm_bwd_partial_floats((int)BT, (int)C));
   sf = std::max(sf, encoder_bwd_partial_floats((int)BT, (int)C));
-  sf = std::max<size_t>(sf, (size_t)256 * 4 * C);  // column-sum partials
+  sf = std::max<size_t>(sf, (size_t)512 * 4 * C);  // column-sum partials (separate or in a GEMM epilogue)
   M->scratch_floats = sf;
   M->scratch = (float*)take(sf * 4);
   M->norm_partial = (double*)take(NORM_PARTS * 8);
@@ -362,7 +362,7 @@ hipError_t refresh_transposed() {
 
 int gemm(bool akc, bool bkc, Epi epi, int M, int N, int K, const void* A, long lda, const void* Bp, long ldb,
          void* Cp, long ldc, const void* bias = nullptr, const void* aux = nullptr, long ldaux = 0,
-         void* C2 = nullptr, int accumulate = 0, bool split = false) {
+         void* C2 = nullptr, int accumulate = 0, bool split = false, float* colsum = nullptr, int colsum_acc = 0) {
   GemmArgs a{};
   a.M = M;
   a.N = N;
@@ -378,7 +378,10 @@ int gemm(bool akc, bool bkc, Epi epi, int M, int N, int K, const void* A, long l
   a.ldaux = ldaux;
   a.C2 = C2;
   a.accumulate = accumulate;
-  HIPCHK(launch_gemm(g.dt, akc, bkc, epi, a, split ? g.scratch : nullptr, split ? g.scratch_floats : 0, g.stream));
+  a.colsum = colsum;
+  a.colsum_accumulate = colsum_acc;
+  const bool scr = split || colsum;
+  HIPCHK(launch_gemm(g.dt, akc, bkc, epi, a, scr ? g.scratch : nullptr, scr ? g.scratch_floats : 0, g.stream));
   return GPT2_OK;
 }
 
@@ -498,12 +501,14 @@ int backward_impl() {
     // fcproj: res2 = res1 + gelu(z) Wfcproj^T + b ; dz = (dres Wfcproj) * gelu'(z)
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DX);
+      // dz = (dres Wfcproj) * gelu'(z); its column sums are the fc bias gradient
+      float* dfcb = lb ? G(o.fcb) : nullptr;
       if (g.shadow_t)
         RUN(gemm(true, true, EPI_MUL, BT, 4 * C, C, g.dres, C, WT(o.fcprojw), C, g.dbuf1, 4 * C, nullptr, a.fch,
-                 4 * C));
+                 4 * C, nullptr, 0, false, dfcb, acc));
       else
         RUN(gemm(true, false, EPI_MUL, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
-                 4 * C));
+                 4 * C, nullptr, 0, false, dfcb, acc));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DW);
@@ -521,10 +526,6 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_GEMM_FC_DW);
       RUN(gemm(false, false, EPI_F32, 4 * C, C, BT, g.dbuf1, 4 * C, a.ln2, C, G(o.fcw), C, nullptr, nullptr, 0,
              nullptr, acc, true));
-    }
-    {
-      ProfScope ps_(GPT2_K_BIAS_GRAD);
-      if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 4 * C, BT, 4 * C, G(o.fcb), acc, sc, sf, s));
     }
     {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
@@ -857,6 +858,34 @@ int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, in
   a.ldaux = ldaux;
   a.C2 = C2;
   a.accumulate = accumulate;
+  return op_ret(launch_gemm(to_dt(dtype), a_kcontig != 0, b_kcontig != 0, (Epi)epilogue, a, scratch, scratch_floats,
+                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_gemm_colsum(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
+                       int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias,
+                       const void* aux, int64_t ldaux, void* C2, float* colsum, int colsum_accumulate,
+                       float* scratch, uint64_t scratch_floats, void* stream) {
+  if (epilogue < 0 || epilogue > 6 || epilogue == EPI_F32 || M < 0 || N < 0 || K < 0 || !colsum)
+    return fail(GPT2_EINVAL, "bad gemm_colsum arguments");
+  if (!scratch || (uint64_t)cdiv(M, 128) * 2 * N > scratch_floats)
+    return fail(GPT2_EINVAL, "gemm_colsum needs scratch of ceil(M/128)*2*N floats");
+  GemmArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = A;
+  a.lda = lda;
+  a.B = B;
+  a.ldb = ldb;
+  a.C = C;
+  a.ldc = ldc;
+  a.bias = bias;
+  a.aux = aux;
+  a.ldaux = ldaux;
+  a.C2 = C2;
+  a.colsum = colsum;
+  a.colsum_accumulate = colsum_accumulate;
   return op_ret(launch_gemm(to_dt(dtype), a_kcontig != 0, b_kcontig != 0, (Epi)epilogue, a, scratch, scratch_floats,
                             reinterpret_cast<hipStream_t>(stream)));
 }

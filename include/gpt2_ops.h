@@ -37,6 +37,16 @@ extern "C" {
 int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias, const void* aux,
                 int64_t ldaux, void* C2, int accumulate, float* scratch, uint64_t scratch_floats, void* stream);
+/* gpt2op_gemm with an epilogue other than GPT2_EPI_F32 that also sums the stored C over its rows:
+ * colsum[n] = (or += when colsum_accumulate) sum_m C[m][n], the values as stored in dtype: the
+ * bias gradient of the linear layer whose output gradient this product writes (the hand-ordered
+ * backward of "Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 代码解剖).
+ * Deterministic: fixed-order partial sums through scratch, which must hold ceil(M/128) * 2 * N
+ * floats (else GPT2_EINVAL). colsum (float [N]) is caller-owned device memory. */
+int gpt2op_gemm_colsum(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
+                       int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias,
+                       const void* aux, int64_t ldaux, void* C2, float* colsum, int colsum_accumulate,
+                       float* scratch, uint64_t scratch_floats, void* stream);
 
 /* LayerNorm over rows of width C (eps 1e-5, biased variance): y, mean[rows], rstd[rows]. b may be NULL. */
 int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,

@@ -111,6 +111,45 @@ def test_gemm_bf16_256x192_tile_path(epi, K):
     check_big_gemm((1, 1), epi, K, 4100, 2300)
 
 
+@pytest.mark.parametrize("dt,M,N,K,epi", [
+    (bd.GPT2_BF16, 200, 136, 72, bd.EPI_MUL),         # 128 x 128 tiles, ragged M, N and K
+    (bd.GPT2_FP32, 200, 136, 72, bd.EPI_BIAS),
+    (bd.GPT2_BF16, 4100, 6392, 192, bd.EPI_MUL),      # 256 x 256 tiles (column sums in the epilogue)
+    (bd.GPT2_BF16, 4100, 2296, 192, bd.EPI_BIAS),     # 256 x 192 tiles (separate column-sum pass)
+])
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_gemm_colsum(dt, M, N, K, epi, accumulate):
+    """colsum[n] (+)= sum over rows of the stored C, whichever tile the shape takes; the product
+    itself matches the plain gpt2op_gemm bit for bit."""
+    rng = np.random.default_rng(M + N + K + epi)
+    A, W, b, aux = rng.normal(0, 1, (M, K)), rng.normal(0, 0.2, (N, K)), rng.normal(0, 0.5, N), rng.normal(0, 1, (M, N))
+    Ad, Wd, bd_, auxd = dev(A, dt), dev(W, dt), dev(b, dt), dev(aux, dt)
+    C = torch.zeros((M, N), dtype=TD[dt], device="cuda")
+    Cref = torch.zeros((M, N), dtype=TD[dt], device="cuda")
+    cs0 = rng.normal(0, 1, N)
+    cs = torch.tensor(cs0, dtype=torch.float32, device="cuda")
+    scr = torch.zeros(-(-M // 128) * 2 * N, dtype=torch.float32, device="cuda")
+    lib = bd.load()
+    rc = lib.gpt2op_gemm_colsum(dt, 1, 1, epi, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, C.data_ptr(), N,
+                                bd_.data_ptr(), auxd.data_ptr(), N, None, cs.data_ptr(), accumulate, scr.data_ptr(),
+                                scr.numel(), stream())
+    assert rc == 0, bd.last_error()
+    rc = lib.gpt2op_gemm(dt, 1, 1, epi, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, Cref.data_ptr(), N,
+                         bd_.data_ptr(), auxd.data_ptr(), N, None, 0, None, 0, stream())
+    assert rc == 0, bd.last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(C, Cref)
+    c64 = h64(C)
+    want = c64.sum(0) + (cs0.astype(np.float32) if accumulate else 0.0)
+    bound = 2e-5 * (np.abs(c64).sum(0) + (np.abs(cs0) if accumulate else 0.0)) + 1e-30
+    assert np.all(np.abs(cs.cpu().numpy().astype(np.float64) - want) <= bound)
+    # too small a scratch is refused
+    rc = lib.gpt2op_gemm_colsum(dt, 1, 1, epi, M, N, K, Ad.data_ptr(), K, Wd.data_ptr(), K, C.data_ptr(), N,
+                                bd_.data_ptr(), auxd.data_ptr(), N, None, cs.data_ptr(), accumulate, scr.data_ptr(),
+                                scr.numel() - 1, stream())
+    assert rc == bd.GPT2_EINVAL
+
+
 def check_big_gemm(layout, epi, K, M, N):
     akc, bkc = layout
     rng = np.random.default_rng(epi * 10 + akc * 2 + bkc)
