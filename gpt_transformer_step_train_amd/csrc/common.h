@@ -162,22 +162,30 @@ constexpr float GELU_K = 0.7978845608028654f;  // sqrt(2/pi)
 constexpr float GELU_C = 0.044715f;
 
 // GELU, tanh form, written as x * sigmoid(2u) with u = sqrt(2/pi)(x + 0.044715 x^3);
-// 0.5(1 + tanh u) equals sigmoid(2u) exactly.
-__device__ __forceinline__ float gelu_sig(float x) {
-  const float u = GELU_K * (x + GELU_C * x * x * x);
-  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-2.0f * LOG2E * u));
+// 0.5(1 + tanh u) equals sigmoid(2u) exactly. The constants are folded so that the exponent is
+// x (a + b x^2) in base 2 (two VALU ops) and the derivative
+//   s + 2 x s (1 - s) sqrt(2/pi) (1 + 3 * 0.044715 x^2) = s + g (1 - s) (p + q x^2), g = x s,
+// costs three more fused multiply-adds: these run in GEMM epilogues, where VALU time counts.
+constexpr float GELU_EA = -2.0f * LOG2E * GELU_K;           // exponent: x (EA + EB x^2)
+constexpr float GELU_EB = -2.0f * LOG2E * GELU_K * GELU_C;
+constexpr float GELU_DP = 2.0f * GELU_K;                    // derivative polynomial p + q x^2
+constexpr float GELU_DQ = 6.0f * GELU_K * GELU_C;
+__device__ __forceinline__ float gelu_sig2(float x, float x2) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * fmaf(x2, GELU_EB, GELU_EA)));
 }
-__device__ __forceinline__ float gelu_fwd(float x) { return x * gelu_sig(x); }
-// d/dx: s + x * 2 s (1 - s) * sqrt(2/pi) (1 + 3 * 0.044715 x^2), with s = 0.5 (1 + tanh u).
+__device__ __forceinline__ float gelu_fwd(float x) { return x * gelu_sig2(x, x * x); }
 __device__ __forceinline__ float gelu_bwd(float x) {
-  const float s = gelu_sig(x);
-  return s + 2.0f * x * s * (1.0f - s) * GELU_K * (1.0f + 3.0f * GELU_C * x * x);
+  const float x2 = x * x;
+  const float s = gelu_sig2(x, x2);
+  const float g = x * s;
+  return fmaf(fmaf(-g, s, g), fmaf(x2, GELU_DQ, GELU_DP), s);
 }
 // gelu(x) and gelu'(x) sharing one sigmoid
 __device__ __forceinline__ void gelu_both(float x, float& g, float& dg) {
-  const float s = gelu_sig(x);
+  const float x2 = x * x;
+  const float s = gelu_sig2(x, x2);
   g = x * s;
-  dg = s + 2.0f * x * s * (1.0f - s) * GELU_K * (1.0f + 3.0f * GELU_C * x * x);
+  dg = fmaf(fmaf(-g, s, g), fmaf(x2, GELU_DQ, GELU_DP), s);
 }
 
 __host__ __device__ constexpr int cdiv(long a, long b) { return (int)((a + b - 1) / b); }

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
   }
 }
 
-constexpr int LNB_BLOCKS = 1024;
+constexpr int LNB_BLOCKS = 512;
 
 // Raw (packed) inputs of one row of the backward, held in registers so that the loads of the next
 // row are in flight while this one is processed.
