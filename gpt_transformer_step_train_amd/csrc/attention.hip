@@ -339,7 +339,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
   }
   const float c2 = LOG2E / sqrtf((float)HD);  // scale folded into base-2 exponent
   f32x16 o[2] = {zero16(), zero16()};         // O^T: rows d (2 x 32), columns = queries
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  // The softmax denominators come out of the matrix cores: an A operand whose row 0 is all ones
+  // (lanes 0 and 32 supply row 0) times P^T adds the row sums of P, in row 0 of lsum (register 0
+  // of lanes 0..31). They sum the bf16 probabilities that also enter P V.
+  f32x16 lsum = zero16();
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, l32 == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                                                          : u32x4{0u, 0u, 0u, 0u});
 
   const int kend = min(T, q0 + BQ);
   const int ntiles = cdiv(kend, KT);
@@ -381,19 +387,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
       for (int i = 1; i < 32; ++i) mloc = fmaxf(mloc, sc[i]);
       mloc = pair_max(mloc);
       const float m_new = fmaxf(m_run, mloc * c2);  // scaled, log2 units
-      const float corr = fast_exp2(m_run - m_new);
-      float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        sc[i] = fast_exp2(fmaf(sc[i], c2, -m_new));
-        psum += sc[i];
+      for (int i = 0; i < 32; ++i) sc[i] = fast_exp2(fmaf(sc[i], c2, -m_new));
+      // rescale only when some query of the wave has a new running max (corr is exactly 1 for
+      // the others, and for all of them once the maxima settle)
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+        const float corr = fast_exp2(m_run - m_new);
+        lsum[0] *= corr;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= corr;
       }
-      l_run = l_run * corr + psum;
       m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= corr;
       // O^T += V^T P^T : A = V^T (rows d, k = keys), B = P^T (k = keys, columns = queries)
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -403,11 +409,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
 #pragma unroll
           for (int db = 0; db < 2; ++db)
             o[db] = mfma(tr_frag(Vs, sb * 32 + 16 * ks, db * 32, lane), pf, o[db]);
+          lsum = mfma(ones, pf, lsum);
         }
     }
     __syncthreads();
   }
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = pair_sum(g == 0 ? lsum[0] : 0.f);
   if (myq < T) {
     const float inv = 1.f / l_tot;
     uint16_t* dst = out + ((size_t)b * T + myq) * C + h * HD;
