@@ -25,6 +25,7 @@ EXPORTS = [
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
+    "gpt2op_attention_backward_colsum",
 ]
 
 
@@ -77,6 +78,8 @@ def load(path=LIB_PATH):
         "gpt2op_layernorm_backward_scratch": (_u64, [ctypes.c_int, ctypes.c_int]),
         "gpt2op_attention_forward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 4),
         "gpt2op_attention_backward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7),
+        "gpt2op_attention_backward_colsum": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7 + [ctypes.c_int, _vp, _u64,
+                                                                                          _vp]),
         "gpt2op_cross_entropy": (ctypes.c_int, [ctypes.c_int] * 4 + [_vp] * 5),
         "gpt2op_encoder_forward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 6),
         "gpt2op_encoder_backward": (ctypes.c_int, [ctypes.c_int] * 6 + [_vp] * 4 + [ctypes.c_int, _vp, _vp, _vp]),

@@ -431,13 +431,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
   }
 }
 
+// Bias-gradient partials of one block's 128 rows of dqkv: lane sums a[db] (and b[db]) cover
+// column db * 32 + (lane & 31) of the head over the lane's 16 rows; lanes l and l ^ 32 hold the
+// other 16 rows of the wave, the 4 waves the other 96. Written in a fixed order to
+// cs[row][col0 + c] (a) and cs[row][col0 + C + c] (b), c < 64, with C = C3 / 3. red: 2 KB of the
+// block's LDS, free once every wave has passed the last barrier of the main loop.
+__device__ __forceinline__ void bias_partial(float* __restrict__ cs, int row, long C3, int col0, float (&a)[2],
+                                             const float* b, float* red, int w, int lane) {
+  const int nq = b ? 2 : 1;
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const float ta = a[db] + __shfl_xor(a[db], 32);
+    if (lane < 32) red[w * 128 + db * 32 + lane] = ta;
+    if (b) {
+      const float tb = b[db] + __shfl_xor(b[db], 32);
+      if (lane < 32) red[w * 128 + 64 + db * 32 + lane] = tb;
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 64 * nq) {
+    const float v = (red[t] + red[128 + t]) + (red[256 + t] + red[384 + t]);
+    cs[(size_t)row * C3 + col0 + (t >> 6) * (C3 / 3) + (t & 63)] = v;
+  }
+}
+
 // ---------------------------------------------------------------- backward: dK, dV
 // grid (T/128, B*H): block owns 128 keys (wave w: 32 keys), loops over 64-query tiles.
 __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const uint16_t* __restrict__ qkv,
                                                            const uint16_t* __restrict__ dout,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ dvec,
-                                                           uint16_t* __restrict__ dqkv) {
+                                                           uint16_t* __restrict__ dqkv,
+                                                           float* __restrict__ cs) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[KT * LDP];   // [q][d]
   __shared__ __attribute__((aligned(16))) uint16_t dOs[KT * LDP];  // [q][d]
   __shared__ __attribute__((aligned(16))) float Ls[KT];
@@ -549,6 +575,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   }
   // store: accumulator rows = keys, columns = d
   const float sc = 1.0f / sqrtf((float)HD);
+  float sk[2] = {0.f, 0.f}, sv[2] = {0.f, 0.f};  // column sums over this lane's keys (as stored)
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = db * 32 + l32;
@@ -557,11 +584,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
       const int key = kw0 + acc_row(i, g);
       if (key < T) {
         uint16_t* dst = dqkv + ((size_t)b * T + key) * C3 + h * HD + d;
-        dst[C] = f2bf(dk[db][i] * sc);
-        dst[2 * C] = f2bf(dv[db][i]);
+        const uint16_t k16 = f2bf(dk[db][i] * sc), v16 = f2bf(dv[db][i]);
+        dst[C] = k16;
+        dst[2 * C] = v16;
+        sk[db] += bf2f(k16);
+        sv[db] += bf2f(v16);
       }
     }
   }
+  if (cs) bias_partial(cs, b * gridDim.x + kt_blk, C3, C + h * HD, sk, sv, reinterpret_cast<float*>(Qs), w, lane);
 }
 
 // ---------------------------------------------------------------- backward: dQ
@@ -570,7 +601,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
                                                           const uint16_t* __restrict__ dout,
                                                           const float* __restrict__ lse,
                                                           const float* __restrict__ dvec,
-                                                          uint16_t* __restrict__ dqkv) {
+                                                          uint16_t* __restrict__ dqkv,
+                                                          float* __restrict__ cs) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
   __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
   int bh, rank;
@@ -649,15 +681,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
     __syncthreads();
   }
   const float sc = 1.0f / sqrtf((float)HD);
+  float sq[2] = {0.f, 0.f};  // column sums over this lane's queries (as stored)
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = db * 32 + l32;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int q = qw0 + acc_row(i, g);
-      if (q < T) dqkv[((size_t)b * T + q) * C3 + h * HD + d] = f2bf(dq[db][i] * sc);
+      if (q < T) {
+        const uint16_t q16 = f2bf(dq[db][i] * sc);
+        dqkv[((size_t)b * T + q) * C3 + h * HD + d] = q16;
+        sq[db] += bf2f(q16);
+      }
     }
   }
+  if (cs) bias_partial(cs, b * gridDim.x + qt, C3, h * HD, sq, nullptr, reinterpret_cast<float*>(Ks), w, lane);
 }
 
 // =====================================================================================
@@ -684,9 +722,11 @@ hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const voi
   return hipGetLastError();
 }
 
+int attention_bias_partial_rows(int B, int T) { return B * cdiv(T, BQ); }
+
 hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
                                 const void* dout, const float* lse, void* dqkv, float* dvec, int parts,
-                                hipStream_t s) {
+                                hipStream_t s, float* cs) {
   if (B * T <= 0) return hipSuccess;
   const int BT = B * T;
   if (dt == DT_BF16) {
@@ -698,8 +738,8 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
     auto Q = reinterpret_cast<const uint16_t*>(qkv);
     auto dO = reinterpret_cast<const uint16_t*>(dout);
     auto dQ = reinterpret_cast<uint16_t*>(dqkv);
-    if (parts & ATT_BWD_KV) attn_bwd_kv_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
-    if (parts & ATT_BWD_Q) attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ);
+    if (parts & ATT_BWD_KV) attn_bwd_kv_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ, cs);
+    if (parts & ATT_BWD_Q) attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ, cs);
     return hipGetLastError();
   }
   if (parts & ATT_BWD_PRE) {

@@ -826,6 +826,12 @@ __global__ __launch_bounds__(RP_THREADS) void colsum_finish(const float* __restr
   reduce_partials_block(partial, ny, N, N, out, accumulate);
 }
 
+hipError_t launch_colsum_finish(const float* partial, int ny, int N, float* out, int accumulate, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  colsum_finish<<<cdiv(N, 32), RP_THREADS, 0, s>>>(partial, ny, N, out, accumulate);
+  return hipGetLastError();
+}
+
 hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float* db, int accumulate,
                          float* partial, size_t partial_floats, hipStream_t s) {
   if (N <= 0) return hipSuccess;

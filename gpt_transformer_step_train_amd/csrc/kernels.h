@@ -47,6 +47,8 @@ hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& 
 // Choose the number of K splits for an EPI_F32 GEMM (1 = none).
 int gemm_splits(int M, int N, int K, size_t scratch_floats);
 
+// out[n] (+)= sum_{y < ny} partial[y * N + n], summed in a fixed order
+hipError_t launch_colsum_finish(const float* partial, int ny, int N, float* out, int accumulate, hipStream_t s);
 // db[n] (+)= sum_m dY[m*ld + n]; deterministic, two stages through `partial` (rows_split*N floats)
 hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float* db, int accumulate,
                          float* partial, size_t partial_floats, hipStream_t s);
@@ -77,9 +79,14 @@ hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const voi
 // dqkv [B,T,3C] is fully written. `dvec` holds B*H*T floats of scratch.
 // parts: any of ATT_BWD_PRE (D = rowsum(dO * O)), ATT_BWD_KV (dK, dV), ATT_BWD_Q (dQ), in that order
 constexpr int ATT_BWD_PRE = 1, ATT_BWD_KV = 2, ATT_BWD_Q = 4, ATT_BWD_ALL = 7;
+// cs (bf16 only, may be null): the KV and Q kernels also write the column sums of the dqkv rows
+// they store, one partial row of 3C floats per (sequence, 128-row tile):
+// attention_bias_partial_rows(B, T) rows in all; launch_colsum_finish turns them into the qkv
+// bias gradient.
 hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
                                 const void* dout, const float* lse, void* dqkv, float* dvec, int parts,
-                                hipStream_t s);
+                                hipStream_t s, float* cs = nullptr);
+int attention_bias_partial_rows(int B, int T);
 
 // Softmax cross-entropy over the first V columns of each row (row stride ld).
 // targets < 0 are ignored. When dloss != nullptr the logits are overwritten by

@@ -549,15 +549,22 @@ int backward_impl() {
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
                                   ATT_BWD_PRE, s));
     }
+    // bf16: the attention kernels also leave the column partials of dqkv (the qkv bias gradient)
+    float* csa = (lb && g.dt == DT_BF16) ? sc : nullptr;
     {
       ProfScope ps_(GPT2_K_ATTENTION_BWD);
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
-                                  ATT_BWD_KV, s));
+                                  ATT_BWD_KV, s, csa));
     }
     {
       ProfScope ps_(GPT2_K_ATTENTION_BWD_Q);
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
-                                  ATT_BWD_Q, s));
+                                  ATT_BWD_Q, s, csa));
+    }
+    {
+      ProfScope ps_(GPT2_K_BIAS_GRAD);
+      if (csa) HIPCHK(launch_colsum_finish(csa, attention_bias_partial_rows(g.B, g.T), 3 * C, G(o.qkvb), acc, s));
+      else if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
     }
     // qkv = ln1 Wqkv^T + b
     {
@@ -569,10 +576,6 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_GEMM_QKV_DW);
       RUN(gemm(false, false, EPI_F32, 3 * C, C, BT, g.dbuf1, 3 * C, a.ln1, C, G(o.qkvw), C, nullptr, nullptr, 0,
              nullptr, acc, true));
-    }
-    {
-      ProfScope ps_(GPT2_K_BIAS_GRAD);
-      if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
     }
     {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
@@ -914,6 +917,26 @@ int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void
                               const void* dout, const float* lse, void* dqkv, float* dvec, void* stream) {
   return op_ret(launch_attention_bwd(to_dt(dtype), B, T, H, hs, qkv, out, dout, lse, dqkv, dvec, ATT_BWD_ALL,
                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_attention_backward_colsum(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
+                                     const void* dout, const float* lse, void* dqkv, float* dvec, float* dbias,
+                                     int accumulate, float* scratch, uint64_t scratch_floats, void* stream) {
+  if (B < 0 || T < 0 || H < 1 || hs < 1 || !dbias) return fail(GPT2_EINVAL, "bad attention_backward_colsum arguments");
+  const long C3 = 3L * H * hs;
+  if (!scratch || (uint64_t)cdiv((long)B * T, 128) * C3 > scratch_floats ||
+      (uint64_t)attention_bias_partial_rows(B, T) * C3 > scratch_floats)
+    return fail(GPT2_EINVAL, "attention_backward_colsum needs scratch of B*ceil(T/128)*3*H*hs floats");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const DType dt = to_dt(dtype);
+  if (dt == DT_BF16) {
+    int rc = op_ret(launch_attention_bwd(dt, B, T, H, hs, qkv, out, dout, lse, dqkv, dvec, ATT_BWD_ALL, s, scratch));
+    if (rc != GPT2_OK || B * T == 0) return rc;
+    return op_ret(launch_colsum_finish(scratch, attention_bias_partial_rows(B, T), (int)C3, dbias, accumulate, s));
+  }
+  int rc = op_ret(launch_attention_bwd(dt, B, T, H, hs, qkv, out, dout, lse, dqkv, dvec, ATT_BWD_ALL, s));
+  if (rc != GPT2_OK) return rc;
+  return op_ret(launch_colsum(dt, dqkv, C3, B * T, (int)C3, dbias, accumulate, scratch, scratch_floats, s));
 }
 
 int gpt2op_cross_entropy(int dtype, int rows, int V, int ld, void* logits, const int32_t* targets, const float* dloss,

@@ -68,6 +68,14 @@ int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void*
 /* dqkv [B,T,3C] (fully written) from qkv, out, dout, lse; dvec: float scratch [B*H*T]. */
 int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
                               const void* dout, const float* lse, void* dqkv, float* dvec, void* stream);
+/* gpt2op_attention_backward that also sums dqkv over its B*T rows: dbias[3C] = (or += when
+ * accumulate) sum over rows of dqkv as stored, the gradient of the qkv bias (the hand-ordered
+ * backward of "Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 代码解剖).
+ * bf16: the backward kernels leave per-tile column partials; fp32: a separate column-sum pass.
+ * Deterministic. scratch (float) must hold B * ceil(T/128) * 3C floats (else GPT2_EINVAL). */
+int gpt2op_attention_backward_colsum(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
+                                     const void* dout, const float* lse, void* dqkv, float* dvec, float* dbias,
+                                     int accumulate, float* scratch, uint64_t scratch_floats, void* stream);
 
 /* Softmax cross-entropy over the first V of ld columns of each row. losses[rows] (float).
  * When dloss != NULL (device float scalar), logits are overwritten by (softmax - onehot)*dloss,

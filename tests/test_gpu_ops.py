@@ -347,6 +347,44 @@ def test_attention_forward_backward(dt, B, T, H, hs):
         assert rel(h64(dq)[b], dq_ref) <= tol(dt, 5e-5, 2e-2)
 
 
+@pytest.mark.parametrize("dt,B,T,H,hs", [(bd.GPT2_BF16, 2, 200, 3, 64), (bd.GPT2_BF16, 1, 384, 2, 64),
+                                         (bd.GPT2_FP32, 2, 70, 2, 16)])
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_attention_backward_colsum(dt, B, T, H, hs, accumulate):
+    """The qkv bias gradient that comes with the attention backward equals the column sums of the
+    dqkv it stores (ragged last tile at T = 200 and 70), and dqkv is the plain backward's."""
+    C = H * hs
+    rng = np.random.default_rng(T + H + accumulate)
+    qd, dod = dev(rng.normal(0, 1, (B, T, 3 * C)), dt), dev(rng.normal(0, 1, (B, T, C)), dt)
+    out = torch.empty((B, T, C), dtype=TD[dt], device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    lib = bd.load()
+    assert lib.gpt2op_attention_forward(dt, B, T, H, hs, qd.data_ptr(), out.data_ptr(), lse.data_ptr(), stream()) == 0
+    dq = torch.empty((B, T, 3 * C), dtype=TD[dt], device="cuda")
+    dq2 = torch.empty((B, T, 3 * C), dtype=TD[dt], device="cuda")
+    dvec = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    b0 = rng.normal(0, 1, 3 * C)
+    dbias = torch.tensor(b0, dtype=torch.float32, device="cuda")
+    nsc = B * -(-T // 128) * 3 * C
+    scr = torch.zeros(nsc, dtype=torch.float32, device="cuda")
+    rc = lib.gpt2op_attention_backward_colsum(dt, B, T, H, hs, qd.data_ptr(), out.data_ptr(), dod.data_ptr(),
+                                              lse.data_ptr(), dq.data_ptr(), dvec.data_ptr(), dbias.data_ptr(),
+                                              accumulate, scr.data_ptr(), nsc, stream())
+    assert rc == 0, bd.last_error()
+    assert lib.gpt2op_attention_backward(dt, B, T, H, hs, qd.data_ptr(), out.data_ptr(), dod.data_ptr(),
+                                         lse.data_ptr(), dq2.data_ptr(), dvec.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2)
+    d64 = h64(dq).reshape(B * T, 3 * C)
+    want = d64.sum(0) + (b0.astype(np.float32) if accumulate else 0.0)
+    bound = 2e-5 * (np.abs(d64).sum(0) + (np.abs(b0) if accumulate else 0.0)) + 1e-30
+    assert np.all(np.abs(dbias.cpu().numpy().astype(np.float64) - want) <= bound)
+    rc = lib.gpt2op_attention_backward_colsum(dt, B, T, H, hs, qd.data_ptr(), out.data_ptr(), dod.data_ptr(),
+                                              lse.data_ptr(), dq.data_ptr(), dvec.data_ptr(), dbias.data_ptr(),
+                                              accumulate, scr.data_ptr(), nsc - 1, stream())
+    assert rc == bd.GPT2_EINVAL
+
+
 def test_attention_rejects_unsupported_head_size():
     lib = bd.load()
     x = torch.zeros(8, device="cuda")
