@@ -47,7 +47,7 @@ def class_work(name, w):
             "gemm_fcproj": (BT, C, 4 * C), "gemm_classifier": (BT, Vp, C), "gemm_classifier_dx": (BT, C, Vp),
             "gemm_classifier_dw": (Vp, C, BT), "gemm_fcproj_dx": (BT, 4 * C, C), "gemm_fcproj_dw": (C, 4 * C, BT),
             "gemm_fc_dx": (BT, C, 4 * C), "gemm_fc_dw": (4 * C, C, BT), "gemm_attproj_dx": (BT, C, C),
-            "gemm_attproj_dw": (C, C, BT), "gemm_qkv_dx": (BT, C, 3 * C), "gemm_qkv_dw": (3 * C, C, BT)}
+            "gemm_attproj_dw": (C, C, BT), "gemm_qkv_dx": (BT, C, 3 * C), "gemm_qkv_dw": (4 * C, C, BT)}  # qkv_dw: qkv and attproj dW
     if name in gemm:
         M, N, K = gemm[name]
         return "mfma", 2.0 * M * N * K

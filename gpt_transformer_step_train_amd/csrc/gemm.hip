@@ -511,17 +511,19 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
         for (int j = 0; j < FN; ++j) acc[i][j] = MM::mma(fa[cb][i], fb[cb][j], acc[i][j]);
     }
     {
-      // issue order: the reads of step 0, then for each step one read of the next step after
-      // every FM*FN/(FM+FN) MFMAs, so no MFMA waits for a read issued in its own step
+      // issue order: the reads of step 0, then within each step one read of the next step after
+      // each MFMA (the rest at the end), so no MFMA waits for a read issued in its own step
       constexpr int NR = FM * (OA::MODE == 2 ? 2 : 1) + FN * (OB::MODE == 2 ? 2 : 1);
       __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
       for (int st = 0; st + 1 < KS; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NR / 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NR - NR / 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 2, 0);
+#pragma unroll
+        for (int r = 0; r < NR && r < FM * FN; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NR > FM * FN) __builtin_amdgcn_sched_group_barrier(0x100, NR - FM * FN, 0);
+        if (FM * FN > NR) __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - NR, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
     }
@@ -595,22 +597,27 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
 }
 
 template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(GemmArgs p, int k_split,
-                                                                               float* split_out) {
+__global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(GemmArgs p0, int k_split,
+                                                                               float* split_out0, GemmArgs p1,
+                                                                               float* split_out1, int nblk0) {
   using CF = Cfg<T, BM, BN, AKC, BKC>;
   constexpr int BK = CF::BK, TM = CF::TM, TN = CF::TN, FM = CF::FM, FN = CF::FN;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* const st0 = reinterpret_cast<T*>(smem);
 
-  // Block -> (split, tile). The 1-D grid holds splits x tiles blocks padded to a multiple of 8;
-  // blocks are dealt round-robin to the 8 XCDs, so block L is renumbered to give each XCD a
-  // contiguous run of (split, tile) pairs (tiles of one split that share operand rows or columns
-  // then share an L2); padding blocks exit. Inside a split, tiles go in groups of GROUP_M
-  // tile-rows.
+  // Block -> (problem, split, tile). The 1-D grid holds splits x tiles blocks of problem 0, then
+  // (grouped weight gradients) those of problem 1, padded to a multiple of 8; blocks are dealt
+  // round-robin to the 8 XCDs, so block L is renumbered to give each XCD a contiguous run of
+  // (split, tile) pairs (tiles of one split that share operand rows or columns then share an L2);
+  // padding blocks exit. Inside a split, tiles go in groups of GROUP_M tile-rows.
+  int bb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const bool second = bb >= nblk0;
+  const GemmArgs p = second ? p1 : p0;
+  float* const split_out = second ? split_out1 : split_out0;
+  if (second) bb -= nblk0;
   const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
   const int ntiles = tiles_m * tiles_n;
   const int nsplit = cdiv(p.K, k_split);
-  const int bb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   if (bb >= ntiles * nsplit) return;
   const int zs = bb / ntiles, b = bb % ntiles;
   const int group = GROUP_M * tiles_n;
@@ -765,20 +772,31 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
 }
 
 // dst[i] (+)= sum_z part[z][i], z in order
-__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, int splits, size_t n,
-                                                     float* __restrict__ dst, int accumulate) {
+__device__ __forceinline__ void splitk_reduce_seg(const float* __restrict__ part, int splits, size_t n,
+                                                  float* __restrict__ dst, int accumulate, size_t first,
+                                                  size_t stride) {
   const size_t n4 = n / 4;
-  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+  for (size_t i = first; i < n4; i += stride) {
     f32x4 s = accumulate ? reinterpret_cast<const f32x4*>(dst)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int z = 0; z < splits; ++z) s += reinterpret_cast<const f32x4*>(part + (size_t)z * n)[i];
     reinterpret_cast<f32x4*>(dst)[i] = s;
   }
-  for (size_t i = n4 * 4 + blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  for (size_t i = n4 * 4 + first; i < n; i += stride) {
     float s = accumulate ? dst[i] : 0.f;
     for (int z = 0; z < splits; ++z) s += part[(size_t)z * n + i];
     dst[i] = s;
   }
 }
+// one or two products' partials (n1 = 0: one)
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part0, size_t n0,
+                                                     float* __restrict__ dst0, const float* __restrict__ part1,
+                                                     size_t n1, float* __restrict__ dst1, int splits,
+                                                     int accumulate0, int accumulate1) {
+  const size_t first = blockIdx.x * 256ull + threadIdx.x, stride = (size_t)gridDim.x * 256;
+  splitk_reduce_seg(part0, splits, n0, dst0, accumulate0, first, stride);
+  if (n1) splitk_reduce_seg(part1, splits, n1, dst1, accumulate1, first, stride);
+}
+static int splitk_reduce_blocks(size_t n) { return (int)std::min<size_t>(4096, (n / 4 + 255) / 256 + 1); }
 
 // ----------------------------------------------------------------------------------------
 // Column sums (bias gradients): partial[y][n] over a chunk of rows, 16-byte loads, then a
@@ -868,23 +886,25 @@ static bool use_big(DType dt, bool kc_both, int M, int N) {
 // Split-K factor for the fp32 weight-gradient products. The blocks run in ceil(tiles s / NCU)
 // rounds of K / s each, and every split adds an fp32 partial of M x N that is written and read
 // back once; pick the s that minimises that time (K per split >= 512, partials within scratch).
-int gemm_splits_t(int M, int N, int K, size_t scratch_floats, int tile) {
-  const long tiles = (long)cdiv(M, tile) * cdiv(N, tile);
+static int splits_for(long tiles, long mn, int K, size_t scratch_floats, int tile) {
   // per-CU MFMA rate and HBM rate as seen by these kernels (order of magnitude is enough)
   const double cu_flops = 1.8e12, hbm = 5.0e12;
   const double tile_flops_per_k = 2.0 * tile * tile;
   int best = 1;
   double best_t = 1e30;
   for (int s = 1; s <= 32; ++s) {
-    if (s > 1 && ((long)K / s < 512 || (size_t)s * M * N > scratch_floats)) break;
+    if (s > 1 && ((long)K / s < 512 || (size_t)s * mn > scratch_floats)) break;
     const double rounds = (double)((tiles * s + NCU - 1) / NCU);
-    const double t = rounds * tile_flops_per_k * ((double)K / s) / cu_flops + (s > 1 ? s * 8.0 * M * N / hbm : 0.0);
+    const double t = rounds * tile_flops_per_k * ((double)K / s) / cu_flops + (s > 1 ? s * 8.0 * mn / hbm : 0.0);
     if (t < best_t * 0.995) {
       best_t = t;
       best = s;
     }
   }
   return best;
+}
+int gemm_splits_t(int M, int N, int K, size_t scratch_floats, int tile) {
+  return splits_for((long)cdiv(M, tile) * cdiv(N, tile), (long)M * N, K, scratch_floats, tile);
 }
 int gemm_splits(int M, int N, int K, size_t scratch_floats) { return gemm_splits_t(M, N, K, scratch_floats, 128); }
 
@@ -898,7 +918,7 @@ static void launch_cfg(dim3 grid, const GemmArgs& a, int k_split, float* split, 
                               (int)CF::LDS_BYTES);
     attr = true;
   }
-  kern<<<grid, CF::NTHR, CF::LDS_BYTES, s>>>(a, k_split, split);
+  kern<<<grid, CF::NTHR, CF::LDS_BYTES, s>>>(a, k_split, split, a, nullptr, INT_MAX);
 }
 
 template <typename T, int BM, int BN, bool AKC, bool BKC>
@@ -931,8 +951,8 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
       launch_cfg<T, BM, BN, AKC, BKC, EPI_F32>(grid, a, k_split, splits > 1 ? scratch : nullptr, s);
       if (splits > 1) {
         const size_t n = (size_t)a.M * a.N;
-        const int blocks = (int)std::min<size_t>(4096, (n / 4 + 255) / 256 + 1);
-        splitk_reduce<<<blocks, 256, 0, s>>>(scratch, splits, n, reinterpret_cast<float*>(a.C), a.accumulate);
+        splitk_reduce<<<splitk_reduce_blocks(n), 256, 0, s>>>(scratch, n, reinterpret_cast<float*>(a.C), nullptr, 0,
+                                                              nullptr, splits, a.accumulate, 0);
       }
       break;
   }
@@ -951,8 +971,10 @@ static double round_fill(long tiles) { return (double)tiles / (double)(cdiv((int
 
 template <typename T, bool AKC, bool BKC>
 static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
-  // split-K weight gradients (their M x N is small)
-  if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2) return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
+  // split-K weight gradients (their M x N is small): 256 x 256 tiles unless there are fewer than
+  // 16 of them (C x C), where the 128 x 128 tile's smaller partials win
+  if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2 && (long)cdiv(a.M, 256) * cdiv(a.N, 256) >= 16)
+    return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
   if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N)) {
     // K-contiguous products whose 256-wide column tiles leave CUs idle in the last round
     // (N = 768: 192 tiles per 16384 rows) take 192-wide column tiles when those fill the rounds
@@ -982,6 +1004,54 @@ hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& 
   if (a_kc && !b_kc) return launch_t<float, 128, 128, true, false>(epi, a, scratch, scratch_floats, s);
   if (!a_kc && !b_kc) return launch_t<float, 128, 128, false, false>(epi, a, scratch, scratch_floats, s);
   return launch_t<float, 128, 128, false, true>(epi, a, scratch, scratch_floats, s);
+}
+
+// Two fp32-output (weight-gradient) products with the same K and operand layouts in one split-K
+// launch of 256 x 256 tiles: the splits are chosen for the tiles of both, so two small products
+// fill the CUs with fewer, larger partials than each would alone; then one reduction for both.
+template <bool AKC, bool BKC>
+static hipError_t launch_pair_t(const GemmArgs& a0, const GemmArgs& a1, float* scratch, size_t sf, hipStream_t s) {
+  using CF = Cfg<bf16, 256, 256, AKC, BKC>;
+  const long t0 = (long)cdiv(a0.M, 256) * cdiv(a0.N, 256), t1 = (long)cdiv(a1.M, 256) * cdiv(a1.N, 256);
+  const size_t n0 = (size_t)a0.M * a0.N, n1 = (size_t)a1.M * a1.N;
+  int splits = splits_for(t0 + t1, (long)(n0 + n1), a0.K, sf, 256);
+  int k_split = a0.K;
+  if (splits > 1) {
+    k_split = cdiv(cdiv(a0.K, splits), CF::BK) * CF::BK;
+    splits = cdiv(a0.K, k_split);
+  }
+  float* part0 = splits > 1 ? scratch : nullptr;
+  float* part1 = splits > 1 ? scratch + (size_t)splits * n0 : nullptr;
+  const int nblk0 = (int)(t0 * splits);
+  dim3 grid(((t0 + t1) * splits + 7) & ~7L);
+  static bool attr = false;
+  auto kern = gemm_kernel<bf16, 256, 256, AKC, BKC, EPI_F32>;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)CF::LDS_BYTES);
+    attr = true;
+  }
+  kern<<<grid, CF::NTHR, CF::LDS_BYTES, s>>>(a0, k_split, part0, a1, part1, nblk0);
+  if (splits > 1)
+    splitk_reduce<<<splitk_reduce_blocks(n0 + n1), 256, 0, s>>>(part0, n0, reinterpret_cast<float*>(a0.C), part1, n1,
+                                                                 reinterpret_cast<float*>(a1.C), splits,
+                                                                 a0.accumulate, a1.accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32_pair(DType dt, bool a_kc, bool b_kc, const GemmArgs& a0, const GemmArgs& a1,
+                                float* scratch, size_t scratch_floats, hipStream_t s) {
+  const bool ok = dt == DT_BF16 && a0.K == a1.K && a0.M > 0 && a0.N > 0 && a1.M > 0 && a1.N > 0 && a0.K > 0 &&
+                  a0.ldc == a0.N && a1.ldc == a1.N && scratch;
+  if (!ok) {  // one after the other
+    hipError_t e = launch_gemm(dt, a_kc, b_kc, EPI_F32, a0, scratch, scratch_floats, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm(dt, a_kc, b_kc, EPI_F32, a1, scratch, scratch_floats, s);
+  }
+  if (a_kc && b_kc) return launch_pair_t<true, true>(a0, a1, scratch, scratch_floats, s);
+  if (a_kc && !b_kc) return launch_pair_t<true, false>(a0, a1, scratch, scratch_floats, s);
+  if (!a_kc && !b_kc) return launch_pair_t<false, false>(a0, a1, scratch, scratch_floats, s);
+  return launch_pair_t<false, true>(a0, a1, scratch, scratch_floats, s);
 }
 
 }  // namespace g2

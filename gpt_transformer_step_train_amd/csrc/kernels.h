@@ -44,6 +44,11 @@ struct GemmArgs {
 // Column sums (GemmArgs::colsum): `scratch` must hold (M/128 rounded up) * 2 * N floats.
 hipError_t launch_gemm(DType dt, bool a_kc, bool b_kc, Epi epi, const GemmArgs& a, float* scratch,
                        size_t scratch_floats, hipStream_t s);
+// Two EPI_F32 products with the same K (weight gradients of two layers) in one split-K launch;
+// scratch as for launch_gemm, for the partials of both. Falls back to two launches when the
+// shapes do not allow it (K differs, ldc != N, fp32).
+hipError_t launch_gemm_f32_pair(DType dt, bool a_kc, bool b_kc, const GemmArgs& a0, const GemmArgs& a1,
+                                float* scratch, size_t scratch_floats, hipStream_t s);
 // Choose the number of K splits for an EPI_F32 GEMM (1 = none).
 int gemm_splits(int M, int N, int K, size_t scratch_floats);
 

@@ -539,11 +539,7 @@ int backward_impl() {
       if (g.shadow_t) RUN(gemm(true, true, EPI_BIAS, BT, C, C, g.dres, C, WT(o.attprojw), C, g.dbuf2, C));
       else RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
     }
-    {
-      ProfScope ps_(GPT2_K_GEMM_ATTPROJ_DW);
-      RUN(gemm(false, false, EPI_F32, C, C, BT, g.dres, C, a.atty, C, G(o.attprojw), C, nullptr, nullptr, 0, nullptr,
-             acc, true));
-    }
+    // (the attproj weight gradient, dres^T atty, is taken together with the qkv one below)
     {
       ProfScope ps_(GPT2_K_ATTENTION_BWD_PRE);
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
@@ -573,9 +569,27 @@ int backward_impl() {
       else RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
     }
     {
+      // the qkv and attproj weight gradients in one split-K launch (dres still holds the gradient
+      // at the attention block's output: nothing above touched it)
       ProfScope ps_(GPT2_K_GEMM_QKV_DW);
-      RUN(gemm(false, false, EPI_F32, 3 * C, C, BT, g.dbuf1, 3 * C, a.ln1, C, G(o.qkvw), C, nullptr, nullptr, 0,
-             nullptr, acc, true));
+      GemmArgs q{}, pj{};
+      q.M = 3 * C;
+      q.N = C;
+      q.K = BT;
+      q.A = g.dbuf1;
+      q.lda = 3 * C;
+      q.B = a.ln1;
+      q.ldb = C;
+      q.C = G(o.qkvw);
+      q.ldc = C;
+      q.accumulate = acc;
+      pj = q;
+      pj.M = C;
+      pj.A = g.dres;
+      pj.lda = C;
+      pj.B = a.atty;
+      pj.C = G(o.attprojw);
+      HIPCHK(launch_gemm_f32_pair(g.dt, false, false, q, pj, g.scratch, g.scratch_floats, s));
     }
     {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);

@@ -123,10 +123,10 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_GEMM_FC_DX 15
 #define GPT2_K_GEMM_FC_DW 16
 #define GPT2_K_GEMM_ATTPROJ_DX 17
-#define GPT2_K_GEMM_ATTPROJ_DW 18
+#define GPT2_K_GEMM_ATTPROJ_DW 18     /* no launches: taken with GPT2_K_GEMM_QKV_DW */
 #define GPT2_K_ATTENTION_BWD 19      /* dK, dV                                */
 #define GPT2_K_GEMM_QKV_DX 20
-#define GPT2_K_GEMM_QKV_DW 21
+#define GPT2_K_GEMM_QKV_DW 21         /* qkv and attproj weight gradients, one launch */
 #define GPT2_K_ENCODER_BWD 22
 #define GPT2_K_GRAD_NORM 23
 #define GPT2_K_ADAMW 24
