@@ -528,7 +528,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qq0 = qt0 + 32 * qb;
-      if (qq0 + 31 < kw0) continue;  // all queries before this wave's keys
+      // sub-blocks whose queries all precede this wave's keys are not skipped but fully masked
+      // below: a skip here puts the dK/dV accumulators on two control paths, and the register
+      // copies the compiler then makes on every tile cost more than the few extra MFMAs
       f32x16 sacc = zero16(), dpacc = zero16();  // rows = queries, cols = keys
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
