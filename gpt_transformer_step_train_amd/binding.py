@@ -21,7 +21,7 @@ EXPORTS = [
     "gpt2_workspace_bytes", "gpt2_init", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_grad_norm",
     "gpt2_last_status", "gpt2_last_error", "gpt2_num_params", "gpt2_get_params", "gpt2_set_params",
     "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_logits", "gpt2_free", "gpt2_profile_enable",
-    "gpt2_profile_read",
+    "gpt2_profile_read", "gpt2_skip_update", "gpt2_lr_schedule", "gpt2_outlier_reset", "gpt2_outlier_update",
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
@@ -36,6 +36,14 @@ class gpt2_config(ctypes.Structure):
                 ("linear_bias", ctypes.c_int32), ("ln_bias", ctypes.c_int32), ("grad_accum", ctypes.c_int32),
                 ("grad_clip", ctypes.c_float), ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_uint64)]
+
+
+GPT2_OUTLIER_WINDOW = 128
+
+
+class gpt2_outlier(ctypes.Structure):
+    _fields_ = [("values", ctypes.c_double * GPT2_OUTLIER_WINDOW), ("count", ctypes.c_int32),
+                ("next", ctypes.c_int32)]
 
 
 _lib = None
@@ -69,6 +77,10 @@ def load(path=LIB_PATH):
         "gpt2_free": (None, []),
         "gpt2_profile_enable": (ctypes.c_int, [ctypes.c_uint32]),
         "gpt2_profile_read": (ctypes.c_int, [_vp, _vp, _i32]),
+        "gpt2_skip_update": (ctypes.c_int, []),
+        "gpt2_lr_schedule": (_f32, [_i32, _f32, _i32, _i32, _f32]),
+        "gpt2_outlier_reset": (None, [ctypes.POINTER(gpt2_outlier)]),
+        "gpt2_outlier_update": (ctypes.c_double, [ctypes.POINTER(gpt2_outlier), ctypes.c_double]),
         "gpt2op_gemm": (ctypes.c_int, [ctypes.c_int] * 7 + [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp,
                                                             ctypes.c_int, _vp, _u64, _vp]),
         "gpt2op_gemm_colsum": (ctypes.c_int, [ctypes.c_int] * 7 + [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
@@ -153,6 +165,22 @@ def gpt2_adamw_step(lr, b1, b2, eps, wd, t):
 
 def gpt2_grad_norm():
     return load().gpt2_grad_norm()
+
+
+def gpt2_skip_update():
+    return load().gpt2_skip_update()
+
+
+def gpt2_lr_schedule(step, lr_max, warmup, total, final_frac):
+    return load().gpt2_lr_schedule(step, lr_max, warmup, total, final_frac)
+
+
+def gpt2_outlier_reset(d):
+    load().gpt2_outlier_reset(ctypes.byref(d))
+
+
+def gpt2_outlier_update(d, x):
+    return load().gpt2_outlier_update(ctypes.byref(d), x)
 
 
 def gpt2_last_status():

@@ -789,6 +789,45 @@ int gpt2_profile_read(float* ms, int32_t* launches, int32_t n) {
 }
 
 int gpt2_last_status(void) { return g_status; }
+
+int gpt2_skip_update(void) {
+  RUN(check_ready());
+  g.micro = 0;
+  return ok();
+}
+
+float gpt2_lr_schedule(int32_t step, float lr_max, int32_t warmup, int32_t total, float final_frac) {
+  if (step < 1 || warmup < 0 || total <= warmup) return NAN;
+  if (step <= warmup) return (float)((double)lr_max * step / warmup);
+  const double lr_min = (double)final_frac * lr_max;
+  if (step >= total) return (float)lr_min;
+  const double ratio = (double)(step - warmup) / (double)(total - warmup);
+  const double coeff = 0.5 * (1.0 + cos(M_PI * ratio));
+  return (float)(lr_min + coeff * ((double)lr_max - lr_min));
+}
+
+void gpt2_outlier_reset(gpt2_outlier* d) {
+  if (!d) return;
+  memset(d, 0, sizeof(*d));
+}
+
+double gpt2_outlier_update(gpt2_outlier* d, double x) {
+  if (!d) return NAN;
+  double z = NAN;
+  if (d->count >= GPT2_OUTLIER_WINDOW) {
+    double mean = 0.0;
+    for (int i = 0; i < GPT2_OUTLIER_WINDOW; ++i) mean += d->values[i];
+    mean /= GPT2_OUTLIER_WINDOW;
+    double var = 0.0;
+    for (int i = 0; i < GPT2_OUTLIER_WINDOW; ++i) var += (d->values[i] - mean) * (d->values[i] - mean);
+    var /= GPT2_OUTLIER_WINDOW;
+    if (var > 0.0) z = (x - mean) / sqrt(var);
+  }
+  d->values[d->next] = x;
+  d->next = (d->next + 1) % GPT2_OUTLIER_WINDOW;
+  if (d->count < GPT2_OUTLIER_WINDOW) d->count++;
+  return z;
+}
 const char* gpt2_last_error(void) { return g_err.c_str(); }
 uint64_t gpt2_num_params(void) { return g.ready ? g.N : 0; }
 

@@ -89,6 +89,34 @@ int gpt2_backward(void);
  * skipped on the device; gpt2_grad_norm() then returns a non-finite value. Asynchronous. */
 int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t);
 
+/* Discard the gradients accumulated since the last update without applying them (the update is
+ * skipped, e.g. after a loss or gradient-norm spike); the next gpt2_backward overwrites them.
+ * Host-side state only. */
+int gpt2_skip_update(void);
+
+/* Host-side training-loop helpers (no device work, callable before gpt2_init).
+ * Learning rate of update `step` (1-based): linear warmup from 0 to lr_max over `warmup` updates
+ * (lr_max * step / warmup), then a cosine decay from lr_max to final_frac * lr_max reached at
+ * update `total`, constant after that: "Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section
+ * 参数指南 (flags -k cosine, -l, -q, -u, -x) and the lr column printed in section 训练. The shape of
+ * the decay between the two ends is half a cosine period. warmup >= 0, total > warmup. */
+float gpt2_lr_schedule(int32_t step, float lr_max, int32_t warmup, int32_t total, float final_frac);
+
+/* Spike detector for the update-skip of the same post (flags -sl / -sg, section 400B token 运行):
+ * gpt2_outlier_update returns the z-score (x - mean) / std of x against the previous
+ * GPT2_OUTLIER_WINDOW values it was given (population standard deviation), or NaN while fewer than
+ * that many have been seen or the window has zero spread, and then adds x to the window. The caller
+ * skips the update when the loss or gradient-norm z-score exceeds its threshold (5.0 on the page).
+ * The state is caller-owned host memory; gpt2_outlier_reset empties it. */
+#define GPT2_OUTLIER_WINDOW 128
+typedef struct {
+  double values[GPT2_OUTLIER_WINDOW];
+  int32_t count; /* values seen, saturating at GPT2_OUTLIER_WINDOW */
+  int32_t next;  /* slot the next value goes to */
+} gpt2_outlier;
+void gpt2_outlier_reset(gpt2_outlier* d);
+double gpt2_outlier_update(gpt2_outlier* d, double x);
+
 /* Diagnostics and parity (synchronous; host buffers owned by the caller). */
 float gpt2_grad_norm(void);     /* pre-clip global L2 norm of the last update's gradients */
 int gpt2_last_status(void);     /* status of the most recent call */

@@ -47,7 +47,7 @@ __all__ = [
     "attention_forward", "attention_backward", "cross_entropy_forward_backward",
     "encoder_forward", "encoder_backward",
     "forward_backward", "forward_logits", "next_token_probs",
-    "grad_norm", "clip_scale", "adamw_update", "train", "matmul_nt",
+    "grad_norm", "clip_scale", "adamw_update", "train", "matmul_nt", "lr_schedule", "OutlierDetector",
     "CFG_TOY", "CFG_124M", "CFG_350M", "CFG_1558M",
 ]
 
@@ -414,6 +414,52 @@ def train(cfg: Config, params, batches, lr, b1, b2, eps, wd, clip=0.0, grad_accu
         losses.append(lsum / grad_accum)
         norms.append(nrm)
     return p, m, v, losses, norms
+
+
+# ----------------------------------------------------------------------------------------
+# Training-loop helpers around the update
+# ----------------------------------------------------------------------------------------
+
+def lr_schedule(step: int, lr_max: float, warmup: int, total: int, final_frac: float) -> float:
+    """Learning rate of update `step` (1-based).
+
+    "Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南: -u warms the rate up linearly
+    from 0 to the maximum (-l) over the first updates; -k cosine with -q decays it to that
+    fraction of the maximum over the whole run (-x updates). Section 训练 prints the first ten
+    rates of such a run. Between warmup and the end the decay is half a cosine period (the
+    plain reading of "cosine"); after the end it stays at the final value.
+    """
+    if step <= warmup:
+        return lr_max * step / warmup
+    lr_min = final_frac * lr_max
+    if step >= total:
+        return lr_min
+    frac = (step - warmup) / (total - warmup)
+    return lr_min + 0.5 * (1.0 + math.cos(math.pi * frac)) * (lr_max - lr_min)
+
+
+class OutlierDetector:
+    """z-score of each new value against the previous `window` values (population standard
+    deviation); None until `window` values have been seen or when they are all equal.
+
+    The update-skip of the same post (section 400B token 运行, flags -sl 5.0 -sg 5.0) compares the
+    loss and the gradient norm this way; the window length is not printed (128 here).
+    """
+
+    def __init__(self, window: int = 128):
+        self.window = window
+        self.values = []
+
+    def update(self, x: float):
+        z = None
+        if len(self.values) == self.window:
+            mean = sum(self.values) / self.window
+            var = sum((v - mean) ** 2 for v in self.values) / self.window
+            if var > 0.0:
+                z = (x - mean) / math.sqrt(var)
+            self.values.pop(0)
+        self.values.append(x)
+        return z
 
 
 def matmul_nt(a, b):

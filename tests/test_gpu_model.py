@@ -166,6 +166,31 @@ def test_grad_accumulation_two_micro_steps():
     assert max(worst.values()) <= 1e-3, worst
 
 
+def test_skipped_update_discards_the_gradients():
+    """After gpt2_skip_update the next backward starts from zero: its gradients equal those of a
+    lone backward of the same batch, bit for bit, and the parameters are untouched."""
+    cfg = SMALL
+    B, T = 2, 64
+    (t0, y0), (t1, y1) = (synth.zipf_batch(cfg.vocab, B, T, s) for s in range(2))
+    m = model(cfg, B, T, bd.GPT2_BF16)
+    p_before = m.params()
+    m.forward(cuda_i32(t0), cuda_i32(y0))
+    m.backward()
+    bd.check(bd.gpt2_skip_update(), "gpt2_skip_update")
+    m.forward(cuda_i32(t1), cuda_i32(y1))
+    m.backward()
+    g_after_skip = m.grads()
+    assert np.array_equal(m.params(), p_before)
+    m2 = model(cfg, B, T, bd.GPT2_BF16)
+    m2.forward(cuda_i32(t1), cuda_i32(y1))
+    m2.backward()
+    assert np.array_equal(g_after_skip, m2.grads())
+    # an update right after a skip has no gradients to apply
+    assert bd.gpt2_adamw_step(6e-4, 0.9, 0.95, 1e-8, 0.1, 1) == bd.GPT2_OK
+    bd.check(bd.gpt2_skip_update(), "gpt2_skip_update")
+    assert bd.gpt2_adamw_step(6e-4, 0.9, 0.95, 1e-8, 0.1, 2) == bd.GPT2_ESTATE
+
+
 def test_bf16_bitwise_deterministic():
     cfg = SMALL
     B, T = 4, 128
