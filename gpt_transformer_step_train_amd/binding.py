@@ -13,6 +13,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgpt2.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ENOMEM, GPT2_EHIP, GPT2_ESTATE, GPT2_ERANGE, GPT2_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
+GPT2_EIO = -7
 GPT2_FP32, GPT2_BF16 = 0, 1
 EPI_BIAS, EPI_GELU, EPI_RESID, EPI_GELU_BWD, EPI_F32, EPI_GELU_GRAD, EPI_MUL = 0, 1, 2, 3, 4, 5, 6
 
@@ -21,7 +22,7 @@ EXPORTS = [
     "gpt2_workspace_bytes", "gpt2_init", "gpt2_forward", "gpt2_backward", "gpt2_adamw_step", "gpt2_grad_norm",
     "gpt2_last_status", "gpt2_last_error", "gpt2_num_params", "gpt2_get_params", "gpt2_set_params",
     "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_logits", "gpt2_free", "gpt2_profile_enable",
-    "gpt2_profile_read", "gpt2_skip_update", "gpt2_lr_schedule", "gpt2_outlier_reset", "gpt2_outlier_update",
+    "gpt2_profile_read", "gpt2_skip_update", "gpt2_save", "gpt2_load", "gpt2_lr_schedule", "gpt2_outlier_reset", "gpt2_outlier_update",
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
@@ -78,6 +79,8 @@ def load(path=LIB_PATH):
         "gpt2_profile_enable": (ctypes.c_int, [ctypes.c_uint32]),
         "gpt2_profile_read": (ctypes.c_int, [_vp, _vp, _i32]),
         "gpt2_skip_update": (ctypes.c_int, []),
+        "gpt2_save": (ctypes.c_int, [ctypes.c_char_p, _i32, _u64]),
+        "gpt2_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(_u64)]),
         "gpt2_lr_schedule": (_f32, [_i32, _f32, _i32, _i32, _f32]),
         "gpt2_outlier_reset": (None, [ctypes.POINTER(gpt2_outlier)]),
         "gpt2_outlier_update": (ctypes.c_double, [ctypes.POINTER(gpt2_outlier), ctypes.c_double]),
@@ -169,6 +172,17 @@ def gpt2_grad_norm():
 
 def gpt2_skip_update():
     return load().gpt2_skip_update()
+
+
+def gpt2_save(path, t, cursor):
+    return load().gpt2_save(os.fsencode(path), t, cursor)
+
+
+def gpt2_load(path):
+    """Returns (status, t, cursor)."""
+    t, cur = _i32(0), _u64(0)
+    rc = load().gpt2_load(os.fsencode(path), ctypes.byref(t), ctypes.byref(cur))
+    return rc, t.value, cur.value
 
 
 def gpt2_lr_schedule(step, lr_max, warmup, total, final_frac):

@@ -853,6 +853,102 @@ int gpt2_set_params(const float* src, uint64_t n) {
   return ok();
 }
 
+// ------------------------------------------------------------------ checkpoint
+namespace {
+constexpr char CKPT_MAGIC[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', 'T'};
+constexpr uint32_t CKPT_VERSION = 1;
+constexpr size_t CKPT_CHUNK = (size_t)16 << 20;  // floats per host staging chunk (64 MiB)
+
+void ckpt_arch(int32_t (&a)[8]) {
+  const gpt2_config& c = g.cfg;
+  const int32_t v[8] = {c.n_layer, c.n_head, c.n_embd, c.vocab, c.padded_vocab, c.max_seq, c.linear_bias, c.ln_bias};
+  for (int i = 0; i < 8; ++i) a[i] = v[i];
+}
+
+struct File {
+  FILE* f = nullptr;
+  ~File() {
+    if (f) fclose(f);
+  }
+};
+
+// device fp32 array <-> file, through a host chunk
+int write_dev(FILE* f, const float* dev, size_t n, std::vector<float>& buf) {
+  for (size_t i = 0; i < n; i += CKPT_CHUNK) {
+    const size_t k = std::min(CKPT_CHUNK, n - i);
+    HIPCHK(hipMemcpyAsync(buf.data(), dev + i, k * 4, hipMemcpyDeviceToHost, g.stream));
+    HIPCHK(hipStreamSynchronize(g.stream));
+    if (fwrite(buf.data(), 4, k, f) != k) return fail(GPT2_EIO, "checkpoint: write failed");
+  }
+  return GPT2_OK;
+}
+int read_dev(FILE* f, float* dev, size_t n, std::vector<float>& buf) {
+  for (size_t i = 0; i < n; i += CKPT_CHUNK) {
+    const size_t k = std::min(CKPT_CHUNK, n - i);
+    if (fread(buf.data(), 4, k, f) != k) return fail(GPT2_EIO, "checkpoint: file too short");
+    HIPCHK(hipMemcpyAsync(dev + i, buf.data(), k * 4, hipMemcpyHostToDevice, g.stream));
+    HIPCHK(hipStreamSynchronize(g.stream));
+  }
+  return GPT2_OK;
+}
+}  // namespace
+
+int gpt2_save(const char* path, int32_t t, uint64_t cursor) {
+  RUN(check_ready());
+  if (!path) return fail(GPT2_EINVAL, "gpt2_save: null path");
+  if (g.micro != 0) return fail(GPT2_ESTATE, "gpt2_save: gradients pending; save between updates");
+  HIPCHK(hipStreamSynchronize(g.stream));
+  File file;
+  file.f = fopen(path, "wb");
+  if (!file.f) return fail(GPT2_EIO, "gpt2_save: cannot open %s", path);
+  int32_t arch[8];
+  ckpt_arch(arch);
+  const uint64_t n = g.N;
+  bool okw = fwrite(CKPT_MAGIC, 1, 8, file.f) == 8 && fwrite(&CKPT_VERSION, 4, 1, file.f) == 1 &&
+             fwrite(arch, 4, 8, file.f) == 8 && fwrite(&n, 8, 1, file.f) == 1 && fwrite(&t, 4, 1, file.f) == 1 &&
+             fwrite(&cursor, 8, 1, file.f) == 1;
+  if (!okw) return fail(GPT2_EIO, "gpt2_save: write failed");
+  std::vector<float> buf(std::min<size_t>(CKPT_CHUNK, g.N));
+  RUN(write_dev(file.f, g.params, g.N, buf));
+  RUN(write_dev(file.f, g.m, g.N, buf));
+  RUN(write_dev(file.f, g.v, g.N, buf));
+  if (fflush(file.f) != 0) return fail(GPT2_EIO, "gpt2_save: write failed");
+  return ok();
+}
+
+int gpt2_load(const char* path, int32_t* t, uint64_t* cursor) {
+  RUN(check_ready());
+  if (!path || !t || !cursor) return fail(GPT2_EINVAL, "gpt2_load: null argument");
+  File file;
+  file.f = fopen(path, "rb");
+  if (!file.f) return fail(GPT2_EIO, "gpt2_load: cannot open %s", path);
+  char magic[8];
+  uint32_t version = 0;
+  int32_t arch[8], want[8], tt = 0;
+  uint64_t n = 0, cur = 0;
+  bool okr = fread(magic, 1, 8, file.f) == 8 && fread(&version, 4, 1, file.f) == 1 &&
+             fread(arch, 4, 8, file.f) == 8 && fread(&n, 8, 1, file.f) == 1 && fread(&tt, 4, 1, file.f) == 1 &&
+             fread(&cur, 8, 1, file.f) == 1;
+  if (!okr || memcmp(magic, CKPT_MAGIC, 8) != 0 || version != CKPT_VERSION)
+    return fail(GPT2_EIO, "gpt2_load: %s is not a version-%u checkpoint", path, CKPT_VERSION);
+  ckpt_arch(want);
+  if (memcmp(arch, want, sizeof arch) != 0 || n != g.N)
+    return fail(GPT2_EIO, "gpt2_load: %s holds a different architecture", path);
+  std::vector<float> buf(std::min<size_t>(CKPT_CHUNK, g.N));
+  RUN(read_dev(file.f, g.params, g.N, buf));
+  RUN(read_dev(file.f, g.m, g.N, buf));
+  RUN(read_dev(file.f, g.v, g.N, buf));
+  if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
+  HIPCHK(refresh_transposed());
+  HIPCHK(hipStreamSynchronize(g.stream));
+  g.micro = 0;
+  g.fwd_targets = false;
+  g.fwd_logits = false;
+  *t = tt;
+  *cursor = cur;
+  return ok();
+}
+
 int gpt2_get_grads(float* dst, uint64_t n) {
   RUN(check_ready());
   if (!dst || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);

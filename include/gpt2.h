@@ -45,6 +45,7 @@ extern "C" {
 #define GPT2_ESTATE (-4)     /* call out of order (e.g. backward without a forward with targets) */
 #define GPT2_ERANGE (-5)     /* token not in [0, V) or target not in [-1, V) */
 #define GPT2_ENONFINITE (-6) /* gradient norm not finite: the update was skipped */
+#define GPT2_EIO (-7)        /* checkpoint file could not be written or read, or does not match */
 
 #define GPT2_FP32 0 /* fp32 everywhere */
 #define GPT2_BF16 1 /* bf16 activations and matmul inputs, fp32 accumulation, fp32 master/grads/m/v */
@@ -93,6 +94,21 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
  * skipped, e.g. after a loss or gradient-norm spike); the next gpt2_backward overwrites them.
  * Host-side state only. */
 int gpt2_skip_update(void);
+
+/* Checkpoint and bitwise resume ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南:
+ * -n checkpoints every n steps, -y 1 resumes, and determinism makes a resumed run continue
+ * exactly). gpt2_save writes the fp32 master parameters, AdamW's m and v, the caller's update
+ * count t and an opaque data cursor (e.g. the index of the next batch) to the host file `path`;
+ * it must be called between updates (no gradients pending: GPT2_ESTATE otherwise). gpt2_load
+ * reads such a file into the current model, whose architecture (n_layer, n_head, n_embd, vocab,
+ * padded_vocab, max_seq, linear_bias, ln_bias) must match the file's (precision, batch and seq
+ * may differ), refreshes the bf16 copies, discards pending gradients, and returns t and the
+ * cursor. Continuing from a loaded checkpoint reproduces the uninterrupted run bit for bit.
+ * File: the 8 bytes "GPT2CKPT", uint32 version 1, the 8 int32 architecture fields above, uint64
+ * N, int32 t, uint64 cursor, then N floats each of parameters, m and v (little-endian).
+ * Synchronous. GPT2_EIO on a file error, a short file or a mismatch. */
+int gpt2_save(const char* path, int32_t t, uint64_t cursor);
+int gpt2_load(const char* path, int32_t* t, uint64_t* cursor);
 
 /* Host-side training-loop helpers (no device work, callable before gpt2_init).
  * Learning rate of update `step` (1-based): linear warmup from 0 to lr_max over `warmup` updates
