@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute", type=int, default=0, choices=(0, 1, 2),
+                    help="activation recompute: 1 GELU, 2 also the LayerNorm outputs (less memory)")
     ap.add_argument("--kernel-table", action="store_true", help="print the per-class kernel times to stderr")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain device copy of MIB MiB (counter calibration)")
@@ -154,7 +156,7 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     m = bd.Model(w["L"], w["H"], w["C"], w["V"], w["Vp"], w["T"], w["B"], w["T"], bd.GPT2_BF16,
-                 grad_accum=w["accum"], grad_clip=1.0, seed=synth.PARAM_SEED)
+                 grad_accum=w["accum"], grad_clip=1.0, seed=synth.PARAM_SEED, recompute=args.recompute)
     n_micro = (args.warmup + args.steps + 1) * w["accum"]
     n_distinct = min(n_micro, 8)           # batches are reused cyclically beyond 8 micro-steps
     batches = []
@@ -232,12 +234,14 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload} train step, B={w['B']} T={w['T']} grad_accum={w['accum']}, "
-                               f"bf16 mixed (fp32 master/grads/AdamW), Zipf(1.1) tokens",
+                               f"bf16 mixed (fp32 master/grads/AdamW), Zipf(1.1) tokens"
+                               + (f", activation recompute {args.recompute}" if args.recompute else ""),
                    "global_batch": w["B"] * w["accum"], "seq_len": w["T"], "parallelism": "single GPU"},
         "mfu": round(mfu, 4),
         "flops_per_token": flops_tok,
         "final_loss": round(float(losses[-1]), 5),
         "roofline": roof,
+        "workspace_bytes": int(m.cfg.workspace_bytes),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -35,7 +35,8 @@ class gpt2_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("padded_vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("linear_bias", ctypes.c_int32), ("ln_bias", ctypes.c_int32), ("grad_accum", ctypes.c_int32),
-                ("grad_clip", ctypes.c_float), ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("grad_clip", ctypes.c_float), ("recompute", ctypes.c_int32), ("stream", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -140,9 +141,9 @@ def check(rc, what=""):
 
 def make_config(n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision=GPT2_BF16,
                 linear_bias=1, ln_bias=1, grad_accum=1, grad_clip=0.0, stream=None, workspace=None,
-                workspace_bytes=0):
+                workspace_bytes=0, recompute=0):
     return gpt2_config(n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision, linear_bias,
-                       ln_bias, grad_accum, grad_clip, _ptr(stream) if stream is not None else None,
+                       ln_bias, grad_accum, grad_clip, recompute, _ptr(stream) if stream is not None else None,
                        _ptr(workspace), workspace_bytes)
 
 
@@ -235,7 +236,7 @@ KERNEL_CLASSES = ["encoder_fwd", "layernorm_fwd", "gemm_qkv", "attention_fwd", "
                   "layernorm_bwd", "gemm_fcproj_dx", "gemm_fcproj_dw", "bias_grad", "gemm_fc_dx", "gemm_fc_dw",
                   "gemm_attproj_dx", "gemm_attproj_dw", "attention_bwd", "gemm_qkv_dx", "gemm_qkv_dw",
                   "encoder_bwd", "grad_norm", "adamw", "attention_bwd_q", "attention_bwd_pre",
-                  "weight_transpose"]
+                  "weight_transpose", "recompute"]
 
 
 def gpt2_profile_enable(mask):
@@ -252,12 +253,12 @@ class Model:
     """Owns the torch workspace and stream pointer of one gpt2_init'ed model."""
 
     def __init__(self, n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision=GPT2_BF16,
-                 linear_bias=1, ln_bias=1, grad_accum=1, grad_clip=0.0, seed=1337, device="cuda"):
+                 linear_bias=1, ln_bias=1, grad_accum=1, grad_clip=0.0, seed=1337, device="cuda", recompute=0):
         import torch
         self.torch = torch
         self.stream = torch.cuda.current_stream(device)
         cfg = make_config(n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision,
-                          linear_bias, ln_bias, grad_accum, grad_clip)
+                          linear_bias, ln_bias, grad_accum, grad_clip, recompute=recompute)
         nbytes = gpt2_workspace_bytes(cfg)
         if nbytes == 0:
             raise GPT2Error(f"bad config: {last_error()}")

@@ -131,6 +131,8 @@ hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float
 hipError_t launch_init_params(const WorkItem* items, int nitems, float* p, uint64_t seed, double std_,
                               hipStream_t s);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);
+// out[i] = gelu(in[i]) (tanh form) in the compute dtype; n a multiple of 8
+hipError_t launch_gelu(DType dt, const void* in, void* out, size_t n, hipStream_t s);
 // Transposed bf16 copy of a weight matrix: dst[dst_off + c * ldd + r] = src[src_off + r * cols + c],
 // r < rows, c < cols. tile0: the first 64 x 64 tile of this matrix in the launch's tile numbering.
 struct TransItem {

@@ -31,7 +31,10 @@ struct LayerOff {
   size_t ln1w, ln1b, qkvw, qkvb, attprojw, attprojb, ln2w, ln2b, fcw, fcb, fcprojw, fcprojb;
 };
 struct LayerAct {
-  // fch holds gelu'(z) of the MLP pre-activation z (all the backward needs of z), fchg gelu(z)
+  // recompute 0: fch holds gelu'(z) of the MLP pre-activation z (all the backward needs of z),
+  // fchg gelu(z). recompute >= 1: fch holds z and fchg is the buffer all layers share, refilled
+  // with gelu(z) in the backward. recompute 2: ln1 and ln2 are one shared buffer as well,
+  // refilled from the LayerNorm inputs and saved statistics in the backward.
   char *ln1, *qkv, *atty, *res1, *ln2, *fch, *fchg, *res2;
   float *ln1_mean, *ln1_rstd, *ln2_mean, *ln2_rstd, *lse;
 };
@@ -130,6 +133,7 @@ const char* check_config(const gpt2_config* c) {
     return "GPT2_FP32 needs head size in {4, 8, 16, 32, 64}";
   if (c->n_embd > 2048) return "n_embd must be <= 2048";
   if (c->grad_accum < 1) return "grad_accum must be >= 1";
+  if (c->recompute < 0 || c->recompute > 2) return "recompute must be 0, 1 or 2";
   if (c->linear_bias != 0 && c->linear_bias != 1) return "linear_bias must be 0 or 1";
   if (c->ln_bias != 0 && c->ln_bias != 1) return "ln_bias must be 0 or 1";
   return nullptr;
@@ -242,20 +246,23 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
   M->items = (WorkItem*)take(nitems * sizeof(WorkItem));
   M->encoded = take(BT * C * es);
   M->la.resize(L);
+  const int rc = c->recompute;
+  char* gelu_shared = rc >= 1 ? take(BT * 4 * C * es) : nullptr;
+  char* ln_shared = rc >= 2 ? take(BT * C * es) : nullptr;
   for (size_t l = 0; l < L; ++l) {
     LayerAct& a = M->la[l];
-    a.ln1 = take(BT * C * es);
+    a.ln1 = rc >= 2 ? ln_shared : take(BT * C * es);
     a.ln1_mean = (float*)take(BT * 4);
     a.ln1_rstd = (float*)take(BT * 4);
     a.qkv = take(BT * 3 * C * es);
     a.atty = take(BT * C * es);
     a.lse = (float*)take(B * H * T * 4);
     a.res1 = take(BT * C * es);
-    a.ln2 = take(BT * C * es);
+    a.ln2 = rc >= 2 ? ln_shared : take(BT * C * es);
     a.ln2_mean = (float*)take(BT * 4);
     a.ln2_rstd = (float*)take(BT * 4);
     a.fch = take(BT * 4 * C * es);
-    a.fchg = take(BT * 4 * C * es);
+    a.fchg = rc >= 1 ? gelu_shared : take(BT * 4 * C * es);
     a.res2 = take(BT * C * es);
   }
   M->lnf = take(BT * C * es);
@@ -434,8 +441,9 @@ int forward_impl(const int32_t* tokens, const int32_t* targets) {
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FC);
-      RUN(gemm(true, true, EPI_GELU_GRAD, BT, 4 * C, C, a.ln2, C, W(o.fcw), C, a.fch, 4 * C, W(o.fcb), nullptr, 0,
-               a.fchg));
+      // fch = gelu'(z), fchg = gelu(z); with recompute fch = z
+      RUN(gemm(true, true, g.cfg.recompute >= 1 ? EPI_GELU : EPI_GELU_GRAD, BT, 4 * C, C, a.ln2, C, W(o.fcw), C,
+               a.fch, 4 * C, W(o.fcb), nullptr, 0, a.fchg));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ);
@@ -501,14 +509,20 @@ int backward_impl() {
     // fcproj: res2 = res1 + gelu(z) Wfcproj^T + b ; dz = (dres Wfcproj) * gelu'(z)
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DX);
-      // dz = (dres Wfcproj) * gelu'(z); its column sums are the fc bias gradient
+      // dz = (dres Wfcproj) * gelu'(z) (gelu'(z) stored, or from z with recompute); its column sums
+      // are the fc bias gradient
       float* dfcb = lb ? G(o.fcb) : nullptr;
+      const Epi ep = g.cfg.recompute >= 1 ? EPI_GELU_BWD : EPI_MUL;
       if (g.shadow_t)
-        RUN(gemm(true, true, EPI_MUL, BT, 4 * C, C, g.dres, C, WT(o.fcprojw), C, g.dbuf1, 4 * C, nullptr, a.fch,
-                 4 * C, nullptr, 0, false, dfcb, acc));
+        RUN(gemm(true, true, ep, BT, 4 * C, C, g.dres, C, WT(o.fcprojw), C, g.dbuf1, 4 * C, nullptr, a.fch, 4 * C,
+                 nullptr, 0, false, dfcb, acc));
       else
-        RUN(gemm(true, false, EPI_MUL, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
+        RUN(gemm(true, false, ep, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
                  4 * C, nullptr, 0, false, dfcb, acc));
+    }
+    if (g.cfg.recompute >= 1) {  // gelu(z) again, for the fcproj weight gradient
+      ProfScope ps_(GPT2_K_RECOMPUTE);
+      HIPCHK(launch_gelu(g.dt, a.fch, a.fchg, (size_t)BT * 4 * C, s));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FCPROJ_DW);
@@ -521,6 +535,10 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_GEMM_FC_DX);
       if (g.shadow_t) RUN(gemm(true, true, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, WT(o.fcw), 4 * C, g.dbuf2, C));
       else RUN(gemm(true, false, EPI_BIAS, BT, C, 4 * C, g.dbuf1, 4 * C, W(o.fcw), C, g.dbuf2, C));
+    }
+    if (g.cfg.recompute >= 2) {  // ln2 again, for the fc weight gradient
+      ProfScope ps_(GPT2_K_RECOMPUTE);
+      HIPCHK(launch_layernorm_fwd(g.dt, BT, C, a.res1, W(o.ln2w), W(o.ln2b), a.ln2, a.ln2_mean, a.ln2_rstd, s));
     }
     {
       ProfScope ps_(GPT2_K_GEMM_FC_DW);
@@ -567,6 +585,10 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_GEMM_QKV_DX);
       if (g.shadow_t) RUN(gemm(true, true, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, WT(o.qkvw), 3 * C, g.dbuf2, C));
       else RUN(gemm(true, false, EPI_BIAS, BT, C, 3 * C, g.dbuf1, 3 * C, W(o.qkvw), C, g.dbuf2, C));
+    }
+    if (g.cfg.recompute >= 2) {  // ln1 again, for the qkv weight gradient
+      ProfScope ps_(GPT2_K_RECOMPUTE);
+      HIPCHK(launch_layernorm_fwd(g.dt, BT, C, xin, W(o.ln1w), W(o.ln1b), a.ln1, a.ln1_mean, a.ln1_rstd, s));
     }
     {
       // the qkv and attproj weight gradients in one split-K launch (dres still holds the gradient

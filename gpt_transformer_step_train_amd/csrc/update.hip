@@ -274,6 +274,33 @@ hipError_t launch_transpose_bf16(const TransItem* items, int nitems, int ntiles,
   return hipGetLastError();
 }
 
+// out = gelu(in), 8 elements (16 or 32 bytes) per thread and step
+template <typename T>
+__global__ __launch_bounds__(256) void gelu_kernel(const T* __restrict__ in, T* __restrict__ out, size_t n8) {
+  constexpr int VEC = Elt<T>::VEC;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+#pragma unroll
+    for (int h = 0; h < 8 / VEC; ++h) {
+      V16<T> v;
+      v.load(in + i * 8 + h * VEC);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v.v[e] = gelu_fwd(v.v[e]);
+      v.store(out + i * 8 + h * VEC);
+    }
+  }
+}
+hipError_t launch_gelu(DType dt, const void* in, void* out, size_t n, hipStream_t s) {
+  if (n % 8) return hipErrorInvalidValue;
+  const size_t n8 = n / 8;
+  if (!n8) return hipSuccess;
+  const int blocks = (int)std::min<size_t>(8192, (n8 + 255) / 256);
+  if (dt == DT_BF16)
+    gelu_kernel<bf16><<<blocks, 256, 0, s>>>(reinterpret_cast<const bf16*>(in), reinterpret_cast<bf16*>(out), n8);
+  else
+    gelu_kernel<float><<<blocks, 256, 0, s>>>(reinterpret_cast<const float*>(in), reinterpret_cast<float*>(out), n8);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
                                                    size_t n16) {
   for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = src[i];

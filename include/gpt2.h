@@ -59,6 +59,13 @@ typedef struct {
   int32_t linear_bias, ln_bias;    /* 1/1 for GPT-2; 0/1 for the BabyGPT toy */
   int32_t grad_accum;              /* micro-steps per update, >= 1 */
   float grad_clip;                 /* global-norm clip; <= 0 disables */
+  int32_t recompute;               /* activation recompute ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672",
+                                      section 参数指南, flag -r): 0 keeps every activation the
+                                      backward reads; 1 keeps the MLP pre-activation only and
+                                      recomputes GELU in the backward; 2 also recomputes the
+                                      outputs of the two LayerNorms of each layer from their
+                                      inputs and saved statistics. Same results up to the bf16
+                                      rounding of the recomputed GELU input; less memory. */
   void* stream;                    /* hipStream_t */
   void* workspace;                 /* device memory, >= gpt2_workspace_bytes(cfg), 256-byte aligned */
   uint64_t workspace_bytes;
@@ -177,7 +184,8 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_ATTENTION_BWD_Q 25    /* dQ                                    */
 #define GPT2_K_ATTENTION_BWD_PRE 26  /* D = rowsum(dO * O) per query          */
 #define GPT2_K_WEIGHT_TRANSPOSE 27  /* bf16 weight matrices -> transposed copies */
-#define GPT2_K_COUNT 28
+#define GPT2_K_RECOMPUTE 28          /* activation recompute in the backward (recompute >= 1) */
+#define GPT2_K_COUNT 29
 int gpt2_profile_enable(uint32_t mask);
 int gpt2_profile_read(float* ms, int32_t* launches, int32_t n);
 

@@ -52,8 +52,8 @@ def test_header_constants_match_binding():
 
 
 def test_config_struct_layout_matches_header():
-    # 12 int32 + float + 3 pointers/uint64 on x86-64
-    assert ctypes.sizeof(bd.gpt2_config) == 80  # 12 int32 + float + pad + 3 x 8 bytes
+    # 12 int32 + float + int32 (recompute) + 3 pointers/uint64 on x86-64
+    assert ctypes.sizeof(bd.gpt2_config) == 80  # 12 int32 + float + int32 + 3 x 8 bytes
     assert bd.gpt2_config.stream.offset == 56
 
 
@@ -88,11 +88,21 @@ def test_workspace_planner_host_only(lib):
     (dict(n_head=24), "head size 64"),
     (dict(precision=7), "precision"),
     (dict(grad_accum=0), "grad_accum"),
+    (dict(recompute=3), "recompute"),
 ])
 def test_invalid_configs_rejected_on_host(lib, kw, msg):
     assert bd.gpt2_workspace_bytes(_cfg(**kw)) == 0
     assert bd.gpt2_last_status() == bd.GPT2_EINVAL
     assert msg in bd.last_error()
+
+
+def test_recompute_saves_workspace(lib):
+    # recompute 1 drops one [B*T, 4C] buffer per layer but one (shared); 2 also the two LayerNorm
+    # outputs per layer but one
+    L, BT, C = 12, 16 * 1024, 768
+    w0, w1, w2 = (bd.gpt2_workspace_bytes(_cfg(recompute=r)) for r in range(3))
+    assert w0 - w1 >= (L - 1) * BT * 4 * C * 2
+    assert w1 - w2 >= (2 * L - 1) * BT * C * 2 - 256 * 2 * L
 
 
 def test_toy_config_accepted(lib):
