@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-master", type=int, default=0, choices=(0, 1),
+                    help="1: bf16 parameters without an fp32 master copy (stochastic rounding)")
     ap.add_argument("--recompute", type=int, default=0, choices=(0, 1, 2),
                     help="activation recompute: 1 GELU, 2 also the LayerNorm outputs (less memory)")
     ap.add_argument("--kernel-table", action="store_true", help="print the per-class kernel times to stderr")
@@ -156,7 +158,8 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     m = bd.Model(w["L"], w["H"], w["C"], w["V"], w["Vp"], w["T"], w["B"], w["T"], bd.GPT2_BF16,
-                 grad_accum=w["accum"], grad_clip=1.0, seed=synth.PARAM_SEED, recompute=args.recompute)
+                 grad_accum=w["accum"], grad_clip=1.0, seed=synth.PARAM_SEED, recompute=args.recompute,
+                 no_master=args.no_master)
     n_micro = (args.warmup + args.steps + 1) * w["accum"]
     n_distinct = min(n_micro, 8)           # batches are reused cyclically beyond 8 micro-steps
     batches = []
@@ -235,7 +238,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload} train step, B={w['B']} T={w['T']} grad_accum={w['accum']}, "
                                f"bf16 mixed (fp32 master/grads/AdamW), Zipf(1.1) tokens"
-                               + (f", activation recompute {args.recompute}" if args.recompute else ""),
+                               + (f", activation recompute {args.recompute}" if args.recompute else "")
+                               + (", no fp32 master (stochastic rounding)" if args.no_master else ""),
                    "global_batch": w["B"] * w["accum"], "seq_len": w["T"], "parallelism": "single GPU"},
         "mfu": round(mfu, 4),
         "flops_per_token": flops_tok,

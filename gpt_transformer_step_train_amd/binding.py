@@ -26,7 +26,7 @@ EXPORTS = [
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
-    "gpt2op_attention_backward_colsum",
+    "gpt2op_attention_backward_colsum", "gpt2op_stochastic_round",
 ]
 
 
@@ -35,7 +35,8 @@ class gpt2_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("padded_vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("linear_bias", ctypes.c_int32), ("ln_bias", ctypes.c_int32), ("grad_accum", ctypes.c_int32),
-                ("grad_clip", ctypes.c_float), ("recompute", ctypes.c_int32), ("stream", ctypes.c_void_p),
+                ("grad_clip", ctypes.c_float), ("recompute", ctypes.c_int32), ("no_master", ctypes.c_int32),
+                ("stream", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_uint64)]
 
@@ -94,6 +95,7 @@ def load(path=LIB_PATH):
         "gpt2op_layernorm_backward_scratch": (_u64, [ctypes.c_int, ctypes.c_int]),
         "gpt2op_attention_forward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 4),
         "gpt2op_attention_backward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7),
+        "gpt2op_stochastic_round": (ctypes.c_int, [_vp, _vp, _u64, _u64, _i32, _u64, _vp]),
         "gpt2op_attention_backward_colsum": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7 + [ctypes.c_int, _vp, _u64,
                                                                                           _vp]),
         "gpt2op_cross_entropy": (ctypes.c_int, [ctypes.c_int] * 4 + [_vp] * 5),
@@ -141,10 +143,10 @@ def check(rc, what=""):
 
 def make_config(n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision=GPT2_BF16,
                 linear_bias=1, ln_bias=1, grad_accum=1, grad_clip=0.0, stream=None, workspace=None,
-                workspace_bytes=0, recompute=0):
+                workspace_bytes=0, recompute=0, no_master=0):
     return gpt2_config(n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision, linear_bias,
-                       ln_bias, grad_accum, grad_clip, recompute, _ptr(stream) if stream is not None else None,
-                       _ptr(workspace), workspace_bytes)
+                       ln_bias, grad_accum, grad_clip, recompute, no_master,
+                       _ptr(stream) if stream is not None else None, _ptr(workspace), workspace_bytes)
 
 
 def gpt2_workspace_bytes(cfg):
@@ -253,12 +255,13 @@ class Model:
     """Owns the torch workspace and stream pointer of one gpt2_init'ed model."""
 
     def __init__(self, n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision=GPT2_BF16,
-                 linear_bias=1, ln_bias=1, grad_accum=1, grad_clip=0.0, seed=1337, device="cuda", recompute=0):
+                 linear_bias=1, ln_bias=1, grad_accum=1, grad_clip=0.0, seed=1337, device="cuda", recompute=0,
+                 no_master=0):
         import torch
         self.torch = torch
         self.stream = torch.cuda.current_stream(device)
         cfg = make_config(n_layer, n_head, n_embd, vocab, padded_vocab, max_seq, batch, seq, precision,
-                          linear_bias, ln_bias, grad_accum, grad_clip, recompute=recompute)
+                          linear_bias, ln_bias, grad_accum, grad_clip, recompute=recompute, no_master=no_master)
         nbytes = gpt2_workspace_bytes(cfg)
         if nbytes == 0:
             raise GPT2Error(f"bad config: {last_error()}")

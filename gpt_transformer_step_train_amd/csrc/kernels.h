@@ -121,7 +121,19 @@ struct AdamArgs {
   float lr, b1, b2, eps, wd;
   float bc1, bc2;    // 1/(1-b1^t), 1/(1-b2^t)
   float clip;        // <= 0: off
+  // bf16 parameters only (no fp32 master): p is read from and written back to the bf16 copy,
+  // rounded stochastically with the bits of sr_random(sr_seed, t, index)
+  int no_master;
+  int t;
+  uint64_t sr_seed;
 };
+// Stochastic rounding fp32 -> bf16 of element `index` at update t: r = the low 16 bits of the
+// SplitMix64 output number (t << 32 | index) of the stream seeded with `seed`; the magnitude is
+// truncated to bf16 after adding r to it, so it rounds away from zero exactly when r plus the 16
+// discarded bits reach 2^16, i.e. with probability (discarded bits) / 2^16 (unbiased).
+// Inf and NaN round to nearest.
+hipError_t launch_stochastic_round(const float* x, uint16_t* y, size_t n, uint64_t seed, int t, uint64_t index0,
+                                   hipStream_t s);
 // norm: partials -> norm2 (double) ; scale = clip / ||g|| when above the clip
 hipError_t launch_grad_norm_finish(const double* partial, int nparts, double* norm2, float* scale, float clip,
                                    hipStream_t s);

@@ -47,6 +47,7 @@ struct Model {
   int L = 0, H = 0, C = 0, V = 0, Vp = 0, maxT = 0, B = 0, T = 0, BT = 0, ldl = 0;
   size_t N = 0;
   size_t o_wte = 0, o_wpe = 0, o_lnfw = 0, o_lnfb = NONE;
+  uint64_t seed = 0;
   std::vector<LayerOff> lo;
   std::vector<WorkItem> items_host;
 
@@ -134,6 +135,8 @@ const char* check_config(const gpt2_config* c) {
   if (c->n_embd > 2048) return "n_embd must be <= 2048";
   if (c->grad_accum < 1) return "grad_accum must be >= 1";
   if (c->recompute < 0 || c->recompute > 2) return "recompute must be 0, 1 or 2";
+  if (c->no_master != 0 && c->no_master != 1) return "no_master must be 0 or 1";
+  if (c->no_master && c->precision != GPT2_BF16) return "no_master needs GPT2_BF16";
   if (c->linear_bias != 0 && c->linear_bias != 1) return "linear_bias must be 0 or 1";
   if (c->ln_bias != 0 && c->ln_bias != 1) return "ln_bias must be 0 or 1";
   return nullptr;
@@ -233,7 +236,7 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
 
   Model tmp;
   Model* M = m ? m : &tmp;
-  M->params = (float*)take(N * 4);
+  M->params = c->no_master ? nullptr : (float*)take(N * 4);
   M->grads = (float*)take(N * 4);
   M->m = (float*)take(N * 4);
   M->v = (float*)take(N * 4);
@@ -689,11 +692,14 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed) {
   HIPCHK(hipEventCreateWithFlags(&g.ev_sorted, hipEventDisableTiming));
   HIPCHK(hipMemcpyAsync(g.items, g.items_host.data(), g.items_host.size() * sizeof(WorkItem), hipMemcpyHostToDevice,
                         g.stream));
-  HIPCHK(launch_init_params(g.items, (int)g.items_host.size(), g.params, seed, 0.02, g.stream));
+  g.seed = seed;
+  // without an fp32 master the fp32 initial values pass through the gradient buffer
+  float* p0 = g.params ? g.params : g.grads;
+  HIPCHK(launch_init_params(g.items, (int)g.items_host.size(), p0, seed, 0.02, g.stream));
+  if (g.shadow) HIPCHK(launch_to_bf16(p0, g.shadow, g.N, g.stream));
   HIPCHK(launch_fill_f32(g.m, g.N, 0.f, g.stream));
   HIPCHK(launch_fill_f32(g.v, g.N, 0.f, g.stream));
   HIPCHK(launch_fill_f32(g.grads, g.N, 0.f, g.stream));
-  if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
   if (g.shadow_t) {
     make_trans_items();
     HIPCHK(hipMemcpyAsync(g.tr_items, g.tr_host.data(), g.tr_host.size() * sizeof(TransItem), hipMemcpyHostToDevice,
@@ -756,6 +762,9 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
   a.bc1 = (float)(1.0 / (1.0 - pow((double)b1, (double)t)));
   a.bc2 = (float)(1.0 / (1.0 - pow((double)b2, (double)t)));
   a.clip = g.cfg.grad_clip;
+  a.no_master = g.cfg.no_master;
+  a.t = t;
+  a.sr_seed = g.seed ^ 0xD1B54A32D192ED03ull;
   {
       ProfScope ps_(GPT2_K_ADAMW);
       HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale, g.norm2,
@@ -859,19 +868,67 @@ static int copy_d2h(void* dst, const void* src, size_t bytes) {
   return ok();
 }
 
+// host round-to-nearest-even fp32 -> bf16 (the device conversion's rule; NaN stays NaN)
+static uint16_t host_f2bf(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+static float host_bf2f(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+// parameters [i0, i0 + k) as fp32 on the host (from the master, or the bf16 parameters)
+static int params_to_host(float* dst, size_t i0, size_t k, std::vector<uint16_t>& tmp) {
+  if (g.params) {
+    HIPCHK(hipMemcpyAsync(dst, g.params + i0, k * 4, hipMemcpyDeviceToHost, g.stream));
+    HIPCHK(hipStreamSynchronize(g.stream));
+    return GPT2_OK;
+  }
+  tmp.resize(k);
+  HIPCHK(hipMemcpyAsync(tmp.data(), g.shadow + i0, k * 2, hipMemcpyDeviceToHost, g.stream));
+  HIPCHK(hipStreamSynchronize(g.stream));
+  for (size_t i = 0; i < k; ++i) dst[i] = host_bf2f(tmp[i]);
+  return GPT2_OK;
+}
+static int params_from_host(const float* src, size_t i0, size_t k, std::vector<uint16_t>& tmp) {
+  if (g.params) {
+    HIPCHK(hipMemcpyAsync(g.params + i0, src, k * 4, hipMemcpyHostToDevice, g.stream));
+    HIPCHK(hipStreamSynchronize(g.stream));
+    return GPT2_OK;
+  }
+  tmp.resize(k);
+  for (size_t i = 0; i < k; ++i) tmp[i] = host_f2bf(src[i]);
+  HIPCHK(hipMemcpyAsync(g.shadow + i0, tmp.data(), k * 2, hipMemcpyHostToDevice, g.stream));
+  HIPCHK(hipStreamSynchronize(g.stream));
+  return GPT2_OK;
+}
+// after the parameters changed: the bf16 copy (from the master) and the transposed copies
+static int params_changed() {
+  if (g.params && g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
+  HIPCHK(refresh_transposed());
+  HIPCHK(hipStreamSynchronize(g.stream));
+  return GPT2_OK;
+}
+
 int gpt2_get_params(float* dst, uint64_t n) {
   RUN(check_ready());
   if (!dst || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
-  return copy_d2h(dst, g.params, n * 4);
+  std::vector<uint16_t> tmp;
+  RUN(params_to_host(dst, 0, g.N, tmp));
+  return ok();
 }
 
 int gpt2_set_params(const float* src, uint64_t n) {
   RUN(check_ready());
   if (!src || n != g.N) return fail(GPT2_EINVAL, "need n == num_params (%zu)", g.N);
-  HIPCHK(hipMemcpyAsync(g.params, src, n * 4, hipMemcpyHostToDevice, g.stream));
-  if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
-  HIPCHK(refresh_transposed());
-  HIPCHK(hipStreamSynchronize(g.stream));
+  std::vector<uint16_t> tmp;
+  RUN(params_from_host(src, 0, g.N, tmp));
+  RUN(params_changed());
   return ok();
 }
 
@@ -928,10 +985,15 @@ int gpt2_save(const char* path, int32_t t, uint64_t cursor) {
   const uint64_t n = g.N;
   bool okw = fwrite(CKPT_MAGIC, 1, 8, file.f) == 8 && fwrite(&CKPT_VERSION, 4, 1, file.f) == 1 &&
              fwrite(arch, 4, 8, file.f) == 8 && fwrite(&n, 8, 1, file.f) == 1 && fwrite(&t, 4, 1, file.f) == 1 &&
-             fwrite(&cursor, 8, 1, file.f) == 1;
+             fwrite(&cursor, 8, 1, file.f) == 1 && fwrite(&g.seed, 8, 1, file.f) == 1;
   if (!okw) return fail(GPT2_EIO, "gpt2_save: write failed");
   std::vector<float> buf(std::min<size_t>(CKPT_CHUNK, g.N));
-  RUN(write_dev(file.f, g.params, g.N, buf));
+  std::vector<uint16_t> tmp;
+  for (size_t i = 0; i < g.N; i += CKPT_CHUNK) {  // parameters as fp32 (exact from bf16 too)
+    const size_t k = std::min(CKPT_CHUNK, g.N - i);
+    RUN(params_to_host(buf.data(), i, k, tmp));
+    if (fwrite(buf.data(), 4, k, file.f) != k) return fail(GPT2_EIO, "gpt2_save: write failed");
+  }
   RUN(write_dev(file.f, g.m, g.N, buf));
   RUN(write_dev(file.f, g.v, g.N, buf));
   if (fflush(file.f) != 0) return fail(GPT2_EIO, "gpt2_save: write failed");
@@ -947,22 +1009,26 @@ int gpt2_load(const char* path, int32_t* t, uint64_t* cursor) {
   char magic[8];
   uint32_t version = 0;
   int32_t arch[8], want[8], tt = 0;
-  uint64_t n = 0, cur = 0;
+  uint64_t n = 0, cur = 0, seed = 0;
   bool okr = fread(magic, 1, 8, file.f) == 8 && fread(&version, 4, 1, file.f) == 1 &&
              fread(arch, 4, 8, file.f) == 8 && fread(&n, 8, 1, file.f) == 1 && fread(&tt, 4, 1, file.f) == 1 &&
-             fread(&cur, 8, 1, file.f) == 1;
+             fread(&cur, 8, 1, file.f) == 1 && fread(&seed, 8, 1, file.f) == 1;
   if (!okr || memcmp(magic, CKPT_MAGIC, 8) != 0 || version != CKPT_VERSION)
     return fail(GPT2_EIO, "gpt2_load: %s is not a version-%u checkpoint", path, CKPT_VERSION);
   ckpt_arch(want);
   if (memcmp(arch, want, sizeof arch) != 0 || n != g.N)
     return fail(GPT2_EIO, "gpt2_load: %s holds a different architecture", path);
   std::vector<float> buf(std::min<size_t>(CKPT_CHUNK, g.N));
-  RUN(read_dev(file.f, g.params, g.N, buf));
+  std::vector<uint16_t> tmp;
+  for (size_t i = 0; i < g.N; i += CKPT_CHUNK) {
+    const size_t k = std::min(CKPT_CHUNK, g.N - i);
+    if (fread(buf.data(), 4, k, file.f) != k) return fail(GPT2_EIO, "checkpoint: file too short");
+    RUN(params_from_host(buf.data(), i, k, tmp));
+  }
   RUN(read_dev(file.f, g.m, g.N, buf));
   RUN(read_dev(file.f, g.v, g.N, buf));
-  if (g.shadow) HIPCHK(launch_to_bf16(g.params, g.shadow, g.N, g.stream));
-  HIPCHK(refresh_transposed());
-  HIPCHK(hipStreamSynchronize(g.stream));
+  RUN(params_changed());
+  g.seed = seed;
   g.micro = 0;
   g.fwd_targets = false;
   g.fwd_logits = false;
@@ -1077,6 +1143,12 @@ int gpt2op_layernorm_backward(int dtype, int rows, int C, const void* dy, const 
   return op_ret(launch_layernorm_bwd(to_dt(dtype), rows, C, dy, x, w, mean, rstd, dres, 1, dw, db, dsum, accumulate,
                                      partial, layernorm_bwd_partial_floats(rows, C),
                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gpt2op_stochastic_round(const float* x, uint16_t* y, uint64_t n, uint64_t seed, int32_t t, uint64_t index0,
+                            void* stream) {
+  if ((n && (!x || !y)) || t < 0) return fail(GPT2_EINVAL, "bad stochastic_round arguments");
+  return op_ret(launch_stochastic_round(x, y, n, seed, t, index0, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,

@@ -7,6 +7,10 @@
 // AdamW state m, v and an fp32 master copy next to bf16 parameters, and (section 参数指南, -c)
 // weight decay on 2-D tensors only.
 //
+// Without an fp32 master copy ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南: -w 0
+// keeps no fp32 parameters and relies on stochastic rounding) the update reads the bf16
+// parameters, computes in fp32, and rounds the result back stochastically.
+//
 // AdamW, decoupled decay on the pre-update value:
 //   g = s * grad;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2
 //   p = p - lr * ( (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd_i * p ),  wd_i = wd on 2-D tensors
@@ -71,96 +75,6 @@ hipError_t launch_grad_norm_finish(const double* partial, int nparts, double* no
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- AdamW
-constexpr int ADAM_T = 256;
-
-__global__ __launch_bounds__(ADAM_T) void adamw_kernel(const WorkItem* __restrict__ items, float* __restrict__ p,
-                                                       const float* __restrict__ g, float* __restrict__ m,
-                                                       float* __restrict__ v, uint16_t* __restrict__ shadow,
-                                                       const float* __restrict__ scale_p,
-                                                       const double* __restrict__ norm2_p, AdamArgs a) {
-  const double n2 = *norm2_p;
-  if (!(n2 <= 1.0e300)) return;  // non-finite norm: skip the update (NaN fails the compare)
-  const WorkItem it = items[blockIdx.x];
-  const float sc = *scale_p;
-  const float wd = it.kind == 1 ? a.wd : 0.f;
-  const size_t base = it.off;
-  auto step4 = [&](f32x4& pv, const f32x4& gv, f32x4& mv, f32x4& vv) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float gg = gv[e] * sc;
-      mv[e] = a.b1 * mv[e] + (1.f - a.b1) * gg;
-      vv[e] = a.b2 * vv[e] + (1.f - a.b2) * gg * gg;
-      const float mh = mv[e] * a.bc1;
-      const float vh = vv[e] * a.bc2;
-      pv[e] = pv[e] - a.lr * (mh / (sqrtf(vh) + a.eps) + wd * pv[e]);
-    }
-  };
-  // U vectors of 4 per thread and pass: all U x 4 loads are in flight before any arithmetic
-  constexpr int U = 4;
-  const int full = (int)it.len / (ADAM_T * 4 * U) * (ADAM_T * 4 * U);
-  for (int j0 = 0; j0 < full; j0 += ADAM_T * 4 * U) {
-    f32x4 pv[U], gv[U], mv[U], vv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t i = base + j0 + (u * ADAM_T + threadIdx.x) * 4;
-      pv[u] = *reinterpret_cast<const f32x4*>(p + i);
-      gv[u] = *reinterpret_cast<const f32x4*>(g + i);
-      mv[u] = *reinterpret_cast<const f32x4*>(m + i);
-      vv[u] = *reinterpret_cast<const f32x4*>(v + i);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t i = base + j0 + (u * ADAM_T + threadIdx.x) * 4;
-      step4(pv[u], gv[u], mv[u], vv[u]);
-      *reinterpret_cast<f32x4*>(p + i) = pv[u];
-      *reinterpret_cast<f32x4*>(m + i) = mv[u];
-      *reinterpret_cast<f32x4*>(v + i) = vv[u];
-      if (shadow) {
-        u32x2 sv = {pack2bf(pv[u][0], pv[u][1]), pack2bf(pv[u][2], pv[u][3])};
-        *reinterpret_cast<u32x2*>(shadow + i) = sv;
-      }
-    }
-  }
-  for (int j = full + threadIdx.x * 4; j < (int)it.len; j += ADAM_T * 4) {
-    const size_t i = base + j;
-    if (j + 4 <= (int)it.len) {
-      f32x4 pv = *reinterpret_cast<const f32x4*>(p + i);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + i);
-      f32x4 mv = *reinterpret_cast<const f32x4*>(m + i);
-      f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
-      step4(pv, gv, mv, vv);
-      *reinterpret_cast<f32x4*>(p + i) = pv;
-      *reinterpret_cast<f32x4*>(m + i) = mv;
-      *reinterpret_cast<f32x4*>(v + i) = vv;
-      if (shadow) {
-        u32x2 sv = {pack2bf(pv[0], pv[1]), pack2bf(pv[2], pv[3])};
-        *reinterpret_cast<u32x2*>(shadow + i) = sv;
-      }
-    } else {
-      for (int e = 0; j + e < (int)it.len; ++e) {
-        const size_t k = i + e;
-        const float gg = g[k] * sc;
-        const float mm = a.b1 * m[k] + (1.f - a.b1) * gg;
-        const float vv2 = a.b2 * v[k] + (1.f - a.b2) * gg * gg;
-        m[k] = mm;
-        v[k] = vv2;
-        const float pp = p[k] - a.lr * ((mm * a.bc1) / (sqrtf(vv2 * a.bc2) + a.eps) + wd * p[k]);
-        p[k] = pp;
-        if (shadow) shadow[k] = f2bf(pp);
-      }
-    }
-  }
-}
-
-hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float* g, float* m, float* v,
-                        uint16_t* shadow, const float* scale, const double* norm2, AdamArgs a, hipStream_t s) {
-  if (nitems <= 0) return hipSuccess;
-  adamw_kernel<<<nitems, ADAM_T, 0, s>>>(items, p, g, m, v, shadow, scale, norm2, a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- init
 // SplitMix64 (Steele, Lea & Flood 2014): output n of the stream seeded with s is
 // mix(s + (n+1) * 0x9E3779B97F4A7C15). Uniform in (0,1): ((x >> 11) + 0.5) * 2^-53.
 // Box-Muller (1958) on outputs (2p, 2p+1): normals 2p = r cos(2 pi u2), 2p+1 = r sin(2 pi u2),
@@ -172,6 +86,156 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
   return z ^ (z >> 31);
 }
 __device__ __forceinline__ double u01(uint64_t x) { return ((double)(x >> 11) + 0.5) * 0x1.0p-53; }
+
+// stochastic rounding to bf16 (see kernels.h)
+__device__ __forceinline__ uint16_t sr_bf16(float x, uint64_t seed, int t, uint64_t index) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7f800000u) == 0x7f800000u) return f2bf(x);
+  const uint32_t r = (uint32_t)splitmix64(seed, ((uint64_t)(uint32_t)t << 32) | index) & 0xffffu;
+  // adding r to the magnitude carries into the kept bits exactly when r + discarded >= 2^16
+  return (uint16_t)((u + r) >> 16);
+}
+
+__global__ __launch_bounds__(256) void sr_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n,
+                                                 uint64_t seed, int t, uint64_t index0) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    y[i] = sr_bf16(x[i], seed, t, index0 + i);
+}
+hipError_t launch_stochastic_round(const float* x, uint16_t* y, size_t n, uint64_t seed, int t, uint64_t index0,
+                                   hipStream_t s) {
+  if (!n) return hipSuccess;
+  sr_kernel<<<(int)std::min<size_t>(8192, (n + 255) / 256), 256, 0, s>>>(x, y, n, seed, t, index0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- AdamW
+constexpr int ADAM_T = 256;
+
+// NOMASTER: the parameters are the bf16 copy (p unused), read, updated in fp32 and rounded back
+// stochastically; else p is the fp32 master and the bf16 copy (when present) is its RNE rounding.
+template <bool NOMASTER>
+__global__ __launch_bounds__(ADAM_T) void adamw_kernel(const WorkItem* __restrict__ items, float* __restrict__ p,
+                                                       const float* __restrict__ g, float* __restrict__ m,
+                                                       float* __restrict__ v, uint16_t* __restrict__ shadow,
+                                                       const float* __restrict__ scale_p,
+                                                       const double* __restrict__ norm2_p, AdamArgs a) {
+  const double n2 = *norm2_p;
+  if (!(n2 <= 1.0e300)) return;  // non-finite norm: skip the update (NaN fails the compare)
+  const WorkItem it = items[blockIdx.x];
+  const float sc = *scale_p;
+  const float wd = it.kind == 1 ? a.wd : 0.f;
+  const size_t base = it.off;
+  auto upd = [&](float pp, float gg, float& mm, float& vv) {
+    gg *= sc;
+    mm = a.b1 * mm + (1.f - a.b1) * gg;
+    vv = a.b2 * vv + (1.f - a.b2) * gg * gg;
+    const float mh = mm * a.bc1;
+    const float vh = vv * a.bc2;
+    return pp - a.lr * (mh / (sqrtf(vh) + a.eps) + wd * pp);
+  };
+  // 4 consecutive elements from index i
+  auto load_p = [&](size_t i) {
+    if constexpr (NOMASTER) {
+      const u32x2 r = *reinterpret_cast<const u32x2*>(shadow + i);
+      return f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u), __uint_as_float(r[1] << 16),
+                   __uint_as_float(r[1] & 0xffff0000u)};
+    } else {
+      return *reinterpret_cast<const f32x4*>(p + i);
+    }
+  };
+  auto store_p = [&](size_t i, const f32x4& pv) {
+    if constexpr (NOMASTER) {
+      u32x2 r;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        r[h] = (uint32_t)sr_bf16(pv[2 * h], a.sr_seed, a.t, i + 2 * h) |
+               ((uint32_t)sr_bf16(pv[2 * h + 1], a.sr_seed, a.t, i + 2 * h + 1) << 16);
+      *reinterpret_cast<u32x2*>(shadow + i) = r;
+    } else {
+      *reinterpret_cast<f32x4*>(p + i) = pv;
+      if (shadow) {
+        const u32x2 sv = {pack2bf(pv[0], pv[1]), pack2bf(pv[2], pv[3])};
+        *reinterpret_cast<u32x2*>(shadow + i) = sv;
+      }
+    }
+  };
+  // U vectors of 4 per thread and pass: all U x 4 loads are in flight before any arithmetic
+  constexpr int U = 4;
+  const int full = (int)it.len / (ADAM_T * 4 * U) * (ADAM_T * 4 * U);
+  for (int j0 = 0; j0 < full; j0 += ADAM_T * 4 * U) {
+    f32x4 pv[U], gv[U], mv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + j0 + (u * ADAM_T + threadIdx.x) * 4;
+      pv[u] = load_p(i);
+      gv[u] = *reinterpret_cast<const f32x4*>(g + i);
+      mv[u] = *reinterpret_cast<const f32x4*>(m + i);
+      vv[u] = *reinterpret_cast<const f32x4*>(v + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + j0 + (u * ADAM_T + threadIdx.x) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float mm = mv[u][e], vq = vv[u][e];
+        pv[u][e] = upd(pv[u][e], gv[u][e], mm, vq);
+        mv[u][e] = mm;
+        vv[u][e] = vq;
+      }
+      store_p(i, pv[u]);
+      *reinterpret_cast<f32x4*>(m + i) = mv[u];
+      *reinterpret_cast<f32x4*>(v + i) = vv[u];
+    }
+  }
+  for (int j = full + threadIdx.x * 4; j < (int)it.len; j += ADAM_T * 4) {
+    const size_t i = base + j;
+    if (j + 4 <= (int)it.len) {
+      f32x4 pv = load_p(i);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(g + i);
+      f32x4 mv = *reinterpret_cast<const f32x4*>(m + i);
+      f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float mm = mv[e], vq = vv[e];
+        pv[e] = upd(pv[e], gv[e], mm, vq);
+        mv[e] = mm;
+        vv[e] = vq;
+      }
+      store_p(i, pv);
+      *reinterpret_cast<f32x4*>(m + i) = mv;
+      *reinterpret_cast<f32x4*>(v + i) = vv;
+    } else {
+      for (int e = 0; j + e < (int)it.len; ++e) {
+        const size_t k = i + e;
+        float mm = m[k], vv2 = v[k];
+        const float p0 = NOMASTER ? bf2f(shadow[k]) : p[k];
+        const float pp = upd(p0, g[k], mm, vv2);
+        m[k] = mm;
+        v[k] = vv2;
+        if constexpr (NOMASTER) {
+          shadow[k] = sr_bf16(pp, a.sr_seed, a.t, k);
+        } else {
+          p[k] = pp;
+          if (shadow) shadow[k] = f2bf(pp);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float* g, float* m, float* v,
+                        uint16_t* shadow, const float* scale, const double* norm2, AdamArgs a, hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  if (a.no_master) {
+    if (!shadow) return hipErrorInvalidValue;
+    adamw_kernel<true><<<nitems, ADAM_T, 0, s>>>(items, p, g, m, v, shadow, scale, norm2, a);
+  } else {
+    adamw_kernel<false><<<nitems, ADAM_T, 0, s>>>(items, p, g, m, v, shadow, scale, norm2, a);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- init
 
 __global__ __launch_bounds__(256) void init_kernel(const WorkItem* __restrict__ items, float* __restrict__ p,
                                                    uint64_t seed, double std_) {

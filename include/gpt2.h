@@ -66,6 +66,10 @@ typedef struct {
                                       outputs of the two LayerNorms of each layer from their
                                       inputs and saved statistics. Same results up to the bf16
                                       rounding of the recomputed GELU input; less memory. */
+  int32_t no_master;               /* 1: no fp32 master parameters (same post, flag -w 0); the
+                                      bf16 parameters are updated in fp32 and rounded back
+                                      stochastically (seeded SplitMix64 bits, see
+                                      gpt2_adamw_step). GPT2_BF16 only. 0: fp32 master. */
   void* stream;                    /* hipStream_t */
   void* workspace;                 /* device memory, >= gpt2_workspace_bytes(cfg), 256-byte aligned */
   uint64_t workspace_bytes;
@@ -93,7 +97,11 @@ int gpt2_backward(void);
 
 /* AdamW update with t >= 1 (bias correction), decoupled weight decay `wd` on 2-D tensors only,
  * after scaling the gradients by min(1, grad_clip / ||g||) when grad_clip > 0.
- * In GPT2_BF16 mode also rewrites the bf16 parameter copy. If ||g|| is not finite the update is
+ * In GPT2_BF16 mode also rewrites the bf16 parameter copy: rounded to nearest even from the fp32
+ * master, or, with no_master, rounded stochastically: element i (flat layout index) of update t
+ * takes r = the low 16 bits of output number (t << 32 | i) of SplitMix64 seeded with
+ * gpt2_init's seed XOR 0xD1B54A32D192ED03, adds r to the fp32 result's magnitude bits and keeps
+ * the upper 16 (rounds away from zero with probability discarded bits / 2^16). If ||g|| is not finite the update is
  * skipped on the device; gpt2_grad_norm() then returns a non-finite value. Asynchronous. */
 int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t);
 
@@ -110,9 +118,11 @@ int gpt2_skip_update(void);
  * reads such a file into the current model, whose architecture (n_layer, n_head, n_embd, vocab,
  * padded_vocab, max_seq, linear_bias, ln_bias) must match the file's (precision, batch and seq
  * may differ), refreshes the bf16 copies, discards pending gradients, and returns t and the
- * cursor. Continuing from a loaded checkpoint reproduces the uninterrupted run bit for bit.
+ * cursor, and takes over the file's gpt2_init seed (the stream the no_master stochastic rounding
+ * draws from). Continuing from a loaded checkpoint reproduces the uninterrupted run bit for bit.
  * File: the 8 bytes "GPT2CKPT", uint32 version 1, the 8 int32 architecture fields above, uint64
- * N, int32 t, uint64 cursor, then N floats each of parameters, m and v (little-endian).
+ * N, int32 t, uint64 cursor, uint64 seed, then N floats each of parameters, m and v
+ * (little-endian).
  * Synchronous. GPT2_EIO on a file error, a short file or a mismatch. */
 int gpt2_save(const char* path, int32_t t, uint64_t cursor);
 int gpt2_load(const char* path, int32_t* t, uint64_t* cursor);
@@ -145,8 +155,8 @@ float gpt2_grad_norm(void);     /* pre-clip global L2 norm of the last update's 
 int gpt2_last_status(void);     /* status of the most recent call */
 const char* gpt2_last_error(void);
 uint64_t gpt2_num_params(void);
-int gpt2_get_params(float* dst, uint64_t n);      /* fp32 master, layout order */
-int gpt2_set_params(const float* src, uint64_t n); /* also refreshes the bf16 copy */
+int gpt2_get_params(float* dst, uint64_t n);      /* fp32 master (no_master: the bf16 values), layout order */
+int gpt2_set_params(const float* src, uint64_t n); /* also refreshes the bf16 copy (no_master: RNE) */
 int gpt2_get_grads(float* dst, uint64_t n);
 int gpt2_get_adam_state(float* m, float* v, uint64_t n);
 /* Logits [B*T, V] as float (real vocabulary only) of the last gpt2_forward, which must have had

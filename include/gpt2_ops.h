@@ -48,6 +48,13 @@ int gpt2op_gemm_colsum(int dtype, int a_kcontig, int b_kcontig, int epilogue, in
                        const void* aux, int64_t ldaux, void* C2, float* colsum, int colsum_accumulate,
                        float* scratch, uint64_t scratch_floats, void* stream);
 
+/* Stochastic rounding fp32 -> bf16 as the no_master update does it (gpt2.h, gpt2_adamw_step):
+ * y[i] = SR(x[i]) with the random bits of element index0 + i at update t of the stream seeded
+ * with `seed` (the update uses gpt2_init's seed XOR 0xD1B54A32D192ED03). x, y device buffers of
+ * n elements (y: bf16 bits). */
+int gpt2op_stochastic_round(const float* x, uint16_t* y, uint64_t n, uint64_t seed, int32_t t, uint64_t index0,
+                            void* stream);
+
 /* LayerNorm over rows of width C (eps 1e-5, biased variance): y, mean[rows], rstd[rows]. b may be NULL. */
 int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,
                              float* mean, float* rstd, void* stream);

@@ -48,6 +48,7 @@ __all__ = [
     "encoder_forward", "encoder_backward",
     "forward_backward", "forward_logits", "next_token_probs",
     "grad_norm", "clip_scale", "adamw_update", "train", "matmul_nt", "lr_schedule", "OutlierDetector",
+    "splitmix64", "stochastic_round_bf16", "bf16_bits_to_float", "adamw_update_no_master", "SR_SEED_XOR",
     "CFG_TOY", "CFG_124M", "CFG_350M", "CFG_1558M",
 ]
 
@@ -414,6 +415,68 @@ def train(cfg: Config, params, batches, lr, b1, b2, eps, wd, clip=0.0, grad_accu
         losses.append(lsum / grad_accum)
         norms.append(nrm)
     return p, m, v, losses, norms
+
+
+# ----------------------------------------------------------------------------------------
+# Update without an fp32 master copy
+# ----------------------------------------------------------------------------------------
+
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: int) -> int:
+    """Output number n (0-based) of SplitMix64 seeded with `seed` (Steele, Lea & Flood 2014):
+    state_n = seed + (n + 1) * 0x9E3779B97F4A7C15, then the three xor-shift-multiply steps."""
+    z = (seed + (n + 1) * 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+SR_SEED_XOR = 0xD1B54A32D192ED03
+
+
+def _splitmix64_np(seed: int, n: np.ndarray) -> np.ndarray:
+    """splitmix64 for an array of output numbers (uint64 arithmetic wraps mod 2^64)."""
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + (n.astype(np.uint64) + np.uint64(1)) * np.uint64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def stochastic_round_bf16(x, seed: int, t: int, index0: int = 0) -> np.ndarray:
+    """fp32 -> bf16 bits with stochastic rounding ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672",
+    section 参数指南: -w 0 keeps no fp32 master and relies on stochastic rounding).
+
+    Element i takes r = the low 16 bits of SplitMix64 output (t << 32 | (index0 + i)); the
+    magnitude rounds up to the next bf16 value when r + (its 16 discarded bits) >= 2^16, i.e.
+    with probability discarded / 2^16, so the rounding is unbiased. Inf stays inf, NaN stays NaN.
+    """
+    x = np.ascontiguousarray(x, np.float32)
+    u = x.reshape(-1).view(np.uint32).astype(np.uint64)
+    idx = (np.uint64(t) << np.uint64(32)) | (np.uint64(index0) + np.arange(u.size, dtype=np.uint64))
+    r = _splitmix64_np(seed, idx) & np.uint64(0xFFFF)
+    out = ((u + r) >> np.uint64(16)).astype(np.uint16)
+    special = (u & np.uint64(0x7F800000)) == np.uint64(0x7F800000)
+    nan = special & ((u & np.uint64(0x7FFFFF)) != 0)
+    out[special] = (u[special] >> np.uint64(16)).astype(np.uint16)
+    out[nan] |= np.uint16(0x40)
+    return out.reshape(x.shape)
+
+
+def bf16_bits_to_float(b) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def adamw_update_no_master(cfg: Config, params_bf16_bits, grads, m, v, lr, b1, b2, eps, wd, t, seed, clip=0.0):
+    """AdamW on bf16 parameters: the update of adamw_update from the bf16 values, then the result
+    rounded to fp32 and stochastically to bf16 (stream seed XOR SR_SEED_XOR, counters by flat
+    index). Returns (new bf16 bits, m, v, norm, the fp64 updated values before rounding)."""
+    p = bf16_bits_to_float(params_bf16_bits).astype(np.float64)
+    p1, m1, v1, norm = adamw_update(cfg, p, grads, m, v, lr, b1, b2, eps, wd, t, clip)
+    bits = stochastic_round_bf16(p1.astype(np.float32), seed ^ SR_SEED_XOR, t, 0)
+    return bits, m1, v1, norm, p1
 
 
 # ----------------------------------------------------------------------------------------

@@ -52,9 +52,9 @@ def test_header_constants_match_binding():
 
 
 def test_config_struct_layout_matches_header():
-    # 12 int32 + float + int32 (recompute) + 3 pointers/uint64 on x86-64
-    assert ctypes.sizeof(bd.gpt2_config) == 80  # 12 int32 + float + int32 + 3 x 8 bytes
-    assert bd.gpt2_config.stream.offset == 56
+    # 12 int32 + float + 2 int32 (recompute, no_master) + pad + 3 pointers/uint64 on x86-64
+    assert ctypes.sizeof(bd.gpt2_config) == 88
+    assert bd.gpt2_config.stream.offset == 64
 
 
 def _cfg(**kw):
@@ -89,6 +89,8 @@ def test_workspace_planner_host_only(lib):
     (dict(precision=7), "precision"),
     (dict(grad_accum=0), "grad_accum"),
     (dict(recompute=3), "recompute"),
+    (dict(no_master=2), "no_master"),
+    (dict(no_master=1, precision=bd.GPT2_FP32, batch=4), "no_master needs GPT2_BF16"),
 ])
 def test_invalid_configs_rejected_on_host(lib, kw, msg):
     assert bd.gpt2_workspace_bytes(_cfg(**kw)) == 0
@@ -103,6 +105,11 @@ def test_recompute_saves_workspace(lib):
     w0, w1, w2 = (bd.gpt2_workspace_bytes(_cfg(recompute=r)) for r in range(3))
     assert w0 - w1 >= (L - 1) * BT * 4 * C * 2
     assert w1 - w2 >= (2 * L - 1) * BT * C * 2 - 256 * 2 * L
+
+
+def test_no_master_saves_the_fp32_parameters(lib):
+    n = O.num_params(O.CFG_124M)
+    assert bd.gpt2_workspace_bytes(_cfg()) - bd.gpt2_workspace_bytes(_cfg(no_master=1)) >= 4 * n
 
 
 def test_toy_config_accepted(lib):

@@ -15,19 +15,24 @@ pytestmark = pytest.mark.gpu
 WORKER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "workers", "ckpt_worker.py")
 
 
-def worker(*args):
-    r = subprocess.run([sys.executable, "-u", WORKER, *map(str, args)], capture_output=True, text=True, timeout=300)
+def worker(*args, no_master=0):
+    env = dict(os.environ, CKPT_NO_MASTER=str(no_master))
+    r = subprocess.run([sys.executable, "-u", WORKER, *map(str, args)], capture_output=True, text=True, timeout=300,
+                       env=env)
     assert r.returncode == 0, r.stdout + r.stderr
 
 
-def test_resume_is_bitwise_identical(tmp_path):
+@pytest.mark.parametrize("no_master", [0, 1])
+def test_resume_is_bitwise_identical(tmp_path, no_master):
+    """(no_master 1: the stochastic rounding's counters restart from the saved update count, so
+    the resumed run draws the same bits.)"""
     n, k = 7, 3
     straight = tmp_path / "straight.npy"
     resumed = tmp_path / "resumed.npy"
     ckpt = tmp_path / "model.ckpt"
-    worker("straight", n, straight)
-    worker("first", k, n, ckpt)
-    worker("second", n, ckpt, resumed)
+    worker("straight", n, straight, no_master=no_master)
+    worker("first", k, n, ckpt, no_master=no_master)
+    worker("second", n, ckpt, resumed, no_master=no_master)
     a, b = np.load(straight), np.load(resumed)
     assert np.array_equal(a, b)
     la = np.load(str(straight) + ".losses.npy")

@@ -27,9 +27,10 @@ def lib(gpu_lib):
     bd.gpt2_free()
 
 
-def model(cfg, B, T, precision, grad_accum=1, clip=0.0, seed=synth.PARAM_SEED, recompute=0):
+def model(cfg, B, T, precision, grad_accum=1, clip=0.0, seed=synth.PARAM_SEED, recompute=0, no_master=0):
     return bd.Model(cfg.n_layer, cfg.n_head, cfg.n_embd, cfg.vocab, cfg.padded_vocab, cfg.max_seq, B, T,
-                    precision, int(cfg.linear_bias), int(cfg.ln_bias), grad_accum, clip, seed, recompute=recompute)
+                    precision, int(cfg.linear_bias), int(cfg.ln_bias), grad_accum, clip, seed, recompute=recompute,
+                    no_master=no_master)
 
 
 def init_of(cfg, seed=synth.PARAM_SEED):
@@ -198,6 +199,55 @@ def test_bf16_recompute_matches_stored_activations(recompute):
         m1.forward(cuda_i32(tok), cuda_i32(tgt))
         m1.backward()
         assert np.array_equal(m1.grads(), gr)
+
+
+def test_no_master_update_matches_oracle():
+    """bf16 parameters without an fp32 master: one AdamW update from the GPU's own bf16 parameters
+    and gradients against the oracle (fp64 update, then the same stochastic rounding): m and v to
+    fp32 rounding; the new bf16 parameters equal the oracle's except where the fp32 result sits
+    within rounding error of a stochastic-rounding threshold (then they are its neighbour)."""
+    cfg = SMALL
+    B, T = 4, 128
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.95, 1e-8, 0.1
+    m = model(cfg, B, T, bd.GPT2_BF16, clip=1.0, seed=21, no_master=1)
+    p0 = m.params()
+    bits0 = (p0.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bits0.astype(np.uint32) << 16, p0.view(np.uint32))  # parameters are bf16
+    tok, tgt = synth.zipf_batch(cfg.vocab, B, T, 0)
+    m.forward(cuda_i32(tok), cuda_i32(tgt))
+    m.backward()
+    g = m.grads()
+    m.step(lr, b1, b2, eps, wd, 1)
+    p1 = m.params()
+    mm, vv = m.adam_state()
+    want_bits, m_ref, v_ref, _, p_exact = O.adamw_update_no_master(cfg, bits0, g, 0 * g, 0 * g, lr, b1, b2, eps, wd,
+                                                                    1, 21, clip=1.0)
+    assert np.allclose(mm, m_ref, rtol=1e-5, atol=1e-12) and np.allclose(vv, v_ref, rtol=1e-5, atol=1e-18)
+    got_bits = (p1.view(np.uint32) >> 16).astype(np.int64)
+    diff = np.abs(got_bits - want_bits.astype(np.int64))
+    assert diff.max() <= 1
+    assert np.mean(diff == 0) >= 0.999
+    # every parameter moved to one of the two bf16 neighbours of its exact update
+    assert np.all(np.abs(p1.astype(np.float64) - p_exact) <= np.abs(p_exact) * 2.0 ** -7 + 1e-30)
+
+
+def test_no_master_training_is_deterministic_and_tracks_the_master_run():
+    cfg = SMALL
+    B, T = 4, 128
+    runs = []
+    for nm in (1, 1, 0):
+        m = model(cfg, B, T, bd.GPT2_BF16, clip=1.0, no_master=nm)
+        losses = []
+        for s_ in range(5):
+            tok, tgt = synth.zipf_batch(cfg.vocab, B, T, s_)
+            losses.append(m.forward(cuda_i32(tok), cuda_i32(tgt)))
+            m.backward()
+            m.step(1e-3, 0.9, 0.95, 1e-8, 0.1, s_ + 1)
+        runs.append((losses, m.params()))
+    assert runs[0][0] == runs[1][0] and np.array_equal(runs[0][1], runs[1][1])
+    assert runs[0][0][0] == runs[2][0][0]   # same initial bf16 parameters
+    assert np.allclose(runs[0][0], runs[2][0], rtol=2e-2)
+    assert runs[0][0][-1] < runs[0][0][0]
 
 
 def test_skipped_update_discards_the_gradients():

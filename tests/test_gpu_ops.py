@@ -392,6 +392,24 @@ def test_attention_rejects_unsupported_head_size():
                                         stream()) == bd.GPT2_EINVAL
 
 
+# ---------------------------------------------------------------------------- stochastic rounding
+
+@pytest.mark.parametrize("t,index0", [(1, 0), (7, 123457), (40000, (1 << 31) + 5)])
+def test_stochastic_round_matches_oracle_bit_for_bit(t, index0):
+    rng = np.random.default_rng(t)
+    n = 200_003
+    x = (rng.normal(0, 1, n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    x[:6] = [np.inf, -np.inf, 0.0, -0.0, 1.0, 3.0e38]
+    xd = torch.tensor(x, device="cuda")
+    y = torch.empty(n, dtype=torch.int16, device="cuda")
+    seed = 0x1234_5678_9ABC_DEF0
+    assert bd.load().gpt2op_stochastic_round(xd.data_ptr(), y.data_ptr(), n, seed, t, index0, stream()) == 0
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().view(np.uint16)
+    want = O.stochastic_round_bf16(x, seed, t, index0)
+    assert np.array_equal(got, want)
+
+
 # ---------------------------------------------------------------------------- cross-entropy
 
 @pytest.mark.parametrize("dt", DTS)

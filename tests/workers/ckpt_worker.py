@@ -22,8 +22,11 @@ from gpt_transformer_step_train_amd import synth  # noqa: E402
 L, H, C, V, VP, MAXT, B, T = 2, 2, 128, 1000, 1024, 128, 4, 128
 
 
+NO_MASTER = int(os.environ.get("CKPT_NO_MASTER", "0"))  # 1: bf16 parameters, stochastic rounding
+
+
 def make(seed):
-    return bd.Model(L, H, C, V, VP, MAXT, B, T, bd.GPT2_BF16, grad_clip=1.0, seed=seed)
+    return bd.Model(L, H, C, V, VP, MAXT, B, T, bd.GPT2_BF16, grad_clip=1.0, seed=seed, no_master=NO_MASTER)
 
 
 def run(m, first, last, losses):
