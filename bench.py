@@ -68,7 +68,8 @@ def class_work(name, w):
         "bias_grad": BT * C * e,                                      # average row width ~C
         "encoder_bwd": BT * C * e + BT * C * 4 + T * C * 4,
         "grad_norm": N * 4,
-        "adamw": N * (4 * 3 * 2 + 4 + 2),                             # p, m, v rw + g read + bf16 write
+        # p, m, v rw + g read + bf16 write, + the transposed bf16 copies of the matrices
+        "adamw": N * (4 * 3 * 2 + 4 + 2) + (Vp * C + 12 * C * C * L) * e,
         "weight_transpose": (Vp * C + 12 * C * C * L) * e * 2,        # bf16 matrices read + written
     }
     return "hbm", float(bytes_.get(name, 0))

@@ -140,6 +140,23 @@ hipError_t launch_grad_norm_finish(const double* partial, int nparts, double* no
 hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float* g, float* m, float* v,
                         uint16_t* shadow, const float* scale, const double* norm2, AdamArgs a,
                         hipStream_t s);
+// AdamW over ADAM_TR x ADAM_TC tiles of the weight matrices that also have a transposed bf16 copy:
+// the update of launch_adamw, plus the transposed copy written from the same registers through LDS.
+#ifndef ADAM_TR
+#define ADAM_TR 64
+#endif
+#ifndef ADAM_TC
+#define ADAM_TC 64
+#endif
+struct AdamTile {
+  uint64_t off;      // first element of the tile in the flat parameter vector
+  uint64_t dst_off;  // element (c0, r0) of the transposed copy
+  int32_t rows, cols;  // tile extent (<= ADAM_TR, ADAM_TC)
+  int32_t ld, ldd;     // row pitch of the matrix, row pitch of its transposed copy
+};
+hipError_t launch_adamw_tiles(const AdamTile* tiles, int ntiles, float* p, const float* g, float* m, float* v,
+                              uint16_t* shadow, uint16_t* shadow_t, const float* scale, const double* norm2,
+                              AdamArgs a, hipStream_t s);
 hipError_t launch_init_params(const WorkItem* items, int nitems, float* p, uint64_t seed, double std_,
                               hipStream_t s);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t s);

@@ -50,6 +50,12 @@ struct Model {
   uint64_t seed = 0;
   std::vector<LayerOff> lo;
   std::vector<WorkItem> items_host;
+  // bf16 mode: AdamW takes the matrices with transposed copies as tiles (updating the copies in
+  // the same pass) and everything else as flat items
+  std::vector<WorkItem> adam_items_host;
+  std::vector<AdamTile> adam_tiles_host;
+  WorkItem* adam_items = nullptr;
+  AdamTile* adam_tiles = nullptr;
 
   // device pointers inside the workspace
   float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
@@ -179,44 +185,87 @@ size_t layout(const gpt2_config* c, Model* m) {
   return off;
 }
 
-// Work items: tensors cut into runs of <= ITEM_LEN elements; 2-D tensors draw normals.
-std::vector<WorkItem> make_items(const gpt2_config* c) {
-  const size_t C = c->n_embd;
-  std::vector<std::pair<size_t, int>> tensors;  // (size, is2d) in layout order
-  tensors.push_back({(size_t)c->padded_vocab * C, 1});
-  tensors.push_back({(size_t)c->max_seq * C, 1});
+// The tensors in layout order: size, kind (0 LN weight, 1 2-D, 2 bias) and, for the matrices
+// that get a transposed bf16 copy, their rows and columns (else 0).
+struct TensorDesc {
+  size_t size;
+  int kind;
+  int rows, cols;
+};
+std::vector<TensorDesc> tensor_list(const gpt2_config* c) {
+  const int C = c->n_embd;
+  const size_t Cs = C;
+  std::vector<TensorDesc> t;
+  t.push_back({(size_t)c->padded_vocab * Cs, 1, c->padded_vocab, C});
+  t.push_back({(size_t)c->max_seq * Cs, 1, 0, 0});
   for (int l = 0; l < c->n_layer; ++l) {
-    tensors.push_back({C, 0});
-    if (c->ln_bias) tensors.push_back({C, 2});
-    tensors.push_back({3 * C * C, 1});
-    if (c->linear_bias) tensors.push_back({3 * C, 2});
-    tensors.push_back({C * C, 1});
-    if (c->linear_bias) tensors.push_back({C, 2});
-    tensors.push_back({C, 0});
-    if (c->ln_bias) tensors.push_back({C, 2});
-    tensors.push_back({4 * C * C, 1});
-    if (c->linear_bias) tensors.push_back({4 * C, 2});
-    tensors.push_back({4 * C * C, 1});
-    if (c->linear_bias) tensors.push_back({C, 2});
+    t.push_back({Cs, 0, 0, 0});
+    if (c->ln_bias) t.push_back({Cs, 2, 0, 0});
+    t.push_back({3 * Cs * Cs, 1, 3 * C, C});
+    if (c->linear_bias) t.push_back({3 * Cs, 2, 0, 0});
+    t.push_back({Cs * Cs, 1, C, C});
+    if (c->linear_bias) t.push_back({Cs, 2, 0, 0});
+    t.push_back({Cs, 0, 0, 0});
+    if (c->ln_bias) t.push_back({Cs, 2, 0, 0});
+    t.push_back({4 * Cs * Cs, 1, 4 * C, C});
+    if (c->linear_bias) t.push_back({4 * Cs, 2, 0, 0});
+    t.push_back({4 * Cs * Cs, 1, C, 4 * C});
+    if (c->linear_bias) t.push_back({Cs, 2, 0, 0});
   }
-  tensors.push_back({C, 0});
-  if (c->ln_bias) tensors.push_back({C, 2});
+  t.push_back({Cs, 0, 0, 0});
+  if (c->ln_bias) t.push_back({Cs, 2, 0, 0});
+  return t;
+}
+
+// Work items: tensors cut into runs of <= ITEM_LEN elements; 2-D tensors draw normals.
+// skip_transposed: leave out the matrices with a transposed copy (the AdamW tiles cover them).
+std::vector<WorkItem> make_items(const gpt2_config* c, bool skip_transposed = false) {
   std::vector<WorkItem> items;
   size_t off = 0, normal = 0;
-  for (auto& t : tensors) {
-    for (size_t s = 0; s < t.first; s += ITEM_LEN) {
-      WorkItem it{};
-      it.off = off + s;
-      it.len = (uint32_t)std::min<size_t>(ITEM_LEN, t.first - s);
-      it.kind = t.second == 1 ? 1u : 0u;
-      it.normal0 = normal + s;
-      it.init_val = t.second == 0 ? 1.0f : 0.0f;  // LN weights 1, biases 0
-      items.push_back(it);
+  for (const TensorDesc& t : tensor_list(c)) {
+    if (!(skip_transposed && t.rows > 0)) {
+      for (size_t s = 0; s < t.size; s += ITEM_LEN) {
+        WorkItem it{};
+        it.off = off + s;
+        it.len = (uint32_t)std::min<size_t>(ITEM_LEN, t.size - s);
+        it.kind = t.kind == 1 ? 1u : 0u;
+        it.normal0 = normal + s;
+        it.init_val = t.kind == 0 ? 1.0f : 0.0f;  // LN weights 1, biases 0
+        items.push_back(it);
+      }
     }
-    off += t.first;
-    if (t.second == 1) normal += t.first;
+    off += t.size;
+    if (t.kind == 1) normal += t.size;
   }
   return items;
+}
+
+// AdamW tiles of the matrices with a transposed copy. dst offsets are relative to shadow_t; the
+// token embedding's copy ([C, ldl]) starts at wte_off_t.
+std::vector<AdamTile> make_adam_tiles(const gpt2_config* c, size_t wte_off_t, int ldl) {
+  std::vector<AdamTile> tiles;
+  size_t off = 0;
+  bool first = true;
+  for (const TensorDesc& t : tensor_list(c)) {
+    if (t.rows > 0) {
+      const size_t base_t = first ? wte_off_t : off;  // the copy of a layer matrix sits at its offset
+      const int ldd = first ? ldl : t.rows;
+      for (int r0 = 0; r0 < t.rows; r0 += ADAM_TR)
+        for (int c0 = 0; c0 < t.cols; c0 += ADAM_TC) {
+          AdamTile a{};
+          a.off = off + (size_t)r0 * t.cols + c0;
+          a.dst_off = base_t + (size_t)c0 * ldd + r0;
+          a.rows = std::min(ADAM_TR, t.rows - r0);
+          a.cols = std::min(ADAM_TC, t.cols - c0);
+          a.ld = t.cols;
+          a.ldd = ldd;
+          tiles.push_back(a);
+        }
+    }
+    first = false;
+    off += t.size;
+  }
+  return tiles;
 }
 
 // Carve the arena. With base == nullptr only the size is computed.
@@ -247,6 +296,10 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
     M->tr_items = (TransItem*)take((1 + 4 * L) * sizeof(TransItem));
   }
   M->items = (WorkItem*)take(nitems * sizeof(WorkItem));
+  if (c->precision == GPT2_BF16) {
+    M->adam_items = (WorkItem*)take(make_items(c, true).size() * sizeof(WorkItem));
+    M->adam_tiles = (AdamTile*)take(make_adam_tiles(c, 0, (int)ldl).size() * sizeof(AdamTile));
+  }
   M->encoded = take(BT * C * es);
   M->la.resize(L);
   const int rc = c->recompute;
@@ -705,6 +758,12 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed) {
     HIPCHK(hipMemcpyAsync(g.tr_items, g.tr_host.data(), g.tr_host.size() * sizeof(TransItem), hipMemcpyHostToDevice,
                           g.stream));
     HIPCHK(refresh_transposed());
+    g.adam_items_host = make_items(cfg, true);
+    g.adam_tiles_host = make_adam_tiles(cfg, (size_t)(g.wte_t - g.shadow_t), g.ldl);
+    HIPCHK(hipMemcpyAsync(g.adam_items, g.adam_items_host.data(), g.adam_items_host.size() * sizeof(WorkItem),
+                          hipMemcpyHostToDevice, g.stream));
+    HIPCHK(hipMemcpyAsync(g.adam_tiles, g.adam_tiles_host.data(), g.adam_tiles_host.size() * sizeof(AdamTile),
+                          hipMemcpyHostToDevice, g.stream));
   }
   HIPCHK(hipStreamSynchronize(g.stream));
   g.ready = true;
@@ -767,10 +826,16 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
   a.sr_seed = g.seed ^ 0xD1B54A32D192ED03ull;
   {
       ProfScope ps_(GPT2_K_ADAMW);
-      HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale, g.norm2,
-                      a, s));
+      if (g.shadow_t) {  // flat items for the small tensors, tiles (with their transposed copies) for the matrices
+        HIPCHK(launch_adamw(g.adam_items, (int)g.adam_items_host.size(), g.params, g.grads, g.m, g.v, g.shadow,
+                            g.clip_scale, g.norm2, a, s));
+        HIPCHK(launch_adamw_tiles(g.adam_tiles, (int)g.adam_tiles_host.size(), g.params, g.grads, g.m, g.v, g.shadow,
+                                  g.shadow_t, g.clip_scale, g.norm2, a, s));
+      } else {
+        HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale,
+                            g.norm2, a, s));
+      }
     }
-  HIPCHK(refresh_transposed());
   g.micro = 0;
   return ok();
 }

@@ -235,6 +235,118 @@ hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float
   return hipGetLastError();
 }
 
+// ADAM_TR x ADAM_TC tiles of the transposed matrices (decay on: they are all 2-D). With TPR =
+// ADAM_TC / 4 threads per row, thread t owns columns 4 (t % TPR) .. +3 of rows t / TPR + RPP k
+// (RPP = 256 / TPR rows per pass), so every row segment is read and written as 16-byte vectors;
+// the new bf16 values also go to LDS transposed, and come out as 16-byte rows of the transposed
+// copy.
+template <bool NOMASTER>
+__global__ __launch_bounds__(256) void adamw_tile_kernel(const AdamTile* __restrict__ tiles, float* __restrict__ p,
+                                                         const float* __restrict__ g, float* __restrict__ m,
+                                                         float* __restrict__ v, uint16_t* __restrict__ shadow,
+                                                         uint16_t* __restrict__ shadow_t,
+                                                         const float* __restrict__ scale_p,
+                                                         const double* __restrict__ norm2_p, AdamArgs a) {
+  constexpr int TR = ADAM_TR, TC = ADAM_TC, TPR = TC / 4, RPP = 256 / TPR, NP = TR / RPP;
+  static_assert(TC % 4 == 0 && 256 % TPR == 0 && TR % RPP == 0 && TR % 8 == 0, "AdamW tile shape");
+  constexpr int P = TR + 8;  // LDS pitch (bf16 elements) of the transposed tile
+  __shared__ __attribute__((aligned(16))) uint16_t tt[TC * P];
+  const double n2 = *norm2_p;
+  if (!(n2 <= 1.0e300)) return;
+  const AdamTile T = tiles[blockIdx.x];
+  const float sc = *scale_p;
+  const int cq = threadIdx.x % TPR, rg = threadIdx.x / TPR;
+  const bool full = T.rows == TR && T.cols == TC;
+  auto upd = [&](float pp, float gg, float& mm, float& vv) {
+    gg *= sc;
+    mm = a.b1 * mm + (1.f - a.b1) * gg;
+    vv = a.b2 * vv + (1.f - a.b2) * gg * gg;
+    const float mh = mm * a.bc1;
+    const float vh = vv * a.bc2;
+    return pp - a.lr * (mh / (sqrtf(vh) + a.eps) + a.wd * pp);
+  };
+  if (full) {
+    f32x4 pv[NP], gv[NP], mv[NP], vv[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const size_t i = T.off + (size_t)(rg + RPP * k) * T.ld + 4 * cq;
+      if constexpr (NOMASTER) {
+        const u32x2 r = *reinterpret_cast<const u32x2*>(shadow + i);
+        pv[k] = f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                      __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
+      } else {
+        pv[k] = *reinterpret_cast<const f32x4*>(p + i);
+      }
+      gv[k] = *reinterpret_cast<const f32x4*>(g + i);
+      mv[k] = *reinterpret_cast<const f32x4*>(m + i);
+      vv[k] = *reinterpret_cast<const f32x4*>(v + i);
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int r = rg + RPP * k;
+      const size_t i = T.off + (size_t)r * T.ld + 4 * cq;
+      uint16_t b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float mm = mv[k][e], vq = vv[k][e];
+        pv[k][e] = upd(pv[k][e], gv[k][e], mm, vq);
+        mv[k][e] = mm;
+        vv[k][e] = vq;
+        b[e] = NOMASTER ? sr_bf16(pv[k][e], a.sr_seed, a.t, i + e) : f2bf(pv[k][e]);
+      }
+      if constexpr (!NOMASTER) *reinterpret_cast<f32x4*>(p + i) = pv[k];
+      *reinterpret_cast<f32x4*>(m + i) = mv[k];
+      *reinterpret_cast<f32x4*>(v + i) = vv[k];
+      const u32x2 sv = {(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+      *reinterpret_cast<u32x2*>(shadow + i) = sv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tt[(4 * cq + e) * P + r] = b[e];
+    }
+  } else {
+    for (int k = 0; k < NP; ++k) {
+      const int r = rg + RPP * k;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * cq + e;
+        if (r >= T.rows || c >= T.cols) continue;
+        const size_t i = T.off + (size_t)r * T.ld + c;
+        float mm = m[i], vq = v[i];
+        const float p0 = NOMASTER ? bf2f(shadow[i]) : p[i];
+        const float pn = upd(p0, g[i], mm, vq);
+        m[i] = mm;
+        v[i] = vq;
+        const uint16_t b = NOMASTER ? sr_bf16(pn, a.sr_seed, a.t, i) : f2bf(pn);
+        if constexpr (!NOMASTER) p[i] = pn;
+        shadow[i] = b;
+        tt[c * P + r] = b;
+      }
+    }
+  }
+  __syncthreads();
+  // row c of the transposed copy: rows r0 .. r0 + rows - 1 of the tile, 8 at a time
+  for (int w = threadIdx.x; w < TC * (TR / 8); w += 256) {
+    const int c = w / (TR / 8), r = (w % (TR / 8)) * 8;
+    if (c >= T.cols || r >= T.rows) continue;
+    uint16_t* out = shadow_t + T.dst_off + (size_t)c * T.ldd + r;
+    if (full) {
+      *reinterpret_cast<u32x4*>(out) = *reinterpret_cast<const u32x4*>(tt + c * P + r);
+    } else {
+      for (int e = 0; e < 8 && r + e < T.rows; ++e) out[e] = tt[c * P + r + e];
+    }
+  }
+}
+
+hipError_t launch_adamw_tiles(const AdamTile* tiles, int ntiles, float* p, const float* g, float* m, float* v,
+                              uint16_t* shadow, uint16_t* shadow_t, const float* scale, const double* norm2,
+                              AdamArgs a, hipStream_t s) {
+  if (ntiles <= 0) return hipSuccess;
+  if (a.no_master)
+    adamw_tile_kernel<true><<<ntiles, 256, 0, s>>>(tiles, p, g, m, v, shadow, shadow_t, scale, norm2, a);
+  else
+    adamw_tile_kernel<false><<<ntiles, 256, 0, s>>>(tiles, p, g, m, v, shadow, shadow_t, scale, norm2, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- init
 
 __global__ __launch_bounds__(256) void init_kernel(const WorkItem* __restrict__ items, float* __restrict__ p,
