@@ -28,7 +28,10 @@ gradient (this bounds memory, it does not change the result beyond rounding orde
 Pins (tests/test_oracle_*.py): HF transformers GPT2LMHeadModel + torch autograd in fp64
 (forward logits and every gradient), central finite differences, torch's layer_norm / gelu /
 scaled_dot_product_attention / cross_entropy / AdamW / clip_grad_norm_, parameter counts
-printed on the pages, causality, probabilities summing to one, the BabyGPT loss floor.
+printed on the pages, causality, probabilities summing to one, the BabyGPT loss floor; the
+learning-rate schedule against the lr column printed on the pages and its closed forms
+(tests/test_host_helpers.py); the stochastic rounding against the properties that define it and
+its generator against an independent implementation (tests/test_oracle_stochastic_rounding.py).
 """
 from __future__ import annotations
 
