@@ -238,7 +238,7 @@ KERNEL_CLASSES = ["encoder_fwd", "layernorm_fwd", "gemm_qkv", "attention_fwd", "
                   "layernorm_bwd", "gemm_fcproj_dx", "gemm_fcproj_dw", "bias_grad", "gemm_fc_dx", "gemm_fc_dw",
                   "gemm_attproj_dx", "gemm_attproj_dw", "attention_bwd", "gemm_qkv_dx", "gemm_qkv_dw",
                   "encoder_bwd", "grad_norm", "adamw", "attention_bwd_q", "attention_bwd_pre",
-                  "weight_transpose", "recompute"]
+                  "weight_transpose", "recompute", "grad_finish"]
 
 
 def gpt2_profile_enable(mask):

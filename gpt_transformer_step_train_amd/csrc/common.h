@@ -196,25 +196,29 @@ __device__ __forceinline__ void gelu_both(float x, float& g, float& dg) {
 __host__ __device__ constexpr int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // out[c] (+)= sum_{y < ny} part[y * ld + c] for c < ncols, summed in a fixed order.
-// Block of 1024 threads handles 32 columns: 32 row-groups stride over y (8 independent loads in
-// flight per thread), then the 32 group sums of a column are added in order. Grid: cdiv(ncols, 32).
+// Block of 1024 threads handles 32 columns: 32 row-groups stride over y, each thread issuing the
+// loads of 16 rows (y, y + 32, ...) before adding any of them, so that up to 512 rows cost one
+// memory round trip; then the 32 group sums of a column are added in order. Columns
+// [32 chunk, 32 chunk + 32).
 constexpr int RP_THREADS = 1024;
 __device__ __forceinline__ void reduce_partials_block(const float* __restrict__ part, int ny, long ld, int ncols,
-                                                      float* __restrict__ out, int accumulate) {
+                                                      float* __restrict__ out, int accumulate, int chunk) {
+  constexpr int U = 16;
   __shared__ float sh[32][33];
   const int cl = threadIdx.x & 31, yg = threadIdx.x >> 5;
-  const int c = blockIdx.x * 32 + cl;
+  const int c = chunk * 32 + cl;
   float s = 0.f;
   if (c < ncols) {
-    int y = yg;
-    for (; y + 7 * 32 < ny; y += 8 * 32) {
-      float v[8];
+    for (int y0 = yg; y0 < ny; y0 += U * 32) {
+      float v[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(y + u * 32) * ld + c];
+      for (int u = 0; u < U; ++u) {
+        const int y = y0 + u * 32;
+        v[u] = y < ny ? part[(size_t)y * ld + c] : 0.f;
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < U; ++u) s += v[u];
     }
-    for (; y < ny; y += 32) s += part[(size_t)y * ld + c];
   }
   sh[yg][cl] = s;
   __syncthreads();

@@ -841,12 +841,26 @@ __global__ __launch_bounds__(256) void colsum_partial(const T* __restrict__ x, l
 
 __global__ __launch_bounds__(RP_THREADS) void colsum_finish(const float* __restrict__ partial, int ny, int N,
                                                      float* __restrict__ out, int accumulate) {
-  reduce_partials_block(partial, ny, N, N, out, accumulate);
+  reduce_partials_block(partial, ny, N, N, out, accumulate, blockIdx.x);
 }
 
 hipError_t launch_colsum_finish(const float* partial, int ny, int N, float* out, int accumulate, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   colsum_finish<<<cdiv(N, 32), RP_THREADS, 0, s>>>(partial, ny, N, out, accumulate);
+  return hipGetLastError();
+}
+
+int gemm_colsum_rows_max(int M) { return std::max(cdiv(M, 128) * 2, cdiv(M, 256) * 4); }
+
+// The second stages of many column sums in one launch: block b takes FinishBlock b.
+__global__ __launch_bounds__(RP_THREADS) void finish_batch(const FinishBlock* __restrict__ blocks, int accumulate) {
+  const FinishBlock f = blocks[blockIdx.x];
+  reduce_partials_block(f.part, f.ny, f.ld, f.ncols, f.out, accumulate, f.chunk);
+}
+
+hipError_t launch_finish_batch(const FinishBlock* blocks, int nblocks, int accumulate, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  finish_batch<<<nblocks, RP_THREADS, 0, s>>>(blocks, accumulate);
   return hipGetLastError();
 }
 
@@ -937,9 +951,13 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
   // otherwise a separate pass over the stored C
   using CF = Cfg<T, BM, BN, AKC, BKC>;
   const int cs_rows = cdiv(a.M, BM) * CF::WGM;
-  const bool cs_fused = epi != EPI_F32 && a.colsum && 64 % (CF::TN / 8) == 0 && scratch &&
-                        (size_t)cs_rows * a.N <= scratch_floats;
-  float* csp = cs_fused ? scratch : nullptr;
+  const bool cs_ok = epi != EPI_F32 && a.colsum && 64 % (CF::TN / 8) == 0;
+  // partials left for a batched finish when the caller offers room for them
+  ColsumDefer* dfr = a.colsum_defer;
+  if (dfr) dfr->rows = 0;
+  const bool cs_defer = cs_ok && dfr && (size_t)cs_rows * a.N <= dfr->cap;
+  const bool cs_fused = cs_ok && (cs_defer || (scratch && (size_t)cs_rows * a.N <= scratch_floats));
+  float* csp = cs_defer ? dfr->part : cs_fused ? scratch : nullptr;
   switch (epi) {
     case EPI_BIAS: launch_cfg<T, BM, BN, AKC, BKC, EPI_BIAS>(grid, a, k_split, csp, s); break;
     case EPI_GELU: launch_cfg<T, BM, BN, AKC, BKC, EPI_GELU>(grid, a, k_split, csp, s); break;
@@ -956,7 +974,9 @@ static hipError_t launch_t(Epi epi, const GemmArgs& a, float* scratch, size_t sc
       }
       break;
   }
-  if (epi != EPI_F32 && a.colsum) {
+  if (cs_defer) {
+    dfr->rows = cs_rows;
+  } else if (epi != EPI_F32 && a.colsum) {
     if (cs_fused)
       colsum_finish<<<cdiv(a.N, 32), RP_THREADS, 0, s>>>(scratch, cs_rows, a.N, a.colsum, a.colsum_accumulate);
     else

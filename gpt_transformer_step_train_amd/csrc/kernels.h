@@ -8,6 +8,27 @@ namespace g2 {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
+// Column sums taken in two stages (per-block partial rows, then a fixed-order sum over them) may
+// leave their second stage for later: a launcher given a ColsumDefer writes its partial rows into
+// [part, part + cap) floats and sets `rows` to their number (0: it finished the sums itself, as
+// without a ColsumDefer). The caller then lists FinishBlocks for one batched launch.
+struct ColsumDefer {
+  float* part;
+  size_t cap;
+  int rows;
+};
+// One block of the batched second stage:
+//   out[32 chunk + c] (+)= sum_{y < ny} part[y ld + 32 chunk + c],  c < 32, 32 chunk + c < ncols
+struct FinishBlock {
+  const float* part;
+  float* out;
+  long ld;
+  int ny, ncols, chunk, pad;
+};
+// All blocks' sums in one launch (accumulate: add to out instead of storing). Two blocks must not
+// share an output column.
+hipError_t launch_finish_batch(const FinishBlock* blocks, int nblocks, int accumulate, hipStream_t s);
+
 // GEMM  C[M,N] = sum_k A(m,k) * B(n,k)
 //   A(m,k) = A[m*lda + k] when a_kc (K-contiguous) else A[k*lda + m]
 //   B(n,k) = B[n*ldb + k] when b_kc (K-contiguous) else B[k*ldb + n]
@@ -38,6 +59,7 @@ struct GemmArgs {
   // gradient of a layer whose input gradient this product writes); partials go through scratch
   float* colsum;
   int colsum_accumulate;
+  ColsumDefer* colsum_defer;  // when set, the column-sum partials may be left for a batched finish
 };
 
 // split-K: for EPI_F32 only; `scratch` must hold splits*M*N floats (nullptr => no split).
@@ -54,6 +76,8 @@ int gemm_splits(int M, int N, int K, size_t scratch_floats);
 
 // out[n] (+)= sum_{y < ny} partial[y * N + n], summed in a fixed order
 hipError_t launch_colsum_finish(const float* partial, int ny, int N, float* out, int accumulate, hipStream_t s);
+// Upper bound of the fused column-sum partials of an M-row product: rows * N floats.
+int gemm_colsum_rows_max(int M);
 // db[n] (+)= sum_m dY[m*ld + n]; deterministic, two stages through `partial` (rows_split*N floats)
 hipError_t launch_colsum(DType dt, const void* dY, long ld, int M, int N, float* db, int accumulate,
                          float* partial, size_t partial_floats, hipStream_t s);
@@ -65,7 +89,9 @@ hipError_t launch_layernorm_fwd(DType dt, int rows, int C, const void* x, const 
 // dsum (may be null): column sums of the updated dres rows (= or += per accumulate)
 hipError_t launch_layernorm_bwd(DType dt, int rows, int C, const void* dy, const void* x, const void* w,
                                 const float* mean, const float* rstd, void* dres, int add, float* dw, float* db,
-                                float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s);
+                                float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s,
+                                ColsumDefer* defer = nullptr);
+// partial floats of one backward; with a ColsumDefer the partial rows are [rows][3][C] (dw, db, dsum)
 size_t layernorm_bwd_partial_floats(int rows, int C);
 
 // Encoder

@@ -6,7 +6,8 @@
 //   y = (x - mu) * rstd * w + b,   rstd = 1/sqrt(var + eps)
 //   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)),  g = dy * w
 //   dw = sum_rows dy * xhat,  db = sum_rows dy
-// One wave64 owns a row; 16-byte loads; row statistics with DPP reductions (fp32).
+// A row belongs to one wave64 or to one half-wave (whichever idles fewer lanes); 16-byte loads; row
+// statistics with DPP reductions (fp32).
 // Weight/bias gradients: per-block column partials in registers, then a fixed-order sum.
 #include "common.h"
 #include "kernels.h"
@@ -15,14 +16,28 @@ namespace g2 {
 
 constexpr float LN_EPS = 1e-5f;
 
-template <typename T, int NV>
+// Sum over the L lanes that share a row (L = 64: the whole wave, in wave_sum's order; L = 32:
+// each half-wave, every lane receiving its own half's sum).
+template <int L> __device__ __forceinline__ float row_sum(float v) {
+  if constexpr (L == 64) {
+    return wave_sum(v);
+  } else {
+    v = row16_sum(v);
+    const float lo = readlane(v, 0) + readlane(v, 16), hi = readlane(v, 32) + readlane(v, 48);
+    return (threadIdx.x & 32) ? hi : lo;
+  }
+}
+
+// L lanes per row (64, or 32 when that leaves fewer lanes idle: a wave then takes two rows at
+// once), NV 16-byte vectors per lane.
+template <typename T, int NV, int L>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* __restrict__ x,
                                                      const T* __restrict__ w, const T* __restrict__ b,
                                                      T* __restrict__ y, float* __restrict__ mean,
                                                      float* __restrict__ rstd) {
   constexpr int VEC = Elt<T>::VEC;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (256 / L) + (int)threadIdx.x / L;
+  const int li = threadIdx.x & (L - 1);
   if (row >= rows) return;
   const int nvec = C / VEC;
   const T* xr = x + (size_t)row * C;
@@ -30,7 +45,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
   u32x4 xraw[NV], wraw[NV], braw[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = lane + 64 * j;
+    const int v = li + L * j;
     if (v < nvec) {
       xraw[j] = *reinterpret_cast<const u32x4*>(xr + v * VEC);
       wraw[j] = *reinterpret_cast<const u32x4*>(w + v * VEC);
@@ -41,18 +56,18 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = lane + 64 * j;
+    const int v = li + L * j;
     if (v < nvec) {
       xv[j].unpack(xraw[j]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s += xv[j].v[e];
     }
   }
-  const float mu = wave_sum(s) / (float)C;
+  const float mu = row_sum<L>(s) / (float)C;
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = lane + 64 * j;
+    const int v = li + L * j;
     if (v < nvec) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -61,12 +76,12 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
       }
     }
   }
-  const float var = wave_sum(ss) / (float)C;
+  const float var = row_sum<L>(ss) / (float)C;
   const float rs = 1.0f / sqrtf(var + LN_EPS);
   T* yr = y + (size_t)row * C;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = lane + 64 * j;
+    const int v = li + L * j;
     if (v < nvec) {
       V16<T> wv, bv, o;
       wv.unpack(wraw[j]);
@@ -76,33 +91,30 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
       o.store(yr + v * VEC);
     }
   }
-  if (lane == 0) {
+  if (li == 0) {
     mean[row] = mu;
     rstd[row] = rs;
   }
 }
 
-constexpr int LNB_BLOCKS = 512;
-
-// Raw (packed) inputs of one row of the backward, held in registers so that the loads of the next
-// row are in flight while this one is processed.
-template <typename T, int NV> struct LnRow {
-  u32x4 dy[NV], x[NV], dr[NV];
-  float mu, rs;
-};
+// Backward grid: at most LNB_BLOCKS blocks, each taking cdiv(rows, LNB_BLOCKS) consecutive rows, of
+// 8 waves (4 when a lane holds more than two 16-byte vectors of a row: one wave per SIMD then
+// keeps the wider rows' registers without spills).
+constexpr int LNB_BLOCKS = 256;
 
 // dx of every row (into dres: = or += dx), and per-block column partials of
 //   dw = sum dy * xhat,  db = sum dy,  and (when dsum) the sum of the updated dres rows
 // (the bias gradient of the linear layer whose output feeds this residual stream).
-// Block = 4 waves; wave wv takes rows r0 + wv, r0 + wv + 4, ...; partial layout [block][3][C].
-template <typename T, int NV, bool PF>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_per_block,
-                                                     const T* __restrict__ dy, const T* __restrict__ x,
-                                                     const T* __restrict__ w, const float* __restrict__ mean,
-                                                     const float* __restrict__ rstd, T* __restrict__ dres,
-                                                     int add, int dsum, float* __restrict__ partial) {
+// Block = NW waves, one row per wave at a time: wave wv takes rows r0 + wv, r0 + wv + NW, ...;
+// the waves' column partials are added in wave order through LDS; partial layout [block][3][C].
+template <typename T, int NV, int NW>
+__global__ __launch_bounds__(64 * NW) void ln_bwd_kernel(int rows, int C, int rows_per_block,
+                                                         const T* __restrict__ dy, const T* __restrict__ x,
+                                                         const T* __restrict__ w, const float* __restrict__ mean,
+                                                         const float* __restrict__ rstd, T* __restrict__ dres,
+                                                         int add, int dsum, float* __restrict__ partial) {
   constexpr int VEC = Elt<T>::VEC;
-  extern __shared__ float red[];  // [4][C]
+  extern __shared__ float red[];  // [NW][C]
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nvec = C / VEC;
@@ -122,33 +134,32 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_p
       acc[0][j][e] = acc[1][j][e] = acc[2][j][e] = 0.f;
     }
   }
-  auto load_row = [&](int row, LnRow<T, NV>& d) {
+  for (int row = r0 + wv; row < r1; row += NW) {
+    // the row's dy, x and dres, all requested before the first use
+    u32x4 dyr[NV], xr[NV], drr[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int v = lane + 64 * j;
       if (v < nvec) {
         const size_t o = (size_t)row * C + v * VEC;
-        d.dy[j] = *reinterpret_cast<const u32x4*>(dy + o);
-        d.x[j] = *reinterpret_cast<const u32x4*>(x + o);
-        if (add) d.dr[j] = *reinterpret_cast<const u32x4*>(dres + o);
+        dyr[j] = *reinterpret_cast<const u32x4*>(dy + o);
+        xr[j] = *reinterpret_cast<const u32x4*>(x + o);
+        if (add) drr[j] = *reinterpret_cast<const u32x4*>(dres + o);
       }
     }
-    d.mu = mean[row];
-    d.rs = rstd[row];
-  };
-  auto process = [&](int row, const LnRow<T, NV>& d) {
+    const float mu = mean[row], rs = rstd[row];
     float dyf[NV][VEC], xh[NV][VEC];
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       if (lane + 64 * j < nvec) {
-        V16<T> a, b;
-        a.unpack(d.dy[j]);
-        b.unpack(d.x[j]);
+        V16<T> a, bx;
+        a.unpack(dyr[j]);
+        bx.unpack(xr[j]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           dyf[j][e] = a.v[e];
-          xh[j][e] = (b.v[e] - d.mu) * d.rs;
+          xh[j][e] = (bx.v[e] - mu) * rs;
           const float g = a.v[e] * wf[j][e];
           sg += g;
           sgx += g * xh[j][e];
@@ -164,35 +175,19 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_p
       const int v = lane + 64 * j;
       if (v < nvec) {
         V16<T> o;
-        if (add) o.unpack(d.dr[j]);
+        if (add) o.unpack(drr[j]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float dx = d.rs * (dyf[j][e] * wf[j][e] - mg - xh[j][e] * mgx);
+          const float dx = rs * (dyf[j][e] * wf[j][e] - mg - xh[j][e] * mgx);
           o.v[e] = add ? o.v[e] + dx : dx;
           acc[2][j][e] += o.v[e];
         }
         o.store(dres + (size_t)row * C + v * VEC);
       }
     }
-  };
-  int row = r0 + wv;
-  if constexpr (PF) {
-    LnRow<T, NV> cur, nxt;
-    if (row < r1) load_row(row, cur);
-    for (; row < r1; row += 4) {
-      if (row + 4 < r1) load_row(row + 4, nxt);
-      process(row, cur);
-      cur = nxt;
-    }
-  } else {
-    for (; row < r1; row += 4) {
-      LnRow<T, NV> cur;
-      load_row(row, cur);
-      process(row, cur);
-    }
   }
-  // combine the 4 waves' column partials in LDS, one quantity at a time, and write this
-  // block's partial rows
+  // combine the waves' column partials in LDS, one quantity at a time, and write this block's
+  // partial rows
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     if (q == 2 && !dsum) break;
@@ -205,8 +200,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int C, int rows_p
       }
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < C; c += 256) {
-      const float sum = (red[c] + red[C + c]) + (red[2 * C + c] + red[3 * C + c]);
+    for (int c = threadIdx.x; c < C; c += 64 * NW) {
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) sum += red[k * C + c];
       partial[((size_t)blockIdx.x * 3 + q) * C + c] = sum;
     }
     __syncthreads();
@@ -219,26 +216,50 @@ __global__ __launch_bounds__(RP_THREADS) void ln_bwd_finish(const float* __restr
                                                      float* __restrict__ dsum, int accumulate) {
   float* out = blockIdx.y == 0 ? dw : blockIdx.y == 1 ? db : dsum;
   if (!out) return;
-  reduce_partials_block(partial + (size_t)blockIdx.y * C, nblocks, 3L * C, C, out, accumulate);
+  reduce_partials_block(partial + (size_t)blockIdx.y * C, nblocks, 3L * C, C, out, accumulate, blockIdx.x);
 }
 
 size_t layernorm_bwd_partial_floats(int rows, int C) { return (size_t)LNB_BLOCKS * 3 * C; }
+// blocks of the backward (at most LNB_BLOCKS, each taking cdiv(rows, LNB_BLOCKS) rows)
+static int ln_bwd_blocks(int rows) { return rows > 0 ? cdiv(rows, cdiv(rows, LNB_BLOCKS)) : 0; }
+
+// Lanes per row of the forward: 32 when the row's 16-byte vectors leave an odd number of
+// half-waves (then a full wave would idle half its lanes on the last vector) and that fits 8
+// vectors per lane; else 64. Returns the vectors per lane in *nv. (The backward keeps 64: with
+// two rows per wave it measured slower at C = 768, bf16.)
+static int ln_fwd_lanes(int nvec, int* nv) {
+  const int h = cdiv(nvec, 32);
+  if ((h & 1) && h <= 8) {
+    *nv = h;
+    return 32;
+  }
+  *nv = cdiv(nvec, 64);
+  return 64;
+}
 
 template <typename T>
 static hipError_t ln_fwd_t(int rows, int C, const void* x, const void* w, const void* b, void* y, float* mean,
                            float* rstd, hipStream_t s) {
   constexpr int VEC = Elt<T>::VEC;
-  const int nv = cdiv(C / VEC, 64);
-  dim3 grid(cdiv(rows, 4));
+  int nv;
+  const int L = ln_fwd_lanes(C / VEC, &nv);
+  dim3 grid(cdiv(rows, 256 / L));
   auto X = reinterpret_cast<const T*>(x);
   auto W = reinterpret_cast<const T*>(w);
   auto Bb = reinterpret_cast<const T*>(b);
   auto Y = reinterpret_cast<T*>(y);
-  if (nv <= 1) ln_fwd_kernel<T, 1><<<grid, 256, 0, s>>>(rows, C, X, W, Bb, Y, mean, rstd);
-  else if (nv <= 2) ln_fwd_kernel<T, 2><<<grid, 256, 0, s>>>(rows, C, X, W, Bb, Y, mean, rstd);
-  else if (nv <= 4) ln_fwd_kernel<T, 4><<<grid, 256, 0, s>>>(rows, C, X, W, Bb, Y, mean, rstd);
-  else if (nv <= 8) ln_fwd_kernel<T, 8><<<grid, 256, 0, s>>>(rows, C, X, W, Bb, Y, mean, rstd);
+#define LNF(n, l) ln_fwd_kernel<T, n, l><<<grid, 256, 0, s>>>(rows, C, X, W, Bb, Y, mean, rstd)
+  if (L == 32) {
+    if (nv == 1) LNF(1, 32);
+    else if (nv == 3) LNF(3, 32);
+    else if (nv == 5) LNF(5, 32);
+    else LNF(7, 32);
+  } else if (nv <= 1) LNF(1, 64);
+  else if (nv <= 2) LNF(2, 64);
+  else if (nv <= 4) LNF(4, 64);
+  else if (nv <= 8) LNF(8, 64);
   else return hipErrorInvalidValue;
+#undef LNF
   return hipGetLastError();
 }
 
@@ -252,38 +273,51 @@ hipError_t launch_layernorm_fwd(DType dt, int rows, int C, const void* x, const 
 template <typename T>
 static hipError_t ln_bwd_t(int rows, int C, const void* dy, const void* x, const void* w, const float* mean,
                            const float* rstd, void* dres, int add, float* dw, float* db, float* dsum,
-                           int accumulate, float* partial, hipStream_t s) {
+                           int accumulate, float* partial, hipStream_t s, bool finish) {
   constexpr int VEC = Elt<T>::VEC;
   const int nv = cdiv(C / VEC, 64);
   const int rpb = cdiv(rows, LNB_BLOCKS);
-  const int nb = rows > 0 ? cdiv(rows, rpb) : 0;
-  const size_t shm = (size_t)4 * C * sizeof(float);
+  const int nb = ln_bwd_blocks(rows);
   auto DY = reinterpret_cast<const T*>(dy);
   auto X = reinterpret_cast<const T*>(x);
   auto W = reinterpret_cast<const T*>(w);
   auto DR = reinterpret_cast<T*>(dres);
   const int ds = dsum != nullptr;
   if (nb > 0) {
-#define LNB(n, pf) ln_bwd_kernel<T, n, pf><<<nb, 256, shm, s>>>(rows, C, rpb, DY, X, W, mean, rstd, DR, add, ds, partial)
-    if (nv <= 1) LNB(1, true);
-    else if (nv <= 2) LNB(2, true);
-    else if (nv <= 4) LNB(4, false);
-    else if (nv <= 8) LNB(8, false);
+#define LNB(n, nw)                                                                                      \
+  ln_bwd_kernel<T, n, nw><<<nb, 64 * nw, (size_t)nw * C * sizeof(float), s>>>(rows, C, rpb, DY, X, W, mean, \
+                                                                              rstd, DR, add, ds, partial)
+    if (nv <= 1) LNB(1, 8);
+    else if (nv <= 2) LNB(2, 8);
+    else if (nv <= 4) LNB(4, 4);
+    else if (nv <= 8) LNB(8, 4);
     else return hipErrorInvalidValue;
 #undef LNB
   }
-  ln_bwd_finish<<<dim3(cdiv(C, 32), 3), RP_THREADS, 0, s>>>(partial, nb, C, dw, db, dsum, accumulate);
+  if (finish) ln_bwd_finish<<<dim3(cdiv(C, 32), 3), RP_THREADS, 0, s>>>(partial, nb, C, dw, db, dsum, accumulate);
   return hipGetLastError();
 }
 
 hipError_t launch_layernorm_bwd(DType dt, int rows, int C, const void* dy, const void* x, const void* w,
                                 const float* mean, const float* rstd, void* dres, int add, float* dw, float* db,
-                                float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s) {
-  if ((size_t)LNB_BLOCKS * 3 * C > partial_floats) return hipErrorInvalidValue;
+                                float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s,
+                                ColsumDefer* defer) {
+  const size_t pf = layernorm_bwd_partial_floats(rows, C);
   if ((size_t)4 * C * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
+  // partials left for a batched finish when the caller offers room for them
+  bool finish = true;
+  if (defer) {
+    defer->rows = 0;
+    if (rows > 0 && pf <= defer->cap) {
+      partial = defer->part;
+      finish = false;
+      defer->rows = ln_bwd_blocks(rows);
+    }
+  }
+  if (finish && pf > partial_floats) return hipErrorInvalidValue;
   return dt == DT_BF16
-             ? ln_bwd_t<bf16>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, dsum, accumulate, partial, s)
-             : ln_bwd_t<float>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, dsum, accumulate, partial, s);
+             ? ln_bwd_t<bf16>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, dsum, accumulate, partial, s, finish)
+             : ln_bwd_t<float>(rows, C, dy, x, w, mean, rstd, dres, add, dw, db, dsum, accumulate, partial, s, finish);
 }
 
 }  // namespace g2

@@ -79,6 +79,15 @@ struct Model {
   uint32_t* keys = nullptr;
   float* scratch = nullptr;
   size_t scratch_floats = 0;
+  // column-sum partials of the backward (LayerNorm weight / bias gradients, linear-layer bias
+  // gradients) whose second stage runs once, batched, at the end of the backward: the region they
+  // are written to, the device table of the batched launch, and the host lists (this backward's
+  // and the one in the device table)
+  float* defer = nullptr;
+  size_t defer_floats = 0, defer_used = 0;
+  FinishBlock* fin_dev = nullptr;
+  size_t fin_cap = 0;
+  std::vector<FinishBlock> fin_host, fin_up;
   double* norm_partial = nullptr;
   double* norm2 = nullptr;
   float* clip_scale = nullptr;
@@ -337,6 +346,15 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
   sf = std::max<size_t>(sf, (size_t)512 * 4 * C);  // column-sum partials (separate or in a GEMM epilogue)
   M->scratch_floats = sf;
   M->scratch = (float*)take(sf * 4);
+  // deferred column-sum partials: 2L + 1 LayerNorm backwards, L fused fc bias sums (fcproj input
+  // gradient epilogue), L qkv bias sums (attention backward), and the batch table (32 columns a block)
+  const size_t nln = 2 * L + 1;
+  M->defer_floats = nln * layernorm_bwd_partial_floats((int)BT, (int)C) +
+                    L * (size_t)gemm_colsum_rows_max((int)BT) * 4 * C +
+                    L * (size_t)attention_bias_partial_rows((int)B, (int)T) * 3 * C;
+  M->defer = (float*)take(M->defer_floats * 4);
+  M->fin_cap = nln * 3 * cdiv(C, 32) + L * cdiv(4 * C, 32) + L * cdiv(3 * C, 32);
+  M->fin_dev = (FinishBlock*)take(M->fin_cap * sizeof(FinishBlock));
   M->norm_partial = (double*)take(NORM_PARTS * 8);
   M->norm2 = (double*)take(8);
   M->clip_scale = (float*)take(4);
@@ -425,7 +443,8 @@ hipError_t refresh_transposed() {
 
 int gemm(bool akc, bool bkc, Epi epi, int M, int N, int K, const void* A, long lda, const void* Bp, long ldb,
          void* Cp, long ldc, const void* bias = nullptr, const void* aux = nullptr, long ldaux = 0,
-         void* C2 = nullptr, int accumulate = 0, bool split = false, float* colsum = nullptr, int colsum_acc = 0) {
+         void* C2 = nullptr, int accumulate = 0, bool split = false, float* colsum = nullptr, int colsum_acc = 0,
+         ColsumDefer* colsum_defer = nullptr) {
   GemmArgs a{};
   a.M = M;
   a.N = N;
@@ -443,6 +462,7 @@ int gemm(bool akc, bool bkc, Epi epi, int M, int N, int K, const void* A, long l
   a.accumulate = accumulate;
   a.colsum = colsum;
   a.colsum_accumulate = colsum_acc;
+  a.colsum_defer = colsum_defer;
   const bool scr = split || colsum;
   HIPCHK(launch_gemm(g.dt, akc, bkc, epi, a, scr ? g.scratch : nullptr, scr ? g.scratch_floats : 0, g.stream));
   return GPT2_OK;
@@ -532,6 +552,17 @@ int forward_impl(const int32_t* tokens, const int32_t* targets) {
   return GPT2_OK;
 }
 
+// Room in the deferred-partials region for the next launcher.
+ColsumDefer defer_slot() { return ColsumDefer{g.defer + g.defer_used, g.defer_floats - g.defer_used, 0}; }
+// List the blocks of one deferred column sum: out[c] (+)= sum_{y < rows} part[y ld + c], c < ncols.
+int defer_sum(const float* part, long ld, int rows, int ncols, float* out) {
+  const int nch = cdiv(ncols, 32);
+  if (!out) return GPT2_OK;
+  if (g.fin_host.size() + nch > g.fin_cap) return fail(GPT2_ESTATE, "internal: deferred column sums exceed their table");
+  for (int ch = 0; ch < nch; ++ch) g.fin_host.push_back(FinishBlock{part, out, ld, rows, ncols, ch, 0});
+  return GPT2_OK;
+}
+
 int backward_impl() {
   const int BT = g.BT, C = g.C, L = g.L;
   const int acc = g.micro > 0 ? 1 : 0;
@@ -539,6 +570,21 @@ int backward_impl() {
   hipStream_t s = g.stream;
   float* sc = g.scratch;
   const size_t sf = g.scratch_floats;
+  g.fin_host.clear();
+  g.defer_used = 0;
+  // LayerNorm backward into dres; its column sums (dw, db, and dsum when set) go to the batched finish
+  auto ln_bwd = [&](const void* dy, const void* x, const void* w, const float* mean, const float* rstd, int add,
+                    float* dw, float* db, float* dsum) -> int {
+    ColsumDefer d = defer_slot();
+    HIPCHK(launch_layernorm_bwd(g.dt, BT, C, dy, x, w, mean, rstd, g.dres, add, dw, db, dsum, acc, sc, sf, s, &d));
+    if (d.rows > 0) {
+      RUN(defer_sum(d.part, 3L * C, d.rows, C, dw));
+      RUN(defer_sum(d.part + C, 3L * C, d.rows, C, db));
+      if (dsum) RUN(defer_sum(d.part + 2 * C, 3L * C, d.rows, C, dsum));
+      g.defer_used += (size_t)d.rows * 3 * C;
+    }
+    return GPT2_OK;
+  };
   // classifier (tied wte): dz = dlogits wte ; dwte (+)= dlogits^T z
   {
       ProfScope ps_(GPT2_K_GEMM_CLASSIFIER_DX);
@@ -555,8 +601,7 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
       // the column sums of the dres it writes are the bias gradient of the last fcproj
       float* dsum = (lb && L > 0) ? G(g.lo[L - 1].fcprojb) : nullptr;
-      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xlast, W(g.o_lnfw), g.lnf_mean, g.lnf_rstd, g.dres, 0,
-                                  G(g.o_lnfw), G(g.o_lnfb), dsum, acc, sc, sf, s));
+      RUN(ln_bwd(g.dbuf2, xlast, W(g.o_lnfw), g.lnf_mean, g.lnf_rstd, 0, G(g.o_lnfw), G(g.o_lnfb), dsum));
     }
   for (int l = L - 1; l >= 0; --l) {
     const LayerOff& o = g.lo[l];
@@ -569,12 +614,17 @@ int backward_impl() {
       // are the fc bias gradient
       float* dfcb = lb ? G(o.fcb) : nullptr;
       const Epi ep = g.cfg.recompute >= 1 ? EPI_GELU_BWD : EPI_MUL;
+      ColsumDefer d = defer_slot();
       if (g.shadow_t)
         RUN(gemm(true, true, ep, BT, 4 * C, C, g.dres, C, WT(o.fcprojw), C, g.dbuf1, 4 * C, nullptr, a.fch, 4 * C,
-                 nullptr, 0, false, dfcb, acc));
+                 nullptr, 0, false, dfcb, acc, &d));
       else
         RUN(gemm(true, false, ep, BT, 4 * C, C, g.dres, C, W(o.fcprojw), 4 * C, g.dbuf1, 4 * C, nullptr, a.fch,
-                 4 * C, nullptr, 0, false, dfcb, acc));
+                 4 * C, nullptr, 0, false, dfcb, acc, &d));
+      if (d.rows > 0) {
+        RUN(defer_sum(d.part, 4L * C, d.rows, 4 * C, dfcb));
+        g.defer_used += (size_t)d.rows * 4 * C;
+      }
     }
     if (g.cfg.recompute >= 1) {  // gelu(z) again, for the fcproj weight gradient
       ProfScope ps_(GPT2_K_RECOMPUTE);
@@ -604,8 +654,8 @@ int backward_impl() {
     {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
       // + column sums of the updated dres = the attproj bias gradient
-      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, a.res1, W(o.ln2w), a.ln2_mean, a.ln2_rstd, g.dres, 1,
-                                  G(o.ln2w), G(o.ln2b), lb ? G(o.attprojb) : nullptr, acc, sc, sf, s));
+      RUN(ln_bwd(g.dbuf2, a.res1, W(o.ln2w), a.ln2_mean, a.ln2_rstd, 1, G(o.ln2w), G(o.ln2b),
+                 lb ? G(o.attprojb) : nullptr));
     }
     // attproj: res1 = xin + atty Wproj^T + b
     {
@@ -619,8 +669,12 @@ int backward_impl() {
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
                                   ATT_BWD_PRE, s));
     }
-    // bf16: the attention kernels also leave the column partials of dqkv (the qkv bias gradient)
-    float* csa = (lb && g.dt == DT_BF16) ? sc : nullptr;
+    // bf16: the attention kernels also leave the column partials of dqkv (the qkv bias gradient),
+    // summed in the batched finish
+    const int arows = attention_bias_partial_rows(g.B, g.T);
+    const ColsumDefer ad = defer_slot();
+    const bool adefer = (size_t)arows * 3 * C <= ad.cap;
+    float* csa = (lb && g.dt == DT_BF16) ? (adefer ? ad.part : sc) : nullptr;
     {
       ProfScope ps_(GPT2_K_ATTENTION_BWD);
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
@@ -633,8 +687,12 @@ int backward_impl() {
     }
     {
       ProfScope ps_(GPT2_K_BIAS_GRAD);
-      if (csa) HIPCHK(launch_colsum_finish(csa, attention_bias_partial_rows(g.B, g.T), 3 * C, G(o.qkvb), acc, s));
-      else if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
+      if (csa && adefer) {
+        RUN(defer_sum(csa, 3L * C, arows, 3 * C, G(o.qkvb)));
+        g.defer_used += (size_t)arows * 3 * C;
+      } else if (csa) {
+        HIPCHK(launch_colsum_finish(csa, arows, 3 * C, G(o.qkvb), acc, s));
+      } else if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
     }
     // qkv = ln1 Wqkv^T + b
     {
@@ -673,9 +731,20 @@ int backward_impl() {
       ProfScope ps_(GPT2_K_LAYERNORM_BWD);
       // + column sums of the updated dres = the fcproj bias gradient of the layer below
       float* dsum = (lb && l > 0) ? G(g.lo[l - 1].fcprojb) : nullptr;
-      HIPCHK(launch_layernorm_bwd(g.dt, BT, C, g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, g.dres, 1,
-                                  G(o.ln1w), G(o.ln1b), dsum, acc, sc, sf, s));
+      RUN(ln_bwd(g.dbuf2, xin, W(o.ln1w), a.ln1_mean, a.ln1_rstd, 1, G(o.ln1w), G(o.ln1b), dsum));
     }
+  }
+  if (!g.fin_host.empty()) {
+    ProfScope ps_(GPT2_K_GRAD_FINISH);
+    const size_t nb = g.fin_host.size();
+    if (g.fin_up.size() != nb || memcmp(g.fin_up.data(), g.fin_host.data(), nb * sizeof(FinishBlock)) != 0) {
+      // a new table (the first backward: it stays the same while the configuration does); wait
+      // for an earlier copy out of the host list before replacing it
+      HIPCHK(hipStreamSynchronize(s));
+      g.fin_up = g.fin_host;
+      HIPCHK(hipMemcpyAsync(g.fin_dev, g.fin_up.data(), nb * sizeof(FinishBlock), hipMemcpyHostToDevice, s));
+    }
+    HIPCHK(launch_finish_batch(g.fin_dev, (int)nb, acc, s));
   }
   HIPCHK(hipStreamWaitEvent(s, g.ev_sorted, 0));
   {

@@ -195,7 +195,8 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_ATTENTION_BWD_PRE 26  /* D = rowsum(dO * O) per query          */
 #define GPT2_K_WEIGHT_TRANSPOSE 27  /* bf16 weight matrices -> transposed copies */
 #define GPT2_K_RECOMPUTE 28          /* activation recompute in the backward (recompute >= 1) */
-#define GPT2_K_COUNT 29
+#define GPT2_K_GRAD_FINISH 29        /* second stage of the backward's column sums, one batched launch */
+#define GPT2_K_COUNT 30
 int gpt2_profile_enable(uint32_t mask);
 int gpt2_profile_read(float* ms, int32_t* launches, int32_t n);
 
