@@ -71,10 +71,10 @@ def class_work(name, w):
         # p, m, v rw + g read + bf16 write, + the transposed bf16 copies of the matrices
         "adamw": N * (4 * 3 * 2 + 4 + 2) + (Vp * C + 12 * C * C * L) * e,
         "weight_transpose": (Vp * C + 12 * C * C * L) * e * 2,        # bf16 matrices read + written
-        # the column-sum partial rows it reads: 2L + 1 LayerNorm backwards (512 blocks x 3C), the fc
+        # the column-sum partial rows it reads: 2L + 1 LayerNorm backwards (256 blocks x 3C), the fc
         # bias sums of the fcproj input gradient (two rows per 256-row tile x 4C) and the qkv bias sums
         # of the attention backward (one row per 128-query tile x 3C)
-        "grad_finish": 4 * ((2 * L + 1) * 512 * 3 * C + L * (BT // 128) * 4 * C + L * B * (T // 128) * 3 * C),
+        "grad_finish": 4 * ((2 * L + 1) * 256 * 3 * C + L * (BT // 128) * 4 * C + L * B * (T // 128) * 3 * C),
     }
     return "hbm", float(bytes_.get(name, 0))
 
