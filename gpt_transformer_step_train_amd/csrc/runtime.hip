@@ -685,14 +685,15 @@ int backward_impl() {
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
                                   ATT_BWD_Q, s, csa));
     }
-    {
+    if (csa && adefer) {
+      RUN(defer_sum(csa, 3L * C, arows, 3 * C, G(o.qkvb)));
+      g.defer_used += (size_t)arows * 3 * C;
+    } else if (csa) {
       ProfScope ps_(GPT2_K_BIAS_GRAD);
-      if (csa && adefer) {
-        RUN(defer_sum(csa, 3L * C, arows, 3 * C, G(o.qkvb)));
-        g.defer_used += (size_t)arows * 3 * C;
-      } else if (csa) {
-        HIPCHK(launch_colsum_finish(csa, arows, 3 * C, G(o.qkvb), acc, s));
-      } else if (lb) HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
+      HIPCHK(launch_colsum_finish(csa, arows, 3 * C, G(o.qkvb), acc, s));
+    } else if (lb) {
+      ProfScope ps_(GPT2_K_BIAS_GRAD);
+      HIPCHK(launch_colsum(g.dt, g.dbuf1, 3 * C, BT, 3 * C, G(o.qkvb), acc, sc, sf, s));
     }
     // qkv = ln1 Wqkv^T + b
     {

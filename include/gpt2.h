@@ -180,7 +180,7 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_LAYERNORM_BWD 11
 #define GPT2_K_GEMM_FCPROJ_DX 12
 #define GPT2_K_GEMM_FCPROJ_DW 13
-#define GPT2_K_BIAS_GRAD 14
+#define GPT2_K_BIAS_GRAD 14           /* qkv bias gradient outside the batched finish (fp32 runs) */
 #define GPT2_K_GEMM_FC_DX 15
 #define GPT2_K_GEMM_FC_DW 16
 #define GPT2_K_GEMM_ATTPROJ_DX 17
