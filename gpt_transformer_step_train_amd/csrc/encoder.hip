@@ -135,7 +135,9 @@ __device__ __forceinline__ ChunkInfo chunk_info(const uint32_t* keys, int BT, in
   return c;
 }
 
-// grid: (nchunks, cdiv(C/VEC, 64)), block 64: one 16-byte column vector per thread
+// grid: (nchunks, cdiv(C/VEC, 64)), block 64: one 16-byte column vector per thread. The keys and
+// output-gradient rows of the whole chunk are requested before the first is added, so a chunk
+// costs one memory round trip instead of one per entry.
 template <typename T>
 __global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32_t* __restrict__ keys,
                                                      const T* __restrict__ dout, float* __restrict__ dwte,
@@ -145,10 +147,20 @@ __global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32
   if (cv * VEC >= C) return;
   const int ch = blockIdx.x;
   const ChunkInfo ci = chunk_info(keys, BT, ch);
+  const int n = ci.end - ci.start;
+  uint32_t kk[CH];
+  u32x4 raw[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if (i < n) {
+      kk[i] = keys[ci.start + i];
+      raw[i] = *reinterpret_cast<const u32x4*>(dout + (size_t)key_pos(kk[i]) * C + cv * VEC);
+    }
+  }
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  int cur = key_tok(keys[ci.start]);
+  int cur = key_tok(kk[0]);
   bool first = true;
   auto flush = [&](int v, bool last) {
     float* dst;
@@ -163,25 +175,30 @@ __global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32
 #pragma unroll
     for (int e = 0; e < VEC; ++e) dst[e] = add ? dst[e] + acc[e] : acc[e];
   };
-  for (int i = ci.start; i < ci.end; ++i) {
-    const uint32_t k = keys[i];
-    const int v = key_tok(k);
-    if (v != cur) {
-      flush(cur, false);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-      cur = v;
-      first = false;
+  for (int i = 0; i < CH; ++i) {
+    if (i < n) {
+      const int v = key_tok(kk[i]);
+      if (v != cur) {
+        flush(cur, false);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+        cur = v;
+        first = false;
+      }
+      V16<T> d;
+      d.unpack(raw[i]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += d.v[e];
     }
-    V16<T> d;
-    d.load(dout + (size_t)key_pos(k) * C + cv * VEC);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] += d.v[e];
   }
   flush(cur, true);
 }
 
-// Runs that cross chunk boundaries: the chunk where the run starts adds its pieces in order.
+// Runs that cross chunk boundaries: the chunk where the run starts adds the pieces of the chunks
+// the run reaches, in chunk order. The run's end is found by binary search over the sorted keys
+// (a few dependent loads, where walking the chunks one by one cost two per chunk), then the pieces
+// are loaded 8 at a time.
 __global__ __launch_bounds__(256) void wte_bwd_fixup(int BT, int C, int nch, const uint32_t* __restrict__ keys,
                                                      float* __restrict__ dwte, const float* __restrict__ part_head,
                                                      const float* __restrict__ part_tail) {
@@ -189,12 +206,23 @@ __global__ __launch_bounds__(256) void wte_bwd_fixup(int BT, int C, int nch, con
   const ChunkInfo ci = chunk_info(keys, BT, ch);
   if (!ci.tail_cont || (ci.single && ci.head_cont)) return;
   const int v = key_tok(keys[ci.end - 1]);
+  // first sorted index past the run: entries of token v form a prefix of [ci.end, BT)
+  int lo = ci.end, hi = BT;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (key_tok(keys[mid]) == v) lo = mid + 1;
+    else hi = mid;
+  }
+  const int last = (lo - 1) / CH;  // the chunk holding the run's last entry
   for (int c = threadIdx.x; c < C; c += 256) {
     float s = part_tail[(size_t)ch * C + c];
-    for (int n = ch + 1; n < nch; ++n) {
-      s += part_head[(size_t)n * C + c];
-      const ChunkInfo cn = chunk_info(keys, BT, n);
-      if (!(cn.single && cn.tail_cont)) break;
+    for (int n0 = ch + 1; n0 <= last; n0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = n0 + u <= last ? part_head[(size_t)(n0 + u) * C + c] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (n0 + u <= last) s += t[u];
     }
     dwte[(size_t)v * C + c] += s;
   }

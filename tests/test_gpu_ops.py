@@ -442,7 +442,9 @@ def test_cross_entropy(dt, rows, V, ld):
 
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("B,T,maxT,C,V,p0", [(4, 64, 80, 128, 500, 0.14), (4, 256, 256, 64, 300, 0.5),
-                                            (12, 3, 3, 16, 2, 0.5)])
+                                            (12, 3, 3, 16, 2, 0.5),
+                                            # one run over (nearly) every chunk; V = 1: a single token
+                                            (2, 1024, 1024, 64, 3, 0.97), (2, 1024, 1024, 64, 1, 0.0)])
 def test_encoder_forward_backward_deterministic(dt, B, T, maxT, C, V, p0):
     rng = np.random.default_rng(B * T + V)
     tok = rng.integers(0, V, (B, T)).astype(np.int32)
