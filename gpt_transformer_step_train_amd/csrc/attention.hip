@@ -312,8 +312,8 @@ struct Piece {
 // grid (T/128, B*H), 256 threads. Wave w owns queries q0 + 32w .. +31.
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint16_t* __restrict__ qkv,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * LDP];  // [key][d]
+  __shared__ __attribute__((aligned(16))) uint16_t Ksb[2][KT * LDP];  // [key][d], two stages
+  __shared__ __attribute__((aligned(16))) uint16_t Vsb[2][KT * LDP];  // [key][d]
   int bh, rank;
   attn_block_map(bh, rank);
   const int qt = gridDim.x - 1 - rank;  // the last query tiles see the most keys
@@ -356,9 +356,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
     pc.load(base + (is_k ? C : 2 * C) + h * HD, C3, kt * KT, T, p);
   };
   load_tile(0);
+  pc.store_rows(is_k ? Ksb[0] : Vsb[0], p);
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    pc.store_rows(is_k ? Ks : Vs, p);
-    __syncthreads();
+    const uint16_t* Ks = Ksb[kt & 1];
+    const uint16_t* Vs = Vsb[kt & 1];
     if (kt + 1 < ntiles) load_tile(kt + 1);
     // both 32-key halves of the tile at once: two independent S chains, one max, one rescale
     const int kb0 = kt * KT;
@@ -412,6 +414,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
           lsum = mfma(ones, pf, lsum);
         }
     }
+    // the next tile goes to the other stage (last read in the previous iteration, before the
+    // barrier that ended it): one barrier per tile
+    if (kt + 1 < ntiles) pc.store_rows(is_k ? Ksb[(kt + 1) & 1] : Vsb[(kt + 1) & 1], p);
     __syncthreads();
   }
   const float l_tot = pair_sum(g == 0 ? lsum[0] : 0.f);
