@@ -287,24 +287,26 @@ __device__ __forceinline__ void attn_block_map(int& bh, int& rank) {
   }
 }
 
-// A 64 x 64 bf16 tile piece: 4 rows x 8 columns per thread (128 pieces per tile); 4 lanes read
-// 64 contiguous bytes of each global row.
+// A 64 x 64 bf16 tile piece: rows r, r + 16, r + 32, r + 48 (r = p % 16) x 8 columns per thread
+// (128 pieces per tile). The 16 lanes of one 16-byte LDS store cycle write 16 consecutive rows of
+// one column chunk, which the 144-byte row pitch spreads over distinct banks (rows 4 apart, as in
+// a 4-row piece, would put every fourth lane on the same banks).
 struct Piece {
   u32x4 r[4];
-  __device__ __forceinline__ static int rgrp(int p) { return (p & 15) * 4; }
+  __device__ __forceinline__ static int rgrp(int p) { return p & 15; }
   __device__ __forceinline__ static int cgrp(int p) { return (p >> 4) * 8; }
   __device__ __forceinline__ void load(const uint16_t* src, long ld, int row0, int nrows, int p) {
     const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = row0 + rg + j;
+      const int row = row0 + rg + 16 * j;
       r[j] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + cg) : u32x4{0u, 0u, 0u, 0u};
     }
   }
   __device__ __forceinline__ void store_rows(uint16_t* lds, int p) const {  // lds[row][col]
     const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + j) * LDP + cg) = r[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + 16 * j) * LDP + cg) = r[j];
   }
 };
 
