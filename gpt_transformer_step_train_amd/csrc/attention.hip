@@ -104,6 +104,47 @@ __global__ __launch_bounds__(256) void attn_bwd_dvec(int BT, int T_, int H, cons
   dvec[((size_t)b * H + h) * T_ + t] = s;
 }
 
+// bf16, hs = 64: the same D with lane-contiguous loads. The (row, head) pairs are 128-byte runs
+// of out / dout in pair order; a wave takes 64 pairs as 512 consecutive 16-byte chunks, chunk
+// j * 64 + lane in its j-th load (so each load instruction reads 1 KiB contiguous, where one
+// thread per pair makes every instruction touch 64 different 128-byte lines), and the 8 lanes
+// holding one pair's chunks add their partial sums with three xor-shuffles.
+__global__ __launch_bounds__(256) void attn_bwd_dvec_bf16(int npairs, int T_, int H, const bf16* __restrict__ out,
+                                                          const bf16* __restrict__ dout, float* __restrict__ dvec) {
+  const int lane = threadIdx.x & 63;
+  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512;  // first chunk of this wave
+  const int nchunk = npairs * 8;                                // < 2^31 for B T H <= 2^28
+  // straight-line loads (a chunk past the end reads the last one and is dropped below), so all 16
+  // are in flight together; a guarded load would make the compiler wait at every branch join
+  u32x4 a[8], c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int ch = min(c0 + j * 64 + lane, nchunk - 1);
+    a[j] = *reinterpret_cast<const u32x4*>(out + (size_t)ch * 8);
+    c[j] = *reinterpret_cast<const u32x4*>(dout + (size_t)ch * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int ch = c0 + j * 64 + lane;
+    V16<bf16> x, y;
+    x.unpack(a[j]);
+    y.unpack(c[j]);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += x.v[e] * y.v[e];
+    if (ch >= nchunk) sum = 0.f;
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    const int pr = ch >> 3;
+    if ((lane & 7) == 0 && pr < npairs) {
+      const int row = pr / H, h = pr - row * H;
+      const int b = row / T_, t = row - b * T_;
+      dvec[((size_t)b * H + h) * T_ + t] = sum;
+    }
+  }
+}
+
 // dK, dV: one thread per key
 template <int HS>
 __global__ __launch_bounds__(AT) void attn_bwd_kv_f32(int T, int H, const float* __restrict__ qkv,
@@ -741,8 +782,8 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
   if (dt == DT_BF16) {
     if (hs != HD) return hipErrorInvalidValue;
     if (parts & ATT_BWD_PRE)
-      attn_bwd_dvec<bf16, HD><<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT, T, H, reinterpret_cast<const bf16*>(out),
-                                                                      reinterpret_cast<const bf16*>(dout), dvec);
+      attn_bwd_dvec_bf16<<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT * H, T, H, reinterpret_cast<const bf16*>(out),
+                                                               reinterpret_cast<const bf16*>(dout), dvec);
     dim3 grid(cdiv(T, BQ), B * H);
     auto Q = reinterpret_cast<const uint16_t*>(qkv);
     auto dO = reinterpret_cast<const uint16_t*>(dout);
