@@ -62,7 +62,6 @@ __global__ __launch_bounds__(CE_THREADS) void ce_kernel(int V, int ld, T* __rest
   int tgt = targets ? targets[row] : -1;
   if (tgt >= V) tgt = -1;  // reported by count_targets
   const int nvec = ld / VEC;
-  if (threadIdx.x == 0) xt_sh = tgt >= 0 ? ld1(x, tgt) : 0.f;
 
   u32x4 raw[NVT];
 #pragma unroll
@@ -70,6 +69,8 @@ __global__ __launch_bounds__(CE_THREADS) void ce_kernel(int V, int ld, T* __rest
     const int v = threadIdx.x + j * CE_THREADS;
     raw[j] = v < nvec ? *reinterpret_cast<const u32x4*>(x + (size_t)v * VEC) : u32x4{0u, 0u, 0u, 0u};
   }
+  // (after the row's loads are issued, so that wave 0 does not wait for this one first)
+  if (threadIdx.x == 0) xt_sh = tgt >= 0 ? ld1(x, tgt) : 0.f;
   // values in log2 units; columns >= V are -inf
   auto unpack = [&](int j, float (&y)[VEC]) {
     V16<T> t;

@@ -137,25 +137,29 @@ __device__ __forceinline__ ChunkInfo chunk_info(const uint32_t* keys, int BT, in
 
 // grid: (nchunks, cdiv(C/VEC, 64)), block 64: one 16-byte column vector per thread. The keys and
 // output-gradient rows of the whole chunk are requested before the first is added, so a chunk
-// costs one memory round trip instead of one per entry.
+// costs one memory round trip instead of one per entry: the keys with one vector load (lane i
+// holds entry i) broadcast with readlane, the rows as straight-line loads (entries past the chunk
+// end repeat its last one, lanes past the last column vector read the last one; both unused),
+// because a guarded load makes the compiler wait for it at the branch join.
 template <typename T>
 __global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32_t* __restrict__ keys,
                                                      const T* __restrict__ dout, float* __restrict__ dwte,
                                                      float* __restrict__ part_head, float* __restrict__ part_tail) {
   constexpr int VEC = Elt<T>::VEC;
-  const int cv = blockIdx.y * 64 + threadIdx.x;
-  if (cv * VEC >= C) return;
+  const int lane = threadIdx.x;
+  const int cv = blockIdx.y * 64 + lane;
+  const bool active = cv * VEC < C;
+  const int cvc = active ? cv : C / VEC - 1;
   const int ch = blockIdx.x;
   const ChunkInfo ci = chunk_info(keys, BT, ch);
   const int n = ci.end - ci.start;
+  const uint32_t kl = keys[ci.start + min(lane, n - 1)];
   uint32_t kk[CH];
   u32x4 raw[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    if (i < n) {
-      kk[i] = keys[ci.start + i];
-      raw[i] = *reinterpret_cast<const u32x4*>(dout + (size_t)key_pos(kk[i]) * C + cv * VEC);
-    }
+    kk[i] = __builtin_amdgcn_readlane(kl, i);
+    raw[i] = *reinterpret_cast<const u32x4*>(dout + (size_t)key_pos(kk[i]) * C + cvc * VEC);
   }
   float acc[VEC];
 #pragma unroll
@@ -163,6 +167,7 @@ __global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32
   int cur = key_tok(kk[0]);
   bool first = true;
   auto flush = [&](int v, bool last) {
+    if (!active) return;
     float* dst;
     bool add = false;
     if (first && ci.head_cont) dst = part_head + (size_t)ch * C;

@@ -41,16 +41,17 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int C, const T* _
   if (row >= rows) return;
   const int nvec = C / VEC;
   const T* xr = x + (size_t)row * C;
-  // the row, the weight and the bias are all requested before the first reduction
+  // the row, the weight and the bias are all requested before the first reduction, as straight-line
+  // loads (lanes past the row end read its last vector, unused; no bias: the weight again): a
+  // guarded load makes the compiler wait for it at the branch join
   u32x4 xraw[NV], wraw[NV], braw[NV];
+  const T* bsrc = b ? b : w;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = li + L * j;
-    if (v < nvec) {
-      xraw[j] = *reinterpret_cast<const u32x4*>(xr + v * VEC);
-      wraw[j] = *reinterpret_cast<const u32x4*>(w + v * VEC);
-      if (b) braw[j] = *reinterpret_cast<const u32x4*>(b + v * VEC);
-    }
+    const int vc = min(li + L * j, nvec - 1);
+    xraw[j] = *reinterpret_cast<const u32x4*>(xr + vc * VEC);
+    wraw[j] = *reinterpret_cast<const u32x4*>(w + vc * VEC);
+    braw[j] = *reinterpret_cast<const u32x4*>(bsrc + vc * VEC);
   }
   V16<T> xv[NV];
   float s = 0.f;
