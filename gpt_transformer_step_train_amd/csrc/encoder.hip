@@ -43,6 +43,7 @@ hipError_t launch_encoder_fwd(DType dt, int B, int T, int C, int V, const int32_
   const int BT = B * T;
   if (BT <= 0) return hipSuccess;
   const int vec = dt == DT_BF16 ? 8 : 4;
+  if (C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
   const int blocks = std::min(cdiv((long)BT * (C / vec), 256), 8192);
   if (dt == DT_BF16)
     encoder_fwd_kernel<bf16><<<blocks, 256, 0, s>>>(BT, T, C, V, tok, reinterpret_cast<const bf16*>(wte),
@@ -109,16 +110,41 @@ hipError_t launch_encoder_sort(int BT, int V, const int32_t* tok, uint32_t* keys
 // ------------------------------------------------------------------ backward
 constexpr int CH = 32;  // sorted entries per chunk
 
+// dwpe[t] (+)= sum_b dout[b, t]: one thread per 16-byte column vector of one position; the rows of
+// 8 batch entries are requested at a time (straight-line loads), then added in batch order.
 template <typename T>
 __global__ __launch_bounds__(256) void wpe_bwd_kernel(int B, int T_, int maxT, int C, const T* __restrict__ dout,
                                                       float* __restrict__ dwpe, int accumulate) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // over maxT*C; rows t >= T get no gradient
-  if (i >= maxT * C) return;
-  const int t = i / C, c = i % C;
-  float s = 0.f;
-  if (t < T_)
-    for (int b = 0; b < B; ++b) s += ld1(dout, ((size_t)b * T_ + t) * C + c);
-  dwpe[i] = accumulate ? dwpe[i] + s : s;
+  constexpr int VEC = Elt<T>::VEC;
+  const int nv = C / VEC;
+  const int i = blockIdx.x * 256 + threadIdx.x;  // over maxT * nv; rows t >= T get no gradient
+  if (i >= maxT * nv) return;
+  const int t = i / nv, c = (i % nv) * VEC;
+  float s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+  if (t < T_) {
+    for (int b0 = 0; b0 < B; b0 += 8) {
+      u32x4 r[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int b = min(b0 + u, B - 1);
+        r[u] = *reinterpret_cast<const u32x4*>(dout + ((size_t)b * T_ + t) * C + c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < B) {
+          V16<T> v;
+          v.unpack(r[u]);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s[e] += v.v[e];
+        }
+      }
+    }
+  }
+  float* dst = dwpe + (size_t)t * C + c;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) dst[e] = accumulate ? dst[e] + s[e] : s[e];
 }
 
 struct ChunkInfo {
@@ -245,14 +271,15 @@ hipError_t launch_encoder_bwd(DType dt, int B, int T, int maxT, int C, const uin
   float* ph = partial;
   float* pt = partial + (size_t)nch * C;
   const int vec = dt == DT_BF16 ? 8 : 4;
+  if (C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
   dim3 g1(nch, cdiv(C / vec, 64));
   if (dt == DT_BF16) {
     auto D = reinterpret_cast<const bf16*>(dout);
-    wpe_bwd_kernel<bf16><<<cdiv((long)maxT * C, 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
+    wpe_bwd_kernel<bf16><<<cdiv((long)maxT * (C / 8), 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
     wte_bwd_chunks<bf16><<<g1, 64, 0, s>>>(BT, C, keys, D, dwte, ph, pt);
   } else {
     auto D = reinterpret_cast<const float*>(dout);
-    wpe_bwd_kernel<float><<<cdiv((long)maxT * C, 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
+    wpe_bwd_kernel<float><<<cdiv((long)maxT * (C / 4), 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
     wte_bwd_chunks<float><<<g1, 64, 0, s>>>(BT, C, keys, D, dwte, ph, pt);
   }
   wte_bwd_fixup<<<nch, 256, 0, s>>>(BT, C, nch, keys, dwte, ph, pt);
