@@ -161,69 +161,73 @@ __device__ __forceinline__ ChunkInfo chunk_info(const uint32_t* keys, int BT, in
   return c;
 }
 
-// grid: (nchunks, cdiv(C/VEC, 64)), block 64: one 16-byte column vector per thread. The keys and
-// output-gradient rows of the whole chunk are requested before the first is added, so a chunk
-// costs one memory round trip instead of one per entry: the keys with one vector load (lane i
-// holds entry i) broadcast with readlane, the rows as straight-line loads (entries past the chunk
-// end repeat its last one, lanes past the last column vector read the last one; both unused),
-// because a guarded load makes the compiler wait for it at the branch join.
+// 4 consecutive elements of a row of the output gradient (8 bytes in bf16, 16 in fp32), as floats
+template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
+  const u32x2 r = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u), __uint_as_float(r[1] << 16),
+               __uint_as_float(r[1] & 0xffff0000u)};
+}
+
+// grid: (nchunks, cdiv(C/4, 64)), block 64: 4 consecutive columns per thread. Everything a chunk
+// reads is requested before the first value is used, so a chunk costs one memory round trip
+// instead of one per entry and one per token it adds into: the keys with one vector load (lane i
+// holds entry i) broadcast with readlane, then, as straight-line loads, the output-gradient row of
+// every entry and the dwte row of every entry's token (the old value a run adds to; each dwte row
+// is added to by at most one chunk here, the one holding its whole run). Entries past the chunk
+// end repeat its last one and lanes past the last column read the last one; both are unused.
+// (A guarded load would make the compiler wait for it at the branch join.)
 template <typename T>
 __global__ __launch_bounds__(64) void wte_bwd_chunks(int BT, int C, const uint32_t* __restrict__ keys,
                                                      const T* __restrict__ dout, float* __restrict__ dwte,
                                                      float* __restrict__ part_head, float* __restrict__ part_tail) {
-  constexpr int VEC = Elt<T>::VEC;
   const int lane = threadIdx.x;
-  const int cv = blockIdx.y * 64 + lane;
-  const bool active = cv * VEC < C;
-  const int cvc = active ? cv : C / VEC - 1;
+  const int c4 = blockIdx.y * 64 + lane;  // column group of 4
+  const bool active = c4 * 4 < C;
+  const int col = (active ? c4 : C / 4 - 1) * 4;
   const int ch = blockIdx.x;
   const ChunkInfo ci = chunk_info(keys, BT, ch);
   const int n = ci.end - ci.start;
   const uint32_t kl = keys[ci.start + min(lane, n - 1)];
   uint32_t kk[CH];
-  u32x4 raw[CH];
+  f32x4 d[CH], old[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     kk[i] = __builtin_amdgcn_readlane(kl, i);
-    raw[i] = *reinterpret_cast<const u32x4*>(dout + (size_t)key_pos(kk[i]) * C + cvc * VEC);
+    d[i] = load4<T>(dout + (size_t)key_pos(kk[i]) * C + col);
+    old[i] = *reinterpret_cast<const f32x4*>(dwte + (size_t)key_tok(kk[i]) * C + col);
   }
-  float acc[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   int cur = key_tok(kk[0]);
   bool first = true;
-  auto flush = [&](int v, bool last) {
+  // the run of token cur ends at entry i (whose prefetched dwte row is old[i])
+  auto flush = [&](int i, bool last) {
     if (!active) return;
     float* dst;
-    bool add = false;
+    f32x4 v = acc;
     if (first && ci.head_cont) dst = part_head + (size_t)ch * C;
     else if (last && ci.tail_cont) dst = part_tail + (size_t)ch * C;
     else {
-      dst = dwte + (size_t)v * C;
-      add = true;
+      dst = dwte + (size_t)cur * C;
+      v = old[i] + acc;
     }
-    dst += cv * VEC;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) dst[e] = add ? dst[e] + acc[e] : acc[e];
+    *reinterpret_cast<f32x4*>(dst + col) = v;
   };
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     if (i < n) {
       const int v = key_tok(kk[i]);
       if (v != cur) {
-        flush(cur, false);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+        flush(i - 1, false);
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
         cur = v;
         first = false;
       }
-      V16<T> d;
-      d.unpack(raw[i]);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += d.v[e];
+      acc += d[i];
+      if (i == n - 1) flush(i, true);
     }
   }
-  flush(cur, true);
 }
 
 // Runs that cross chunk boundaries: the chunk where the run starts adds the pieces of the chunks
@@ -272,7 +276,7 @@ hipError_t launch_encoder_bwd(DType dt, int B, int T, int maxT, int C, const uin
   float* pt = partial + (size_t)nch * C;
   const int vec = dt == DT_BF16 ? 8 : 4;
   if (C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
-  dim3 g1(nch, cdiv(C / vec, 64));
+  dim3 g1(nch, cdiv(C / 4, 64));
   if (dt == DT_BF16) {
     auto D = reinterpret_cast<const bf16*>(dout);
     wpe_bwd_kernel<bf16><<<cdiv((long)maxT * (C / 8), 256), 256, 0, s>>>(B, T, maxT, C, D, dwpe, accumulate_wpe);
