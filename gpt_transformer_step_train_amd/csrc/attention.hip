@@ -332,22 +332,28 @@ __device__ __forceinline__ void attn_block_map(int& bh, int& rank) {
 // (128 pieces per tile). The 16 lanes of one 16-byte LDS store cycle write 16 consecutive rows of
 // one column chunk, which the 144-byte row pitch spreads over distinct banks (rows 4 apart, as in
 // a 4-row piece, would put every fourth lane on the same banks).
+// The loads are straight-line (rows past nrows read the last row) and the rows past nrows are
+// zeroed only when the piece is stored: a guarded load, or a select on the loaded value, would
+// make the wave wait for the load right after issuing it instead of one tile later.
 struct Piece {
   u32x4 r[4];
+  int nvalid;  // rows of this thread's 4 that are in range: rg + 16 j < nvalid
   __device__ __forceinline__ static int rgrp(int p) { return p & 15; }
   __device__ __forceinline__ static int cgrp(int p) { return (p >> 4) * 8; }
   __device__ __forceinline__ void load(const uint16_t* src, long ld, int row0, int nrows, int p) {
     const int rg = rgrp(p), cg = cgrp(p);
+    nvalid = nrows - row0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = row0 + rg + 16 * j;
-      r[j] = row < nrows ? *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + cg) : u32x4{0u, 0u, 0u, 0u};
+      const int row = min(row0 + rg + 16 * j, nrows - 1);
+      r[j] = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + cg);
     }
   }
   __device__ __forceinline__ void store_rows(uint16_t* lds, int p) const {  // lds[row][col]
     const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + 16 * j) * LDP + cg) = r[j];
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(lds + (rg + 16 * j) * LDP + cg) = rg + 16 * j < nvalid ? r[j] : u32x4{0u, 0u, 0u, 0u};
   }
 };
 
@@ -553,23 +559,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   const int p = tid & 127;
   const bool is_q = tid < 128;
   float lnext = 0.f, dnext = 0.f;  // LSE and D of query tid of the next tile (tid < 64)
+  // Q or dO rows by a pointer select and LSE / D of query qt0 + tid % 64 from a clamped index, all
+  // straight-line (see Piece); out-of-range values are dropped when the tile is stored
+  int lrow = 0;
   auto load_tile = [&](int it) {
     const int qt0 = qstart + it * KT;
-    if (is_q) pc.load(base + h * HD, C3, qt0, T, p);
-    else pc.load(dbase + h * HD, C, qt0, T, p);
-    if (tid < KT) {
-      const int qr = qt0 + tid;
-      lnext = qr < T ? lse[(size_t)bh * T + qr] * LOG2E : 0.f;
-      dnext = qr < T ? dvec[(size_t)bh * T + qr] : 0.f;
-    }
+    pc.load((is_q ? base : dbase) + h * HD, is_q ? C3 : (long)C, qt0, T, p);
+    lrow = qt0 + (tid & (KT - 1));
+    const size_t li = (size_t)bh * T + min(lrow, T - 1);
+    lnext = lse[li];
+    dnext = dvec[li];
   };
   if (ntiles > 0) load_tile(0);
   for (int it = 0; it < ntiles; ++it) {
     const int qt0 = qstart + it * KT;
     pc.store_rows(is_q ? Qs : dOs, p);
     if (tid < KT) {
-      Ls[tid] = lnext;
-      Dsh[tid] = dnext;
+      Ls[tid] = lrow < T ? lnext * LOG2E : 0.f;
+      Dsh[tid] = lrow < T ? dnext : 0.f;
     }
     __syncthreads();
     if (it + 1 < ntiles) load_tile(it + 1);
