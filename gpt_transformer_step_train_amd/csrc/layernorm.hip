@@ -123,12 +123,16 @@ __global__ __launch_bounds__(64 * NW) void ln_bwd_kernel(int rows, int C, int ro
   const int r1 = min(rows, r0 + rows_per_block);
 
   float acc[3][NV][VEC];  // dw, db, dres sums
+  // the weight as straight-line loads (clamped index, masked after), all in flight together
   float wf[NV][VEC];
+  u32x4 wraw[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) wraw[j] = *reinterpret_cast<const u32x4*>(w + min(lane + 64 * j, nvec - 1) * VEC);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = lane + 64 * j;
     V16<T> t;
-    if (v < nvec) t.load(w + v * VEC);
+    t.unpack(wraw[j]);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       wf[j][e] = v < nvec ? t.v[e] : 0.f;
