@@ -776,9 +776,27 @@ __device__ __forceinline__ void splitk_reduce_seg(const float* __restrict__ part
                                                   float* __restrict__ dst, int accumulate, size_t first,
                                                   size_t stride) {
   const size_t n4 = n / 4;
+  // straight-line loads, 8 splits at a time (split indices past the last read the last one, and
+  // without accumulation the old value is read from the first partial instead of dst: both are
+  // dropped by a select after the loads), so that they are all in flight together: a load in a
+  // loop of unknown count, or under a guard, is waited for before the next is issued
+  const float* base0 = accumulate ? dst : part;
   for (size_t i = first; i < n4; i += stride) {
-    f32x4 s = accumulate ? reinterpret_cast<const f32x4*>(dst)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < splits; ++z) s += reinterpret_cast<const f32x4*>(part + (size_t)z * n)[i];
+    const f32x4 d0 = reinterpret_cast<const f32x4*>(base0)[i];
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const f32x4*>(part + (size_t)min(u, splits - 1) * n)[i];
+    f32x4 s = accumulate ? d0 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < splits) s += v[u];
+    for (int z0 = 8; z0 < splits; z0 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const f32x4*>(part + (size_t)min(z0 + u, splits - 1) * n)[i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (z0 + u < splits) s += v[u];
+    }
     reinterpret_cast<f32x4*>(dst)[i] = s;
   }
   for (size_t i = n4 * 4 + first; i < n; i += stride) {
