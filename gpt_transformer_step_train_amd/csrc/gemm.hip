@@ -194,9 +194,9 @@ template <typename T, bool KC, int ROWS, int BK_, int NTHR> struct Operand {
     }
   }
 
-  // Register path. load() only issues the loads (straight-line on interior tiles; on edge tiles
-  // out-of-range addresses are clamped to a valid one); store() zeroes the out-of-range elements
-  // of edge tiles and writes LDS, so no instruction between the two waits for the loads.
+  // Register path. load() only issues the loads (straight-line; out-of-range addresses are
+  // replaced by a valid one); store() zeroes the out-of-range elements of edge tiles and writes
+  // LDS, so no instruction between the two waits for the loads.
   // Per vector i of this thread: its row (M/N side) and k, relative to the tile.
   __device__ __forceinline__ static void coords(int i, int& row, int& k) {
     const int tid = threadIdx.x;
@@ -224,7 +224,8 @@ template <typename T, bool KC, int ROWS, int BK_, int NTHR> struct Operand {
   }
 
   __device__ __forceinline__ void load(const T* __restrict__ ptr, long ld, int row0, int nrows, int k0, int K) {
-    const bool inner = interior(row0, nrows, k0, K);
+    // one straight-line path for interior and edge tiles: a branch between two load sequences
+    // makes the compiler wait for the loads at the join, right after issuing them
 #pragma unroll
     for (int i = 0; i < NREG; ++i) {
       int row, k;
@@ -232,12 +233,8 @@ template <typename T, bool KC, int ROWS, int BK_, int NTHR> struct Operand {
       row += row0;
       k += k0;
       const size_t off = MODE == 0 ? (size_t)row * ld + k : (size_t)k * ld + row;
-      if (inner) {
-        r[i] = *reinterpret_cast<const u32x4*>(ptr + off);
-      } else {
-        const bool ok = MODE == 0 ? (row < nrows && k < K) : (k < K && row < nrows);
-        r[i] = *reinterpret_cast<const u32x4*>(ok ? ptr + off : ptr);
-      }
+      const bool ok = row < nrows && k < K;
+      r[i] = *reinterpret_cast<const u32x4*>(ok ? ptr + off : ptr);
     }
   }
 
