@@ -6,9 +6,11 @@
 //   y = (x - mu) * rstd * w + b,   rstd = 1/sqrt(var + eps)
 //   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)),  g = dy * w
 //   dw = sum_rows dy * xhat,  db = sum_rows dy
-// A row belongs to one wave64 or to one half-wave (whichever idles fewer lanes); 16-byte loads; row
-// statistics with DPP reductions (fp32).
-// Weight/bias gradients: per-block column partials in registers, then a fixed-order sum.
+// Forward: a row belongs to one wave64 or to one half-wave (whichever idles fewer lanes); backward:
+// one wave64 per row, two rows per wave at a time. 16-byte loads, row statistics with DPP
+// reductions (fp32).
+// Weight/bias gradients: per-block column partials in registers, then a fixed-order sum over the
+// blocks (here, or in a batched launch with the other column sums of the backward).
 #include "common.h"
 #include "kernels.h"
 
