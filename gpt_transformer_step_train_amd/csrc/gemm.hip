@@ -593,6 +593,9 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, int m0, int n0,
   }
 }
 
+// 32 zero bytes in global memory: the stand-in source of the bias prefetch when there is no bias
+static __device__ __attribute__((aligned(16))) uint32_t g_zero_chunk[8];
+
 template <typename T, int BM, int BN, bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(GemmArgs p0, int k_split,
                                                                                float* split_out0, GemmArgs p1,
@@ -640,6 +643,29 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // The epilogue's 8-column chunks of this lane: chunk it * 64 + lane of a 32-row slab is row
+  // (it * 64 + lane) / CPR, column chunk % CPR; a lane's column chunk repeats every BP chunks
+  // (1 when CPR divides 64).
+  constexpr int CPR = TN / 8;
+  constexpr int BP = CPR / gcd_c(64, CPR);
+  auto ccol = [&](int it) { return ((it * 64 + lane) % CPR) * 8; };
+  // The bias of those chunks is requested before the main loop (whose first wait covers it) from an
+  // unguarded address, since a load behind a branch is waited for at the branch join; without a
+  // bias, or with N not a whole number of chunks, the loads read a zero chunk instead.
+  constexpr bool BIAS_EPI = EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID || EPI == EPI_GELU_GRAD;
+  constexpr int BVEC = Elt<T>::VEC;
+  const bool bias_pf = BIAS_EPI && p.bias != nullptr && p.N % 8 == 0;
+  u32x4 braw[BP][8 / BVEC];
+  if constexpr (BIAS_EPI) {
+#pragma unroll
+    for (int bp = 0; bp < BP; ++bp) {
+      const int col = min(n0 + wn * TN + ccol(bp), p.N - 8);
+      const T* src = bias_pf ? reinterpret_cast<const T*>(p.bias) + col : reinterpret_cast<const T*>(g_zero_chunk);
+#pragma unroll
+      for (int h = 0; h < 8 / BVEC; ++h) braw[bp][h] = *reinterpret_cast<const u32x4*>(src + h * BVEC);
+    }
+  }
+
   const bool kfull = (kend - kbeg) % BK == 0;
   if constexpr (CF::OA::DIRECT && CF::OB::DIRECT) {
     if (kfull && m0 + BM <= p.M && n0 + BN <= p.N)
@@ -670,36 +696,28 @@ __global__ __launch_bounds__((Cfg<T, BM, BN, AKC, BKC>::NTHR)) void gemm_kernel(
   for (int e = 0; e < 8; ++e) cs[e] = 0.f;
   float* stage = reinterpret_cast<float*>(smem) + w * 32 * CF::EPI_LD;
   const int g = lane >> 5, l32 = lane & 31;
-  constexpr int CPR = TN / 8;             // 8-column chunks per staged row
-  constexpr int NIT = (32 * CPR) / 64;    // chunks per lane per slab
+  constexpr int NIT = (32 * CPR) / 64;    // chunks per lane per slab (CPR: chunks per staged row)
   static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
-  // chunk it * 64 + lane of a slab: row / CPR, column chunk % CPR; a lane's column chunk repeats
-  // every BP chunks (1 when CPR divides 64)
-  constexpr int BP = CPR / gcd_c(64, CPR);
-  auto ccol = [&](int it) { return ((it * 64 + lane) % CPR) * 8; };
   float bv[BP][8];
 #pragma unroll
   for (int bp = 0; bp < BP; ++bp) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) bv[bp][e] = 0.f;
-    const int col = n0 + wn * TN + ccol(bp);
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_GELU || EPI == EPI_RESID || EPI == EPI_GELU_GRAD) {
-      if (p.bias && col < p.N) {
-        const T* bias = reinterpret_cast<const T*>(p.bias) + col;
-        if (col + 8 <= p.N) {
-          constexpr int VEC = Elt<T>::VEC;
+    if constexpr (BIAS_EPI) {
+      if (bias_pf) {
 #pragma unroll
-          for (int h = 0; h < 8 / VEC; ++h) {
-            V16<T> t;
-            t.load(bias + h * VEC);
+        for (int h = 0; h < 8 / BVEC; ++h) {
+          V16<T> t;
+          t.unpack(braw[bp][h]);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) bv[bp][h * VEC + e] = t.v[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.N) bv[bp][e] = ld1(bias, e);
+          for (int e = 0; e < BVEC; ++e) bv[bp][h * BVEC + e] = t.v[e];
         }
+      } else if (p.bias) {  // N not a whole number of chunks: element loads
+        const int col = n0 + wn * TN + ccol(bp);
+        const T* bias = reinterpret_cast<const T*>(p.bias) + col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < p.N) bv[bp][e] = ld1(bias, e);
       }
     }
   }
