@@ -540,16 +540,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   const float c2 = LOG2E / sqrtf((float)HD);
 
   // K and V of this lane's key as B operands (S = Q K^T, dP = dO V^T)
+  // unguarded loads: a key past T reads the last row; its probabilities are masked (every query
+  // precedes it) and its dK, dV are not stored
   bf16x8 kf[4], vf[4];
+  const int krow = min(mykey, T - 1);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-    if (mykey < T) {
-      xk = *reinterpret_cast<const u32x4*>(base + (size_t)mykey * C3 + C + h * HD + 16 * s + 8 * g);
-      xv = *reinterpret_cast<const u32x4*>(base + (size_t)mykey * C3 + 2 * C + h * HD + 16 * s + 8 * g);
-    }
-    kf[s] = __builtin_bit_cast(bf16x8, xk);
-    vf[s] = __builtin_bit_cast(bf16x8, xv);
+    kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + (size_t)krow * C3 + C + h * HD + 16 * s + 8 * g));
+    vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + (size_t)krow * C3 + 2 * C + h * HD + 16 * s + 8 * g));
   }
   f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};  // rows = keys, cols = d
 
@@ -679,19 +677,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
   const int myq = qw0 + l32;
   const float c2 = LOG2E / sqrtf((float)HD);
 
-  bf16x8 qf[4], df[4];  // B operands: Q[myq], dO[myq]
+  // B operands Q[myq], dO[myq] by unguarded loads (a query past T reads the last row; its dS is
+  // masked and its dQ not stored)
+  bf16x8 qf[4], df[4];
+  const int qrow = min(myq, T - 1);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
-    if (myq < T) {
-      xq = *reinterpret_cast<const u32x4*>(base + (size_t)myq * C3 + h * HD + 16 * s + 8 * g);
-      xd = *reinterpret_cast<const u32x4*>(dbase + (size_t)myq * C + h * HD + 16 * s + 8 * g);
-    }
-    qf[s] = __builtin_bit_cast(bf16x8, xq);
-    df[s] = __builtin_bit_cast(bf16x8, xd);
+    qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + (size_t)qrow * C3 + h * HD + 16 * s + 8 * g));
+    df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dbase + (size_t)qrow * C + h * HD + 16 * s + 8 * g));
   }
-  const float L2 = myq < T ? lse[(size_t)bh * T + myq] * LOG2E : 0.f;
-  const float Dq = myq < T ? dvec[(size_t)bh * T + myq] : 0.f;
+  const size_t qi = (size_t)bh * T + qrow;
+  const float L2 = lse[qi] * LOG2E;
+  const float Dq = dvec[qi];
   f32x16 dq[2] = {zero16(), zero16()};  // rows = queries, cols = d
 
   const int kend = min(T, q0 + BQ);
