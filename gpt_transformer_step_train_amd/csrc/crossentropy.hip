@@ -155,7 +155,7 @@ hipError_t launch_count_targets(const int32_t* targets, int rows, int V, int acc
 hipError_t launch_cross_entropy(DType dt, int rows, int V, int ld, void* logits, const int32_t* targets,
                                 const float* dloss, float* losses, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (ld % (dt == DT_BF16 ? 8 : 4)) return hipErrorInvalidValue;
+  if (V <= 0 || ld < V || ld % (dt == DT_BF16 ? 8 : 4)) return hipErrorInvalidValue;
   return dt == DT_BF16 ? ce_t<bf16>(rows, V, ld, logits, targets, dloss, losses, s)
                        : ce_t<float>(rows, V, ld, logits, targets, dloss, losses, s);
 }

@@ -86,7 +86,8 @@ int gpt2op_attention_backward_colsum(int dtype, int B, int T, int H, int hs, con
 
 /* Softmax cross-entropy over the first V of ld columns of each row. losses[rows] (float).
  * When dloss != NULL (device float scalar), logits are overwritten by (softmax - onehot)*dloss,
- * with 0 in padded columns and on rows whose target is < 0. */
+ * with 0 in padded columns and on rows whose target is < 0. Requires 1 <= V <= ld and ld a
+ * multiple of 8 (bf16) or 4 (fp32), else GPT2_EINVAL. */
 int gpt2op_cross_entropy(int dtype, int rows, int V, int ld, void* logits, const int32_t* targets,
                          const float* dloss, float* losses, void* stream);
 

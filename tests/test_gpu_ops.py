@@ -413,7 +413,9 @@ def test_stochastic_round_matches_oracle_bit_for_bit(t, index0):
 # ---------------------------------------------------------------------------- cross-entropy
 
 @pytest.mark.parametrize("dt", DTS)
-@pytest.mark.parametrize("rows,V,ld", [(37, 1000, 1008), (8, 50257, 50304), (36, 2, 8)])
+@pytest.mark.parametrize("rows,V,ld", [(37, 1000, 1008), (8, 50257, 50304), (36, 2, 8),
+                                      # one class: loss 0 and gradient 0; a row with no padded columns
+                                      (5, 1, 8), (3, 57344, 57344)])
 def test_cross_entropy(dt, rows, V, ld):
     rng = np.random.default_rng(rows + V)
     logits = np.zeros((rows, ld))
@@ -436,6 +438,15 @@ def test_cross_entropy(dt, rows, V, ld):
     d = h64(ld_)
     assert rel(d[:, :V], d_ref) <= tol(dt, 1e-5, 8e-3)
     assert np.all(d[:, V:] == 0.0)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("V,ld", [(0, 8), (9, 8), (16, 12)])
+def test_cross_entropy_rejects_bad_shapes(dt, V, ld):
+    x = torch.zeros(2 * 16, dtype=torch.float32, device="cuda")
+    losses = torch.empty(2, dtype=torch.float32, device="cuda")
+    rc = bd.load().gpt2op_cross_entropy(dt, 2, V, ld, x.data_ptr(), None, None, losses.data_ptr(), stream())
+    assert rc == bd.GPT2_EINVAL
 
 
 # ---------------------------------------------------------------------------- encoder
