@@ -252,6 +252,9 @@ static int ln_bwd_blocks(int rows) { return rows > 0 ? cdiv(rows, cdiv(rows, LNB
 // half-waves (then a full wave would idle half its lanes on the last vector) and that fits 8
 // vectors per lane; else 64. Returns the vectors per lane in *nv. (The backward keeps 64: with
 // two rows per wave it measured slower at C = 768, bf16.)
+// elements per 16-byte vector
+static int Elt16(DType dt) { return dt == DT_BF16 ? 8 : 4; }
+
 static int ln_fwd_lanes(int nvec, int* nv) {
   const int h = cdiv(nvec, 32);
   if ((h & 1) && h <= 8) {
@@ -290,6 +293,7 @@ static hipError_t ln_fwd_t(int rows, int C, const void* x, const void* w, const 
 
 hipError_t launch_layernorm_fwd(DType dt, int rows, int C, const void* x, const void* w, const void* b, void* y,
                                 float* mean, float* rstd, hipStream_t s) {
+  if (C <= 0 || C % Elt16(dt)) return hipErrorInvalidValue;  // rows move as 16-byte vectors
   if (rows <= 0) return hipSuccess;
   return dt == DT_BF16 ? ln_fwd_t<bf16>(rows, C, x, w, b, y, mean, rstd, s)
                        : ln_fwd_t<float>(rows, C, x, w, b, y, mean, rstd, s);
@@ -328,7 +332,7 @@ hipError_t launch_layernorm_bwd(DType dt, int rows, int C, const void* dy, const
                                 float* dsum, int accumulate, float* partial, size_t partial_floats, hipStream_t s,
                                 ColsumDefer* defer) {
   const size_t pf = layernorm_bwd_partial_floats(rows, C);
-  if ((size_t)4 * C * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
+  if (C <= 0 || C % Elt16(dt) || (size_t)4 * C * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
   // partials left for a batched finish when the caller offers room for them
   bool finish = true;
   if (defer) {

@@ -55,7 +55,9 @@ int gpt2op_gemm_colsum(int dtype, int a_kcontig, int b_kcontig, int epilogue, in
 int gpt2op_stochastic_round(const float* x, uint16_t* y, uint64_t n, uint64_t seed, int32_t t, uint64_t index0,
                             void* stream);
 
-/* LayerNorm over rows of width C (eps 1e-5, biased variance): y, mean[rows], rstd[rows]. b may be NULL. */
+/* LayerNorm over rows of width C (eps 1e-5, biased variance): y, mean[rows], rstd[rows]. b may be NULL.
+ * C must be a positive multiple of 8 (bf16) or 4 (fp32), at most 4096, else GPT2_EINVAL (both
+ * directions). */
 int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,
                              float* mean, float* rstd, void* stream);
 /* dres += dx; dw, db (float [C]) = or += column sums (accumulate). db may be NULL.

@@ -272,6 +272,22 @@ def test_gemm_f32_weight_gradient_split_k_accumulate(dt, M, N, K):
 # ---------------------------------------------------------------------------- LayerNorm
 
 @pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("C", [0, 6, 8192])
+def test_layernorm_rejects_bad_widths(dt, C):
+    rows, cap = 2, 2 * 8192 + 4096
+    # every pointer sits 4 KiB into a buffer that would hold rows x 8192 elements
+    buf = [torch.zeros(cap, dtype=torch.float32, device="cuda") for _ in range(8)]
+    p = [t.data_ptr() + 4096 for t in buf]
+    part = torch.zeros(int(bd.load().gpt2op_layernorm_backward_scratch(rows, 8192)) + 1024, dtype=torch.float32,
+                       device="cuda")
+    lib = bd.load()
+    assert lib.gpt2op_layernorm_forward(dt, rows, C, p[0], p[1], p[2], p[3], p[4], p[5], stream()) == bd.GPT2_EINVAL
+    assert lib.gpt2op_layernorm_backward(dt, rows, C, p[0], p[3], p[1], p[4], p[5], p[6], p[7], None, None, 0,
+                                         part.data_ptr(), stream()) == bd.GPT2_EINVAL
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("rows,C,has_b", [(37, 16, True), (300, 768, True), (65, 200, False), (1030, 1600, True)])
 def test_layernorm_forward_backward(dt, rows, C, has_b):
     if dt == bd.GPT2_BF16 and C % 8:
