@@ -43,7 +43,7 @@ hipError_t launch_encoder_fwd(DType dt, int B, int T, int C, int V, const int32_
   const int BT = B * T;
   if (BT <= 0) return hipSuccess;
   const int vec = dt == DT_BF16 ? 8 : 4;
-  if (C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
+  if (C <= 0 || C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
   const int blocks = std::min(cdiv((long)BT * (C / vec), 256), 8192);
   if (dt == DT_BF16)
     encoder_fwd_kernel<bf16><<<blocks, 256, 0, s>>>(BT, T, C, V, tok, reinterpret_cast<const bf16*>(wte),
@@ -270,12 +270,13 @@ hipError_t launch_encoder_bwd(DType dt, int B, int T, int maxT, int C, const uin
                               hipStream_t s) {
   const int BT = B * T;
   if (BT <= 0) return hipSuccess;
+  if (T > maxT) return hipErrorInvalidValue;  // positions past the position table
   const int nch = cdiv(BT, CH);
   if (encoder_bwd_partial_floats(BT, C) > partial_floats) return hipErrorInvalidValue;
   float* ph = partial;
   float* pt = partial + (size_t)nch * C;
   const int vec = dt == DT_BF16 ? 8 : 4;
-  if (C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
+  if (C <= 0 || C % vec) return hipErrorInvalidValue;  // rows move as 16-byte vectors
   dim3 g1(nch, cdiv(C / 4, 64));
   if (dt == DT_BF16) {
     auto D = reinterpret_cast<const bf16*>(dout);

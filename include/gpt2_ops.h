@@ -98,7 +98,9 @@ int gpt2op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t*
                            const void* wpe, void* out, int* err, void* stream);
 /* dwte[tok[p]] += dout[p] for every position p (deterministic order); dwpe[t] = or += sum_b dout[b,t]
  * (rows t >= T of the max_seq rows are set to 0 / left). keys: uint32 scratch [B*T];
- * partial: float scratch of gpt2op_encoder_backward_scratch(B*T, C) elements. */
+ * partial: float scratch of gpt2op_encoder_backward_scratch(B*T, C) elements. Both directions
+ * require C to be a positive multiple of 8 (bf16) or 4 (fp32), the backward T <= max_seq, else
+ * GPT2_EINVAL. */
 int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok,
                             const void* dout, float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys,
                             float* partial, void* stream);

@@ -468,6 +468,25 @@ def test_cross_entropy_rejects_bad_shapes(dt, V, ld):
 # ---------------------------------------------------------------------------- encoder
 
 @pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("T,maxT,C", [(8, 4, 16), (4, 4, 0), (4, 4, 6)])
+def test_encoder_rejects_bad_shapes(dt, T, maxT, C):
+    B, V, lib = 2, 10, bd.load()
+    tok = torch.zeros(B * T, dtype=torch.int32, device="cuda")
+    # buffers sized for C = 16, so every access of a shape that were accepted stays inside them
+    big = [torch.zeros(B * T * 16 + V * 16 + 64, dtype=torch.float32, device="cuda") for _ in range(4)]
+    keys = torch.zeros(B * T, dtype=torch.int32, device="cuda")
+    part = torch.zeros(int(lib.gpt2op_encoder_backward_scratch(B * T, 16)) + 64, dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if C != 16:
+        assert lib.gpt2op_encoder_forward(dt, B, T, C, V, tok.data_ptr(), big[0].data_ptr(), big[1].data_ptr(),
+                                          big[2].data_ptr(), err.data_ptr(), stream()) == bd.GPT2_EINVAL
+    assert lib.gpt2op_encoder_backward(dt, B, T, maxT, C, V, tok.data_ptr(), big[2].data_ptr(), big[0].data_ptr(),
+                                       big[1].data_ptr(), 0, keys.data_ptr(), part.data_ptr(),
+                                       stream()) == bd.GPT2_EINVAL
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("B,T,maxT,C,V,p0", [(4, 64, 80, 128, 500, 0.14), (4, 256, 256, 64, 300, 0.5),
                                             (12, 3, 3, 16, 2, 0.5),
                                             # one run over (nearly) every chunk; V = 1: a single token
