@@ -755,7 +755,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
 // =====================================================================================
 hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,
                                 hipStream_t s) {
-  if (B * T <= 0) return hipSuccess;
+  if (B < 0 || T < 0 || H < 1) return hipErrorInvalidValue;
+  if (B == 0 || T == 0) return hipSuccess;
   if (dt == DT_BF16) {
     if (hs != HD) return hipErrorInvalidValue;
     dim3 grid(cdiv(T, BQ), B * H);
@@ -781,7 +782,8 @@ int attention_bias_partial_rows(int B, int T) { return B * cdiv(T, BQ); }
 hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const void* qkv, const void* out,
                                 const void* dout, const float* lse, void* dqkv, float* dvec, int parts,
                                 hipStream_t s, float* cs) {
-  if (B * T <= 0) return hipSuccess;
+  if (B < 0 || T < 0 || H < 1) return hipErrorInvalidValue;
+  if (B == 0 || T == 0) return hipSuccess;
   const int BT = B * T;
   if (dt == DT_BF16) {
     if (hs != HD) return hipErrorInvalidValue;

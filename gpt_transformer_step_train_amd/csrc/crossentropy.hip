@@ -26,7 +26,7 @@ __global__ __launch_bounds__(1024) void count_targets_kernel(const int32_t* __re
   for (int i = threadIdx.x; i < rows; i += 1024) {
     const int t = targets[i];
     if (t >= 0 && t < V) c += 1.f;
-    if (t >= V) bad = true;
+    if (t >= V || t < -1) bad = true;  // -1 marks an ignored position; anything else outside [0, V) is an error
   }
   if (bad) atomicOr(err, 2);
   const float n = block_sum<16>(c, red);

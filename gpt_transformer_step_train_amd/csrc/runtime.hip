@@ -1153,16 +1153,31 @@ int gpt2_load(const char* path, int32_t* t, uint64_t* cursor) {
   ckpt_arch(want);
   if (memcmp(arch, want, sizeof arch) != 0 || n != g.N)
     return fail(GPT2_EIO, "gpt2_load: %s holds a different architecture", path);
-  std::vector<float> buf(std::min<size_t>(CKPT_CHUNK, g.N));
-  std::vector<uint16_t> tmp;
-  for (size_t i = 0; i < g.N; i += CKPT_CHUNK) {
-    const size_t k = std::min(CKPT_CHUNK, g.N - i);
-    if (fread(buf.data(), 4, k, file.f) != k) return fail(GPT2_EIO, "checkpoint: file too short");
-    RUN(params_from_host(buf.data(), i, k, tmp));
+  // the whole file must be there before anything on the device is overwritten
+  const long body = ftell(file.f);
+  if (body < 0 || fseek(file.f, 0, SEEK_END) != 0) return fail(GPT2_EIO, "gpt2_load: cannot seek in %s", path);
+  const long end = ftell(file.f);
+  if (end < 0 || (uint64_t)(end - body) < (uint64_t)3 * g.N * 4 || fseek(file.f, body, SEEK_SET) != 0)
+    return fail(GPT2_EIO, "gpt2_load: %s is shorter than its header says", path);
+  // from here a failure leaves the model half restored: it is marked not ready
+  auto load_body = [&]() -> int {
+    std::vector<float> buf(std::min<size_t>(CKPT_CHUNK, g.N));
+    std::vector<uint16_t> tmp;
+    for (size_t i = 0; i < g.N; i += CKPT_CHUNK) {
+      const size_t k = std::min(CKPT_CHUNK, g.N - i);
+      if (fread(buf.data(), 4, k, file.f) != k) return fail(GPT2_EIO, "checkpoint: file too short");
+      RUN(params_from_host(buf.data(), i, k, tmp));
+    }
+    RUN(read_dev(file.f, g.m, g.N, buf));
+    RUN(read_dev(file.f, g.v, g.N, buf));
+    RUN(params_changed());
+    return GPT2_OK;
+  };
+  if (load_body() != GPT2_OK) {
+    g.ready = false;
+    g_err += " (the model is no longer usable: gpt2_init again)";
+    return g_status;
   }
-  RUN(read_dev(file.f, g.m, g.N, buf));
-  RUN(read_dev(file.f, g.v, g.N, buf));
-  RUN(params_changed());
   g.seed = seed;
   g.micro = 0;
   g.fwd_targets = false;
@@ -1214,10 +1229,34 @@ static int op_ret(hipError_t e) {
   return ok();
 }
 
+// Operand checks of the GEMM ops: the tiles move 16-byte vectors, so every leading dimension must be a
+// whole number of them (8 bf16 or 4 fp32 elements; the EPI_F32 output is fp32) and every pointer
+// 16-byte aligned; a leading dimension must also cover the row it strides over.
+static const char* gemm_op_check(int dtype, int a_kc, int b_kc, int epilogue, int M, int N, int K, const void* A,
+                                 int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                                 const void* bias, const void* aux, int64_t ldaux, const void* C2) {
+  if (dtype != GPT2_FP32 && dtype != GPT2_BF16) return "dtype must be GPT2_FP32 or GPT2_BF16";
+  if (epilogue < 0 || epilogue > 6 || M < 0 || N < 0 || K < 0) return "bad epilogue or negative size";
+  if (M == 0 || N == 0) return nullptr;
+  const int64_t vin = dtype == GPT2_BF16 ? 8 : 4, vout = epilogue == EPI_F32 ? 4 : vin;
+  if (!A || !B || !C) return "null operand";
+  if (lda % vin || ldb % vin || ldc % vout) return "leading dimensions must be multiples of 16 bytes";
+  if (lda < (a_kc ? K : M) || ldb < (b_kc ? K : N) || ldc < N) return "leading dimension smaller than the row";
+  const bool needs_aux = epilogue == EPI_RESID || epilogue == EPI_GELU_BWD || epilogue == EPI_MUL;
+  const bool needs_c2 = epilogue == EPI_GELU || epilogue == EPI_GELU_GRAD;
+  if (needs_aux && (!aux || ldaux % vin || ldaux < N)) return "this epilogue needs aux with a valid leading dimension";
+  if (needs_c2 && !C2) return "this epilogue needs C2";
+  for (const void* ptr : {A, B, C, bias, aux, C2})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return "pointers must be 16-byte aligned";
+  return nullptr;
+}
+
 int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias, const void* aux,
                 int64_t ldaux, void* C2, int accumulate, float* scratch, uint64_t scratch_floats, void* stream) {
-  if (epilogue < 0 || epilogue > 6 || M < 0 || N < 0 || K < 0) return fail(GPT2_EINVAL, "bad gemm arguments");
+  if (const char* e = gemm_op_check(dtype, a_kcontig, b_kcontig, epilogue, M, N, K, A, lda, B, ldb, C, ldc, bias, aux,
+                                    ldaux, C2))
+    return fail(GPT2_EINVAL, "gemm: %s", e);
   GemmArgs a{};
   a.M = M;
   a.N = N;
@@ -1241,8 +1280,10 @@ int gpt2op_gemm_colsum(int dtype, int a_kcontig, int b_kcontig, int epilogue, in
                        int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias,
                        const void* aux, int64_t ldaux, void* C2, float* colsum, int colsum_accumulate,
                        float* scratch, uint64_t scratch_floats, void* stream) {
-  if (epilogue < 0 || epilogue > 6 || epilogue == EPI_F32 || M < 0 || N < 0 || K < 0 || !colsum)
-    return fail(GPT2_EINVAL, "bad gemm_colsum arguments");
+  if (epilogue == EPI_F32 || !colsum) return fail(GPT2_EINVAL, "bad gemm_colsum arguments");
+  if (const char* e = gemm_op_check(dtype, a_kcontig, b_kcontig, epilogue, M, N, K, A, lda, B, ldb, C, ldc, bias, aux,
+                                    ldaux, C2))
+    return fail(GPT2_EINVAL, "gemm_colsum: %s", e);
   if (!scratch || (uint64_t)cdiv(M, 128) * 2 * N > scratch_floats)
     return fail(GPT2_EINVAL, "gemm_colsum needs scratch of ceil(M/128)*2*N floats");
   GemmArgs a{};
@@ -1339,6 +1380,10 @@ int gpt2op_copy(void* dst, const void* src, uint64_t bytes, void* stream) {
 int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok, const void* dout,
                             float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys, float* partial, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the shapes the scatter refuses are refused before the sort writes the keys
+  const int vec = dtype == GPT2_BF16 ? 8 : 4;
+  if (B < 0 || T < 0 || V < 1 || C <= 0 || C % vec || T > max_seq)
+    return fail(GPT2_EINVAL, "encoder_backward: need B, T >= 0, V >= 1, C a positive multiple of 16 bytes, T <= max_seq");
   hipError_t e = launch_encoder_sort(B * T, V, tok, keys, s);
   if (e != hipSuccess) return op_ret(e);
   return op_ret(launch_encoder_bwd(to_dt(dtype), B, T, max_seq, C, keys, dout, dwte, dwpe, accumulate_wpe, partial,

@@ -79,23 +79,39 @@ typedef struct {
 uint64_t gpt2_workspace_bytes(const gpt2_config* cfg);
 
 /* Validate cfg, carve the workspace, initialise the parameters, zero m and v.
+ * Defined by "Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南 (flag -e: a GPT-2 of a
+ * given depth initialised from scratch; flags -b -t: the micro-batch B x T) and section 代码 (all GPU
+ * memory is allocated once at start-up and stays fixed for the run). The init recipe below is the
+ * reading of BASELINE's "normal(0, 0.02)" (the pages give none).
  * Init: every 2-D tensor in layout order draws N(0, 0.02^2) from one stream (SplitMix64 seeded
  * with `seed`, Box-Muller in double, rounded to fp32); biases 0; LayerNorm weights 1.
  * Synchronous. Replaces any previous model. */
 int gpt2_init(const gpt2_config* cfg, uint64_t seed);
 
 /* Forward pass on device int32 tokens [B*T] (row-major [B][T]) and targets [B*T].
+ * Defined by "Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 代码解剖 (the layer
+ * order: encoder, L x [LayerNorm, QKV matmul, attention, projection, LayerNorm, MLP], final
+ * LayerNorm, classifier, then the loss), with the attention softmax(Q K^T / sqrt(d_k)) V of the LLM
+ * primer page, causal.
+ * Errors: GPT2_ERANGE when a token is outside [0, V) or a target outside [-1, V) (the step is not
+ * usable; call gpt2_forward again with valid ids).
  * targets == NULL: logits only (kept for gpt2_get_logits), returns NaN with status OK.
  * target < 0 is ignored; the loss is the mean of -log softmax(logits)[target] over valid targets
  * (0 when there is none). Synchronous: returns the loss, or NaN on error (see gpt2_last_status). */
 float gpt2_forward(const int32_t* tokens, const int32_t* targets);
 
-/* Backward pass of the last forward (which must have had targets). The first backward after
+/* Backward pass of the last forward (which must have had targets), written in the reverse order
+ * of the forward starting from the gradient at the logits ("Karpathy 的 llm.c：从零理解大模型训练的
+ * C/CUDA 实现", section 代码解剖), with gradient accumulation over micro-steps to the total batch
+ * ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南, flag -d). The first backward after
  * gpt2_init or an update overwrites the gradients, later ones add (gradient accumulation; each
  * micro-step's loss is scaled by 1 / grad_accum). Asynchronous. */
 int gpt2_backward(void);
 
-/* AdamW update with t >= 1 (bias correction), decoupled weight decay `wd` on 2-D tensors only,
+/* AdamW update ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672": section 训练 allocates AdamW's m and
+ * v and an fp32 master copy; section 参数指南, flag -c: decay on 2-D weights only; one kernel for all
+ * parameters: "Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 性能对比).
+ * t >= 1 (bias correction), decoupled weight decay `wd` on 2-D tensors only,
  * after scaling the gradients by min(1, grad_clip / ||g||) when grad_clip > 0.
  * In GPT2_BF16 mode also rewrites the bf16 parameter copy: rounded to nearest even from the fp32
  * master, or, with no_master, rounded stochastically: element i (flat layout index) of update t
@@ -123,7 +139,10 @@ int gpt2_skip_update(void);
  * File: the 8 bytes "GPT2CKPT", uint32 version 1, the 8 int32 architecture fields above, uint64
  * N, int32 t, uint64 cursor, uint64 seed, then N floats each of parameters, m and v
  * (little-endian).
- * Synchronous. GPT2_EIO on a file error, a short file or a mismatch. */
+ * Synchronous. GPT2_EIO on a file error, a short file or a mismatch; the file's length is checked
+ * before anything on the device is overwritten, so then the model is unchanged. Only a read or
+ * runtime error after that check (e.g. the file shrinking underneath) leaves the model half
+ * restored: it is then marked not ready and must be initialised again. */
 int gpt2_save(const char* path, int32_t t, uint64_t cursor);
 int gpt2_load(const char* path, int32_t* t, uint64_t* cursor);
 

@@ -6,8 +6,8 @@
  * GPT2_FP32 (float buffers) or GPT2_BF16 (bf16 buffers, 16-bit storage); fp32 statistics and
  * gradients of parameters are always float. `stream` is a hipStream_t. Every call returns
  * GPT2_OK or GPT2_EINVAL (unsupported shape or argument) / GPT2_EHIP (launch failure).
- * Row-major layouts throughout; all leading dimensions and tensor widths must be multiples of
- * 8 elements (16 bytes) and every pointer 16-byte aligned.
+ * Row-major layouts throughout; leading dimensions must be multiples of 16 bytes (8 bf16 or 4
+ * fp32 elements) and pointers 16-byte aligned (the GEMM ops check this and return GPT2_EINVAL).
  */
 #ifndef GPT2_OPS_H
 #define GPT2_OPS_H
@@ -33,7 +33,11 @@ extern "C" {
  * A(m,k) = A[m*lda + k] if a_kcontig else A[k*lda + m]; B(n,k) = B[n*ldb + k] if b_kcontig
  * else B[k*ldb + n]. bias [N] (dtype) may be NULL. aux has leading dimension ldaux.
  * scratch (float, scratch_floats) enables deterministic split-K for GPT2_EPI_F32; may be NULL.
- * Linear layer forward is (a_kcontig=1, b_kcontig=1), input-gradient (1, 0), weight-gradient (0, 0). */
+ * Linear layer forward is (a_kcontig=1, b_kcontig=1), input-gradient (1, 0), weight-gradient (0, 0).
+ * Checked before any launch (else GPT2_EINVAL): M, N, K >= 0; A, B, C non-null when M, N > 0;
+ * lda >= (a_kcontig ? K : M), ldb >= (b_kcontig ? K : N), ldc >= N; lda, ldb, ldaux multiples of 16
+ * bytes of dtype, ldc of its output type (float for GPT2_EPI_F32); aux (and ldaux >= N) present for
+ * RESID / GELU_BWD / MUL, C2 for GELU / GELU_GRAD; A, B, C, bias, aux, C2 16-byte aligned. */
 int gpt2op_gemm(int dtype, int a_kcontig, int b_kcontig, int epilogue, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const void* bias, const void* aux,
                 int64_t ldaux, void* C2, int accumulate, float* scratch, uint64_t scratch_floats, void* stream);
@@ -56,8 +60,9 @@ int gpt2op_stochastic_round(const float* x, uint16_t* y, uint64_t n, uint64_t se
                             void* stream);
 
 /* LayerNorm over rows of width C (eps 1e-5, biased variance): y, mean[rows], rstd[rows]. b may be NULL.
- * C must be a positive multiple of 8 (bf16) or 4 (fp32), at most 4096, else GPT2_EINVAL (both
- * directions). */
+ * C must be a positive multiple of 8 (bf16) or 4 (fp32), at most 4096 in bf16 and 2048 in fp32
+ * (one row is held in one wave's registers: up to 8 16-byte vectors per lane), else GPT2_EINVAL
+ * (both directions). */
 int gpt2op_layernorm_forward(int dtype, int rows, int C, const void* x, const void* w, const void* b, void* y,
                              float* mean, float* rstd, void* stream);
 /* dres += dx; dw, db (float [C]) = or += column sums (accumulate). db may be NULL.
@@ -71,7 +76,8 @@ uint64_t gpt2op_layernorm_backward_scratch(int rows, int C);
 
 /* Causal attention of qkv [B,T,3C] (Q|K|V, head h at columns h*hs of each third) into
  * out [B,T,C] and lse [B,H,T] (natural log of the softmax denominators). bf16 requires hs == 64;
- * fp32 supports hs in {4, 8, 16, 32, 64}. */
+ * fp32 supports hs in {4, 8, 16, 32, 64}. B, T >= 0 (0: nothing to do) and H >= 1, else
+ * GPT2_EINVAL (all attention ops). */
 int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,
                              void* stream);
 /* dqkv [B,T,3C] (fully written) from qkv, out, dout, lse; dvec: float scratch [B*H*T]. */
@@ -100,7 +106,7 @@ int gpt2op_encoder_forward(int dtype, int B, int T, int C, int V, const int32_t*
  * (rows t >= T of the max_seq rows are set to 0 / left). keys: uint32 scratch [B*T];
  * partial: float scratch of gpt2op_encoder_backward_scratch(B*T, C) elements. Both directions
  * require C to be a positive multiple of 8 (bf16) or 4 (fp32), the backward T <= max_seq, else
- * GPT2_EINVAL. */
+ * GPT2_EINVAL; the backward checks its shapes before the sort writes `keys`. */
 int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok,
                             const void* dout, float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys,
                             float* partial, void* stream);

@@ -4,6 +4,9 @@ Calls only oracle/ (and the seeded input generators). Run from the repository ro
     python tests/golden/make_goldens.py cfg2     # GPT-2 124M fp32, B=4: one step   (~2 min)
     python tests/golden/make_goldens.py cfg3     # GPT-2 124M, B=16: 10 updates     (~45 min)
     python tests/golden/make_goldens.py seq350 seq1558   # initial loss of one sequence (~2 + 6 min)
+    python tests/golden/make_goldens.py cfg3grad  # GPT-2 124M, B=16: gradients at init    (~3 min)
+    python tests/golden/make_goldens.py grad1558  # GPT-2 1558M, one sequence: gradients  (~10 min, ~48 GB)
+    python tests/golden/make_goldens.py cfg4      # GPT-2 350M, B=16: 10 updates          (~1.5 h)
 
 cfg2 -> tests/golden/gpt2_124m_fp32_b4_step1.npz: the loss, the pre-clip gradient norm, and
         for every tensor its max |g| plus g, and theta/m/v after one AdamW update, at 64
@@ -12,6 +15,12 @@ cfg3 -> tests/golden/gpt2_124m_b16_10steps.json: the per-update mean losses and 
         10 updates with lr 6e-4, betas (0.9, 0.95), eps 1e-8, wd 0.1, clip 1.0.
 seq350 / seq1558 -> tests/golden/gpt2_{350m,1558m}_seq0_init_loss.json: the mean loss at init of
         the first sequence (T=1024) of micro-step 0 (the first row of the B=16 batch).
+cfg3grad -> tests/golden/gpt2_124m_b16_step1_grads.npz: the loss, the gradient norm and, per
+        tensor, max |g| and g at 64 seeded sample positions, at init on micro-step 0 (B=16).
+grad1558 -> tests/golden/gpt2_1558m_seq0_grads.npz: the same for the first sequence (B=1, T=1024)
+        of GPT-2 1558M at init.
+cfg4 -> tests/golden/gpt2_350m_b16_10steps.json: the per-update mean losses and norms of 10 updates
+        of GPT-2 350M at B=16 with the hyper-parameters of cfg3.
 Inputs: parameters from the seed-1337 normal(0, 0.02) init, Zipf(1.1) token stream of seed 42
 (micro-step s uses stream positions s*(B*T+1) ...).
 """
@@ -92,6 +101,46 @@ def make_cfg3():
                       f, indent=1)
 
 
+def grad_golden(cfg, B, fname):
+    """Loss, norm, per-tensor max |g| and sampled g of one forward + backward at init (micro-step 0)."""
+    p = init(cfg)
+    tok, tgt = synth.zipf_batch(cfg.vocab, B, cfg.max_seq, 0)
+    t0 = time.time()
+    loss, g = O.forward_backward(cfg, p, tok, tgt)
+    del p
+    norm = O.grad_norm(g)
+    print(f"{fname}: loss {loss:.8f} norm {norm:.6f} ({time.time() - t0:.0f} s)", flush=True)
+    pos = sample_positions(cfg)
+    offs = np.cumsum([0] + [int(np.prod(s)) for _, s in O.param_layout(cfg)])
+    gmax = np.array([np.abs(g[offs[i]:offs[i + 1]]).max() for i in range(len(pos))])
+    flat_pos = np.concatenate(pos)
+    np.savez_compressed(os.path.join(HERE, fname), loss=loss, norm=norm, gmax=gmax, positions=flat_pos,
+                        counts=np.array([len(q) for q in pos]), g=g[flat_pos])
+
+
+def make_cfg4():
+    cfg, B, T, steps = O.CFG_350M, 16, 1024, 10
+    p = init(cfg)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    lr, b1, b2, eps, wd, clip = 6e-4, 0.9, 0.95, 1e-8, 0.1, 1.0
+    losses, norms = [], []
+    for s in range(steps):
+        t0 = time.time()
+        tok, tgt = synth.zipf_batch(cfg.vocab, B, T, s)
+        loss, g = O.forward_backward(cfg, p, tok, tgt)
+        p, m, v, norm = O.adamw_update(cfg, p, g, m, v, lr, b1, b2, eps, wd, s + 1, clip)
+        del g
+        losses.append(loss)
+        norms.append(norm)
+        print(f"cfg4 step {s + 1}: loss {loss:.6f} norm {norm:.4f} ({time.time() - t0:.0f} s)", flush=True)
+        with open(os.path.join(HERE, "gpt2_350m_b16_10steps.json"), "w") as f:
+            json.dump({"config": "GPT-2 350M, B=16, T=1024, Zipf(1.1) seed 42, init seed 1337",
+                       "hyper": dict(lr=lr, b1=b1, b2=b2, eps=eps, wd=wd, clip=clip),
+                       "losses": losses, "norms": norms, "complete": len(losses) == steps},
+                      f, indent=1)
+
+
 def make_seq(cfg, tag):
     p = init(cfg)
     tok, tgt = synth.zipf_batch(cfg.vocab, 1, cfg.max_seq, 0)
@@ -106,4 +155,7 @@ def make_seq(cfg, tag):
 if __name__ == "__main__":
     for what in sys.argv[1:]:
         {"cfg2": make_cfg2, "cfg3": make_cfg3, "seq350": lambda: make_seq(O.CFG_350M, "350m"),
-         "seq1558": lambda: make_seq(O.CFG_1558M, "1558m")}[what]()
+         "seq1558": lambda: make_seq(O.CFG_1558M, "1558m"),
+         "cfg3grad": lambda: grad_golden(O.CFG_124M, 16, "gpt2_124m_b16_step1_grads.npz"),
+         "grad1558": lambda: grad_golden(O.CFG_1558M, 1, "gpt2_1558m_seq0_grads.npz"),
+         "cfg4": make_cfg4}[what]()

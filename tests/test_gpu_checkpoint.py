@@ -55,3 +55,33 @@ def test_load_rejects_other_architecture_and_bad_files(tmp_path, gpu_lib):
     m2 = bd.Model(1, 2, 128, 500, 512, 128, 2, 32, bd.GPT2_BF16)  # other max_seq: other wpe
     assert bd.gpt2_load(path)[0] == bd.GPT2_EIO
     del m, m2
+
+
+def test_truncated_checkpoint_leaves_the_model_unchanged(tmp_path, gpu_lib):
+    """A file whose header is whole but whose body is cut short is refused before any device
+    write: parameters and AdamW state stay as they were and the model stays usable."""
+    import torch
+    m = bd.Model(1, 2, 128, 500, 512, 64, 2, 32, bd.GPT2_BF16, grad_clip=1.0)
+    tok = torch.zeros(64, dtype=torch.int32, device="cuda")
+    m.forward(tok, tok)
+    m.backward()
+    m.step(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    path = tmp_path / "a.ckpt"
+    bd.check(bd.gpt2_save(path, 1, 1), "gpt2_save")
+    p_saved = m.params()
+    m.forward(tok, tok)
+    m.backward()
+    m.step(1e-3, 0.9, 0.95, 1e-8, 0.1, 2)
+    p_now, (m_now, v_now) = m.params(), m.adam_state()
+    assert not np.array_equal(p_now, p_saved)
+    raw = path.read_bytes()
+    for cut in (len(raw) - 4, len(raw) - 4 * m.n - 16, 200):
+        (tmp_path / "cut.ckpt").write_bytes(raw[:cut])
+        assert bd.gpt2_load(tmp_path / "cut.ckpt")[0] == bd.GPT2_EIO
+        assert np.array_equal(m.params(), p_now)
+        mm, vv = m.adam_state()
+        assert np.array_equal(mm, m_now) and np.array_equal(vv, v_now)
+    assert np.isfinite(m.forward(tok, tok))  # still usable
+    rc, t, cur = bd.gpt2_load(path)
+    assert (rc, t, cur) == (bd.GPT2_OK, 1, 1)
+    assert np.array_equal(m.params(), p_saved)

@@ -307,6 +307,10 @@ def test_error_paths():
     badt[0, 0] = cfg.vocab
     loss = bd.gpt2_forward(cuda_i32(tok), cuda_i32(badt))
     assert math.isnan(loss) and bd.gpt2_last_status() == bd.GPT2_ERANGE
+    badt = tgt.copy()
+    badt[1, 5] = -7  # only -1 marks an ignored position
+    loss = bd.gpt2_forward(cuda_i32(tok), cuda_i32(badt))
+    assert math.isnan(loss) and bd.gpt2_last_status() == bd.GPT2_ERANGE
     loss = bd.gpt2_forward(cuda_i32(tok), cuda_i32(tgt))
     assert math.isfinite(loss)
     assert bd.gpt2_backward() == 0

@@ -88,6 +88,38 @@ def test_gemm_layouts_bias(dt, akc, bkc, shape):
     assert rel(h64(Cd)[:, :N], ref) <= tol(dt)
 
 
+def test_gemm_rejects_bad_operands():
+    """Leading dimensions that are not whole 16-byte vectors or do not cover a row, unaligned
+    pointers, and epilogues missing their second input are refused before any launch."""
+    lib = bd.load()
+    M, N, K = 64, 64, 64
+    buf = [torch.zeros(M * 80 + 64, dtype=torch.bfloat16, device="cuda") for _ in range(5)]
+    A, Bm, C, aux, C2 = (t.data_ptr() for t in buf)
+
+    def call(dt=bd.GPT2_BF16, epi=bd.EPI_BIAS, lda=K, ldb=K, ldc=N, a=A, b=Bm, c=C, bias=None, x=None, ldx=0,
+             c2=None, akc=1, bkc=1):
+        return lib.gpt2op_gemm(dt, akc, bkc, epi, M, N, K, a, lda, b, ldb, c, ldc, bias, x, ldx, c2, 0, None, 0,
+                               stream())
+    assert call() == bd.GPT2_OK
+    assert call(lda=K + 1) == bd.GPT2_EINVAL            # not a whole number of 16-byte vectors
+    assert call(ldb=K + 4) == bd.GPT2_EINVAL
+    assert call(dt=bd.GPT2_FP32, ldc=N + 2) == bd.GPT2_EINVAL
+    assert call(lda=K - 8) == bd.GPT2_EINVAL            # shorter than the row it strides over
+    assert call(akc=0, lda=M - 8) == bd.GPT2_EINVAL
+    assert call(ldc=N - 8) == bd.GPT2_EINVAL
+    assert call(a=A + 2) == bd.GPT2_EINVAL              # unaligned pointers
+    assert call(c=C + 8) == bd.GPT2_EINVAL
+    assert call(bias=aux + 4) == bd.GPT2_EINVAL
+    assert call(epi=bd.EPI_RESID) == bd.GPT2_EINVAL     # residual epilogue without its input
+    assert call(epi=bd.EPI_RESID, x=aux, ldx=N - 8) == bd.GPT2_EINVAL
+    assert call(epi=bd.EPI_GELU) == bd.GPT2_EINVAL      # GELU epilogue without its second output
+    assert call(epi=bd.EPI_RESID, x=aux, ldx=N) == bd.GPT2_OK
+    assert call(epi=bd.EPI_GELU, c2=C2) == bd.GPT2_OK
+    assert lib.gpt2op_gemm(bd.GPT2_BF16, 1, 1, bd.EPI_BIAS, -1, N, K, A, K, Bm, K, C, N, None, None, 0, None, 0,
+                           None, 0, stream()) == bd.GPT2_EINVAL
+    torch.cuda.synchronize()
+
+
 BIG_CASES = [((1, 1), bd.EPI_BIAS), ((1, 0), bd.EPI_BIAS), ((0, 0), bd.EPI_BIAS), ((0, 1), bd.EPI_BIAS),
              ((1, 1), bd.EPI_GELU), ((1, 1), bd.EPI_RESID), ((1, 0), bd.EPI_GELU_BWD), ((0, 0), bd.EPI_F32),
              ((1, 1), bd.EPI_GELU_GRAD), ((1, 0), bd.EPI_MUL)]
@@ -271,8 +303,8 @@ def test_gemm_f32_weight_gradient_split_k_accumulate(dt, M, N, K):
 
 # ---------------------------------------------------------------------------- LayerNorm
 
-@pytest.mark.parametrize("dt", DTS)
-@pytest.mark.parametrize("C", [0, 6, 8192])
+@pytest.mark.parametrize("dt,C", [(dt, C) for dt in DTS for C in (0, 6, 8192)]
+                         + [(bd.GPT2_FP32, 4096), (bd.GPT2_FP32, 2056)])
 def test_layernorm_rejects_bad_widths(dt, C):
     rows, cap = 2, 2 * 8192 + 4096
     # every pointer sits 4 KiB into a buffer that would hold rows x 8192 elements
@@ -288,7 +320,8 @@ def test_layernorm_rejects_bad_widths(dt, C):
 
 
 @pytest.mark.parametrize("dt", DTS)
-@pytest.mark.parametrize("rows,C,has_b", [(37, 16, True), (300, 768, True), (65, 200, False), (1030, 1600, True)])
+@pytest.mark.parametrize("rows,C,has_b", [(37, 16, True), (300, 768, True), (65, 200, False), (1030, 1600, True),
+                                          (70, 2048, True)])
 def test_layernorm_forward_backward(dt, rows, C, has_b):
     if dt == bd.GPT2_BF16 and C % 8:
         pytest.skip("bf16 needs C % 8 == 0")
@@ -408,6 +441,22 @@ def test_attention_rejects_unsupported_head_size():
                                         stream()) == bd.GPT2_EINVAL
 
 
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("B,T,H,ok", [(-1, -4, 1, False), (2, -1, 1, False), (1, 4, 0, False), (0, 4, 1, True),
+                                      (2, 0, 1, True)])
+def test_attention_shape_checks(dt, B, T, H, ok):
+    """Negative sizes or no head are refused before any launch (B * T alone would let B = T = -1
+    through); an empty batch is a no-op."""
+    lib = bd.load()
+    x = torch.zeros(64, device="cuda")
+    p = x.data_ptr()
+    want = bd.GPT2_OK if ok else bd.GPT2_EINVAL
+    assert lib.gpt2op_attention_forward(dt, B, T, H, 64, p, p, p, stream()) == want
+    assert lib.gpt2op_attention_backward(dt, B, T, H, 64, p, p, p, p, p, p, stream()) == want
+    torch.cuda.synchronize()
+    assert not x.any()
+
+
 # ---------------------------------------------------------------------------- stochastic rounding
 
 @pytest.mark.parametrize("t,index0", [(1, 0), (7, 123457), (40000, (1 << 31) + 5)])
@@ -480,10 +529,12 @@ def test_encoder_rejects_bad_shapes(dt, T, maxT, C):
     if C != 16:
         assert lib.gpt2op_encoder_forward(dt, B, T, C, V, tok.data_ptr(), big[0].data_ptr(), big[1].data_ptr(),
                                           big[2].data_ptr(), err.data_ptr(), stream()) == bd.GPT2_EINVAL
+    keys.fill_(-7)
     assert lib.gpt2op_encoder_backward(dt, B, T, maxT, C, V, tok.data_ptr(), big[2].data_ptr(), big[0].data_ptr(),
                                        big[1].data_ptr(), 0, keys.data_ptr(), part.data_ptr(),
                                        stream()) == bd.GPT2_EINVAL
     torch.cuda.synchronize()
+    assert bool((keys == -7).all())  # refused before the sort wrote its keys
 
 
 @pytest.mark.parametrize("dt", DTS)
