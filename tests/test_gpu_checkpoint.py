@@ -1,6 +1,9 @@
-"""Checkpoint + bitwise resume: N straight updates equal k updates, gpt2_save, a new process,
-gpt2_load, and N - k updates, bit for bit (parameters and every loss). Each part runs in its own
-process, one after the other."""
+"""Checkpoint + bitwise resume ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南:
+-n writes checkpoints, -y 1 resumes, and bitwise determinism makes the resumed run continue exactly):
+N straight updates equal k updates, gpt2_save, a new process, gpt2_load, and N - k updates, bit for
+bit (parameters and every loss). Each part runs in its own process, one after the other. The
+straight run itself is held to the oracle's trajectory on the same inputs (bf16 bar: every loss
+within 2e-2)."""
 import os
 import subprocess
 import sys
@@ -8,7 +11,9 @@ import sys
 import numpy as np
 import pytest
 
+import oracle as O
 from gpt_transformer_step_train_amd import binding as bd
+from gpt_transformer_step_train_amd import synth
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +43,38 @@ def test_resume_is_bitwise_identical(tmp_path, no_master):
     la = np.load(str(straight) + ".losses.npy")
     lb = np.load(str(resumed) + ".losses.npy")
     assert np.array_equal(la[k:], lb)
+    ref = oracle_losses(n, no_master)
+    assert np.abs(la - ref).max() <= 2e-2, (la, ref)
+
+
+def rne_bf16_bits(x):
+    """fp32 -> bf16 bits, round to nearest even (finite inputs): the rounding set_params applies
+    when there is no fp32 master."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def oracle_losses(n, no_master):
+    """The worker's run (same model, batches, schedule and hyper-parameters) in the oracle."""
+    L, H, C, V, VP, MAXT, B, T = 2, 2, 128, 1000, 1024, 128, 4, 128
+    cfg = O.Config(L, H, C, V, VP, MAXT)
+    p = synth.init_params(L, C, VP, MAXT).astype(np.float64)
+    bits = rne_bf16_bits(p) if no_master else None
+    if no_master:
+        p = O.bf16_bits_to_float(bits).astype(np.float64)
+    m, v, losses = np.zeros_like(p), np.zeros_like(p), []
+    for step in range(n):
+        tok, tgt = synth.zipf_batch(V, B, T, 1000 + step)
+        loss, g = O.forward_backward(cfg, p, tok, tgt)
+        losses.append(loss)
+        lr = O.lr_schedule(step + 1, 6e-4, 3, 40, 0.1)
+        if no_master:
+            bits, m, v, _, _ = O.adamw_update_no_master(cfg, bits, g, m, v, lr, 0.9, 0.95, 1e-8, 0.1, step + 1,
+                                                        synth.PARAM_SEED, clip=1.0)
+            p = O.bf16_bits_to_float(bits).astype(np.float64)
+        else:
+            p, m, v, _ = O.adamw_update(cfg, p, g, m, v, lr, 0.9, 0.95, 1e-8, 0.1, step + 1, clip=1.0)
+    return np.array(losses)
 
 
 def test_load_rejects_other_architecture_and_bad_files(tmp_path, gpu_lib):

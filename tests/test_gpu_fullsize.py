@@ -97,7 +97,8 @@ def test_gpt2_124m_bf16_b16_ten_steps_vs_oracle():
     assert np.all(np.abs(np.array(norms) / np.array(gold["norms"]) - 1) <= 5e-2), (norms, gold["norms"])
 
 
-@pytest.mark.parametrize("tag,cfg", [("350m", O.CFG_350M), ("1558m", O.CFG_1558M)])
+# (GPT-2 1558M: the loss of the same sequence is checked with its gradients in test_gpu_bf16_parity.py)
+@pytest.mark.parametrize("tag,cfg", [("350m", O.CFG_350M)])
 def test_larger_models_first_sequence_init_loss_vs_oracle(tag, cfg):
     path = os.path.join(HERE, f"gpt2_{tag}_seq0_init_loss.json")
     gold = json.load(open(path))

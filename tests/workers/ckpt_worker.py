@@ -1,6 +1,6 @@
 """Runs part of a bf16 training run in its own process for the checkpoint-resume test.
 
-python ckpt_worker.py straight N out.npy          N updates from the seeded init
+python ckpt_worker.py straight N out.npy          N updates from the seeded host init
 python ckpt_worker.py first k N ckpt              k updates, then gpt2_save (cursor = k)
 python ckpt_worker.py second N ckpt out.npy       gpt2_load into a differently seeded model,
                                                   then the remaining updates up to N
@@ -25,8 +25,11 @@ L, H, C, V, VP, MAXT, B, T = 2, 2, 128, 1000, 1024, 128, 4, 128
 NO_MASTER = int(os.environ.get("CKPT_NO_MASTER", "0"))  # 1: bf16 parameters, stochastic rounding
 
 
-def make(seed):
-    return bd.Model(L, H, C, V, VP, MAXT, B, T, bd.GPT2_BF16, grad_clip=1.0, seed=seed, no_master=NO_MASTER)
+def make(seed, from_inputs=False):
+    m = bd.Model(L, H, C, V, VP, MAXT, B, T, bd.GPT2_BF16, grad_clip=1.0, seed=seed, no_master=NO_MASTER)
+    if from_inputs:  # the seeded host init the oracle starts from (the stochastic-rounding seed stays `seed`)
+        m.set_params(synth.init_params(L, C, VP, MAXT))
+    return m
 
 
 def run(m, first, last, losses):
@@ -44,11 +47,11 @@ def main():
     losses = []
     if mode == "straight":
         n, out = int(sys.argv[2]), sys.argv[3]
-        m = make(synth.PARAM_SEED)
+        m = make(synth.PARAM_SEED, from_inputs=True)
         run(m, 0, n, losses)
     elif mode == "first":
         k, path = int(sys.argv[2]), sys.argv[4]
-        m = make(synth.PARAM_SEED)
+        m = make(synth.PARAM_SEED, from_inputs=True)
         run(m, 0, k, losses)
         bd.check(bd.gpt2_save(path, k, k), "gpt2_save")
         print("saved", k, flush=True)
