@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1334,6 +1335,41 @@ int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void*
 
 int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
                               const void* dout, const float* lse, void* dqkv, float* dvec, void* stream) {
+  return op_ret(launch_attention_bwd(to_dt(dtype), B, T, H, hs, qkv, out, dout, lse, dqkv, dvec, ATT_BWD_ALL,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- the attention backward that allocates nothing: its scratch (D = rowsum(dO * O), one float per
+// query row and head) lives in this file-scope device array, one copy per GPU. In host code the
+// name `scratch` is only a host-side stand-in: its device address on the current GPU is looked up
+// once per device with hipGetSymbolAddress and only that address is handed to the kernels.
+static __device__ __align__(256) float scratch[GPT2_NOALLOC_ATTN_SCRATCH_FLOATS];
+static constexpr int NOALLOC_MAX_DEVICES = 64;
+static float* g_noalloc_scratch[NOALLOC_MAX_DEVICES];
+static std::mutex g_noalloc_mu;
+
+int gpt2op_attention_backward_noalloc(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
+                                      const void* dout, const float* lse, void* dqkv, void* stream) {
+  if (B < 0 || T < 0 || H < 1) return fail(GPT2_EINVAL, "attention_backward_noalloc: need B, T >= 0 and H >= 1");
+  if ((uint64_t)B * T * H > (uint64_t)GPT2_NOALLOC_ATTN_SCRATCH_FLOATS)
+    return fail(GPT2_EINVAL, "attention_backward_noalloc: B*T*H = %llu exceeds the %d floats of its scratch",
+                (unsigned long long)B * T * H, GPT2_NOALLOC_ATTN_SCRATCH_FLOATS);
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(GPT2_EINVAL, "attention_backward_noalloc: device %d", dev);
+  float* dvec = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    if (!g_noalloc_scratch[dev]) {
+      void* p = nullptr;
+      HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (!p) return fail(GPT2_EHIP, "attention_backward_noalloc: no device address for the scratch array");
+      g_noalloc_scratch[dev] = static_cast<float*>(p);
+    }
+    dvec = g_noalloc_scratch[dev];
+  }
+  // every scratch entry the kernels read is written first by the D kernel of the same call: nothing
+  // needs clearing
   return op_ret(launch_attention_bwd(to_dt(dtype), B, T, H, hs, qkv, out, dout, lse, dqkv, dvec, ATT_BWD_ALL,
                                      reinterpret_cast<hipStream_t>(stream)));
 }

@@ -83,6 +83,16 @@ int gpt2op_attention_forward(int dtype, int B, int T, int H, int hs, const void*
 /* dqkv [B,T,3C] (fully written) from qkv, out, dout, lse; dvec: float scratch [B*H*T]. */
 int gpt2op_attention_backward(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
                               const void* dout, const float* lse, void* dqkv, float* dvec, void* stream);
+/* gpt2op_attention_backward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and results,
+ * with the dvec scratch taken from a fixed array the library holds on each GPU (4 MiB, kept until
+ * the process ends) instead of from the caller. Needs B*T*H <= GPT2_NOALLOC_ATTN_SCRATCH_FLOATS,
+ * else GPT2_EINVAL; calls no allocator. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from several threads) race and must be serialised
+ * by the caller. Each call writes every entry it reads, so no clearing is needed between calls. */
+#define GPT2_NOALLOC_ATTN_SCRATCH_FLOATS (1 << 20)
+int gpt2op_attention_backward_noalloc(int dtype, int B, int T, int H, int hs, const void* qkv, const void* out,
+                                      const void* dout, const float* lse, void* dqkv, void* stream);
 /* gpt2op_attention_backward that also sums dqkv over its B*T rows: dbias[3C] = (or += when
  * accumulate) sum over rows of dqkv as stored, the gradient of the qkv bias (the hand-ordered
  * backward of "Karpathy 的 llm.c：从零理解大模型训练的 C/CUDA 实现", section 代码解剖).
