@@ -113,25 +113,54 @@ def measured_traffic(cls):
     return None
 
 
-def cpu_baseline(w, seconds_hint=""):
-    """The oracle (plain fp64 numpy, test infrastructure) on one sequence of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w):
+    """The oracle (plain fp64 numpy, test infrastructure, as it stands) timed on the host.
+
+    Bounded sample of the workload: one whole training step of the same GPT-2 at B=4 (the fp32
+    parity configuration), timed by phase on every BLAS thread
+    (forward = the logits of the batch; backward = forward + backward minus that; update = AdamW
+    over all parameters); plus the forward of one T-long sequence on one thread for a scaling point.
+    `value` is tokens/s of the whole step on all threads."""
     import numpy as np
     import oracle as O
     from gpt_transformer_step_train_amd import synth
+    from threadpoolctl import threadpool_info, threadpool_limits
     cfg = O.Config(w["L"], w["H"], w["C"], w["V"], w["Vp"], w["T"])
-    p = synth.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq)
-    tok, tgt = synth.zipf_batch(w["V"], 1, w["T"], 0)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    B = 4
+    p = synth.init_params(cfg.n_layer, cfg.n_embd, cfg.padded_vocab, cfg.max_seq).astype(np.float64)
+    tok, tgt = synth.zipf_batch(w["V"], B, w["T"], 0)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     t0 = time.perf_counter()
-    O.forward_backward(cfg, p, tok, tgt)
-    dt = time.perf_counter() - t0
-    return {"value": round(w["T"] / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"forward+backward of 1 of the {w['B']} sequences (T={w['T']}) of one micro-batch, "
-                      f"fp64 numpy oracle, {dt:.1f} s"}
+    O.forward_logits(cfg, p, tok)
+    t1 = time.perf_counter()
+    _, g = O.forward_backward(cfg, p, tok, tgt)
+    t2 = time.perf_counter()
+    O.adamw_update(cfg, p, g, np.zeros_like(p), np.zeros_like(p), 3e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+    t3 = time.perf_counter()
+    fwd, fb, upd = t1 - t0, t2 - t1, t3 - t2
+    ntok = B * w["T"]
+    with threadpool_limits(1):
+        t4 = time.perf_counter()
+        O.forward_logits(cfg, p, tok[:1])
+        one = time.perf_counter() - t4
+    return {"value": round(ntok / (fb + upd), 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"one fp64 oracle training step of the same model at B={B}, T={w['T']} (forward + backward + "
+                      f"AdamW, {fb + upd:.1f} s) on {threads} BLAS threads; one-thread point: forward of one "
+                      f"sequence",
+            "phases_s": {"forward": round(fwd, 2), "backward": round(fb - fwd, 2), "update": round(upd, 2)},
+            "single_thread_forward_tokens_per_s": round(w["T"] / one, 3),
+            "all_threads_forward_tokens_per_s": round(ntok / fwd, 3)}
 
 
 def main():

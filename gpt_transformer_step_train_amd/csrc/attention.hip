@@ -104,47 +104,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dvec(int BT, int T_, int H, cons
   dvec[((size_t)b * H + h) * T_ + t] = s;
 }
 
-// bf16, hs = 64: the same D with lane-contiguous loads. The (row, head) pairs are 128-byte runs
-// of out / dout in pair order; a wave takes 64 pairs as 512 consecutive 16-byte chunks, chunk
-// j * 64 + lane in its j-th load (so each load instruction reads 1 KiB contiguous, where one
-// thread per pair makes every instruction touch 64 different 128-byte lines), and the 8 lanes
-// holding one pair's chunks add their partial sums with three xor-shuffles.
-__global__ __launch_bounds__(256) void attn_bwd_dvec_bf16(int npairs, int T_, int H, const bf16* __restrict__ out,
-                                                          const bf16* __restrict__ dout, float* __restrict__ dvec) {
-  const int lane = threadIdx.x & 63;
-  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 512;  // first chunk of this wave
-  const int nchunk = npairs * 8;                                // < 2^31 for B T H <= 2^28
-  // straight-line loads (a chunk past the end reads the last one and is dropped below), so all 16
-  // are in flight together; a guarded load would make the compiler wait at every branch join
-  u32x4 a[8], c[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int ch = min(c0 + j * 64 + lane, nchunk - 1);
-    a[j] = *reinterpret_cast<const u32x4*>(out + (size_t)ch * 8);
-    c[j] = *reinterpret_cast<const u32x4*>(dout + (size_t)ch * 8);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int ch = c0 + j * 64 + lane;
-    V16<bf16> x, y;
-    x.unpack(a[j]);
-    y.unpack(c[j]);
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sum += x.v[e] * y.v[e];
-    if (ch >= nchunk) sum = 0.f;
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    sum += __shfl_xor(sum, 4);
-    const int pr = ch >> 3;
-    if ((lane & 7) == 0 && pr < npairs) {
-      const int row = pr / H, h = pr - row * H;
-      const int b = row / T_, t = row - b * T_;
-      dvec[((size_t)b * H + h) * T_ + t] = sum;
-    }
-  }
-}
-
 // dK, dV: one thread per key
 template <int HS>
 __global__ __launch_bounds__(AT) void attn_bwd_kv_f32(int T, int H, const float* __restrict__ qkv,
@@ -651,11 +610,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
 }
 
 // ---------------------------------------------------------------- backward: dQ
-// grid (T/128, B*H): block owns 128 queries (wave w: 32), loops over 64-key tiles.
+// grid (T/128, B*H): block owns 128 queries (wave w: 32), loops over 64-key tiles. Every query is
+// owned by exactly one block, which also forms its D = rowsum(dO * O) (from the dO row it holds and
+// the O row) and writes it to dvec for the dK/dV kernel, launched after this one.
 __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const uint16_t* __restrict__ qkv,
+                                                          const uint16_t* __restrict__ out,
                                                           const uint16_t* __restrict__ dout,
                                                           const float* __restrict__ lse,
-                                                          const float* __restrict__ dvec,
+                                                          float* __restrict__ dvec,
                                                           uint16_t* __restrict__ dqkv,
                                                           float* __restrict__ cs) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDP];  // [key][d]
@@ -680,15 +642,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
   // B operands Q[myq], dO[myq] by unguarded loads (a query past T reads the last row; its dS is
   // masked and its dQ not stored)
   bf16x8 qf[4], df[4];
+  u32x4 orow[4];
   const int qrow = min(myq, T - 1);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + (size_t)qrow * C3 + h * HD + 16 * s + 8 * g));
     df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dbase + (size_t)qrow * C + h * HD + 16 * s + 8 * g));
+    orow[s] = *reinterpret_cast<const u32x4*>(out + ((size_t)b * T + qrow) * C + h * HD + 16 * s + 8 * g);
   }
   const size_t qi = (size_t)bh * T + qrow;
   const float L2 = lse[qi] * LOG2E;
-  const float Dq = dvec[qi];
+  // D of this query: the lane holds 32 of the row's 64 (dO, O) pairs, lane ^ 32 the other 32
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4 dw = __builtin_bit_cast(u32x4, df[s]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpart += __uint_as_float(dw[e] << 16) * __uint_as_float(orow[s][e] << 16);
+      dpart += __uint_as_float(dw[e] & 0xffff0000u) * __uint_as_float(orow[s][e] & 0xffff0000u);
+    }
+  }
+  const float Dq = pair_sum(dpart);
+  if (g == 0 && myq < T) dvec[qi] = Dq;
   f32x16 dq[2] = {zero16(), zero16()};  // rows = queries, cols = d
 
   const int kend = min(T, q0 + BQ);
@@ -787,15 +763,16 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
   const int BT = B * T;
   if (dt == DT_BF16) {
     if (hs != HD) return hipErrorInvalidValue;
-    if (parts & ATT_BWD_PRE)
-      attn_bwd_dvec_bf16<<<cdiv((long)BT * H, 256), 256, 0, s>>>(BT * H, T, H, reinterpret_cast<const bf16*>(out),
-                                                               reinterpret_cast<const bf16*>(dout), dvec);
+    // D = rowsum(dO * O) comes out of the dQ kernel, which therefore runs first; ATT_BWD_PRE alone
+    // has nothing left to do
     dim3 grid(cdiv(T, BQ), B * H);
     auto Q = reinterpret_cast<const uint16_t*>(qkv);
+    auto O_ = reinterpret_cast<const uint16_t*>(out);
     auto dO = reinterpret_cast<const uint16_t*>(dout);
     auto dQ = reinterpret_cast<uint16_t*>(dqkv);
+    if (parts & ATT_BWD_Q) attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, O_, dO, lse, dvec, dQ, cs);
     if (parts & ATT_BWD_KV) attn_bwd_kv_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ, cs);
-    if (parts & ATT_BWD_Q) attn_bwd_q_bf16<<<grid, 256, 0, s>>>(T, H, Q, dO, lse, dvec, dQ, cs);
+    (void)BT;
     return hipGetLastError();
   }
   if (parts & ATT_BWD_PRE) {

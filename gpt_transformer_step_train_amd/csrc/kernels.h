@@ -108,7 +108,9 @@ size_t encoder_bwd_partial_floats(int BT, int C);
 hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const void* qkv, void* out,
                                 float* lse, hipStream_t s);
 // dqkv [B,T,3C] is fully written. `dvec` holds B*H*T floats of scratch.
-// parts: any of ATT_BWD_PRE (D = rowsum(dO * O)), ATT_BWD_KV (dK, dV), ATT_BWD_Q (dQ), in that order
+// parts: any of ATT_BWD_PRE (D = rowsum(dO * O)), ATT_BWD_KV (dK, dV), ATT_BWD_Q (dQ). fp32: PRE, then
+// the other two in any order. bf16: the dQ kernel forms D itself and writes it to dvec, so PRE
+// launches nothing and Q must run before KV (ATT_BWD_ALL does so).
 constexpr int ATT_BWD_PRE = 1, ATT_BWD_KV = 2, ATT_BWD_Q = 4, ATT_BWD_ALL = 7;
 // cs (bf16 only, may be null): the KV and Q kernels also write the column sums of the dqkv rows
 // they store, one partial row of 3C floats per (sequence, 128-row tile):

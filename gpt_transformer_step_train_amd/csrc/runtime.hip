@@ -665,7 +665,7 @@ int backward_impl() {
       else RUN(gemm(true, false, EPI_BIAS, BT, C, C, g.dres, C, W(o.attprojw), C, g.dbuf2, C));
     }
     // (the attproj weight gradient, dres^T atty, is taken together with the qkv one below)
-    {
+    if (g.dt != DT_BF16) {  // bf16: D comes out of the dQ kernel
       ProfScope ps_(GPT2_K_ATTENTION_BWD_PRE);
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
                                   ATT_BWD_PRE, s));
@@ -676,15 +676,15 @@ int backward_impl() {
     const ColsumDefer ad = defer_slot();
     const bool adefer = (size_t)arows * 3 * C <= ad.cap;
     float* csa = (lb && g.dt == DT_BF16) ? (adefer ? ad.part : sc) : nullptr;
+    {  // (first: it also forms D = rowsum(dO * O) for the dK/dV kernel)
+      ProfScope ps_(GPT2_K_ATTENTION_BWD_Q);
+      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
+                                  ATT_BWD_Q, s, csa));
+    }
     {
       ProfScope ps_(GPT2_K_ATTENTION_BWD);
       HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
                                   ATT_BWD_KV, s, csa));
-    }
-    {
-      ProfScope ps_(GPT2_K_ATTENTION_BWD_Q);
-      HIPCHK(launch_attention_bwd(g.dt, g.B, g.T, g.H, C / g.H, a.qkv, a.atty, g.dbuf2, a.lse, g.dbuf1, g.dvec,
-                                  ATT_BWD_Q, s, csa));
     }
     if (csa && adefer) {
       RUN(defer_sum(csa, 3L * C, arows, 3 * C, G(o.qkvb)));

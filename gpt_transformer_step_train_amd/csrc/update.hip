@@ -30,10 +30,20 @@ __global__ __launch_bounds__(256) void sumsq_partial_kernel(const float* __restr
   double s = 0.0;
   const size_t n4 = n / 4;
   const size_t stride = (size_t)gridDim.x * 256;
-  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += stride) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(x)[i];
-    const double a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-    s += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
+  // four 16-byte loads in flight per thread (straight-line: an index past the end reads the last
+  // vector, which is then dropped), so that enough bytes are requested to cover the memory latency
+  constexpr int U = 4;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += U * stride) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = reinterpret_cast<const f32x4*>(x)[min(i + u * stride, n4 - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i + u * stride < n4) {
+        const double a0 = v[u][0], a1 = v[u][1], a2 = v[u][2], a3 = v[u][3];
+        s += a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3;
+      }
+    }
   }
   for (size_t i = n4 * 4 + blockIdx.x * 256ull + threadIdx.x; i < n; i += stride) s += (double)x[i] * (double)x[i];
   sh[threadIdx.x] = s;

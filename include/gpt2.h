@@ -81,8 +81,8 @@ uint64_t gpt2_workspace_bytes(const gpt2_config* cfg);
 /* Validate cfg, carve the workspace, initialise the parameters, zero m and v.
  * Defined by "Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南 (flag -e: a GPT-2 of a
  * given depth initialised from scratch; flags -b -t: the micro-batch B x T) and section 代码 (all GPU
- * memory is allocated once at start-up and stays fixed for the run). The init recipe below is the
- * reading of BASELINE's "normal(0, 0.02)" (the pages give none).
+ * memory is allocated once at start-up and stays fixed for the run). The pages give no init recipe;
+ * the one below is the plain reading of a seeded normal(0, 0.02) init.
  * Init: every 2-D tensor in layout order draws N(0, 0.02^2) from one stream (SplitMix64 seeded
  * with `seed`, Box-Muller in double, rounded to fp32); biases 0; LayerNorm weights 1.
  * Synchronous. Replaces any previous model. */
@@ -210,8 +210,8 @@ int gpt2_get_logits(float* dst, uint64_t n);
 #define GPT2_K_ENCODER_BWD 22
 #define GPT2_K_GRAD_NORM 23
 #define GPT2_K_ADAMW 24
-#define GPT2_K_ATTENTION_BWD_Q 25    /* dQ                                    */
-#define GPT2_K_ATTENTION_BWD_PRE 26  /* D = rowsum(dO * O) per query          */
+#define GPT2_K_ATTENTION_BWD_Q 25    /* dQ (bf16: also D = rowsum(dO * O))    */
+#define GPT2_K_ATTENTION_BWD_PRE 26  /* D = rowsum(dO * O) per query (fp32)   */
 #define GPT2_K_WEIGHT_TRANSPOSE 27  /* bf16 weight matrices -> transposed copies */
 #define GPT2_K_RECOMPUTE 28          /* activation recompute in the backward (recompute >= 1) */
 #define GPT2_K_GRAD_FINISH 29        /* second stage of the backward's column sums, one batched launch */

@@ -14,7 +14,7 @@ What it computes follows the pages on llm.c:
     指南, flag -c), gradient accumulation to a total batch (section 参数指南, flag -d);
   * BabyGPT ("无需写代码能力，手搓最简单BabyGPT模型"): 2 tokens, context 3.
 
-Readings where the pages are silent (each listed in the design doc): GELU is the tanh form of
+Readings where the pages are silent: GELU is the tanh form of
 GPT-2; LayerNorm uses eps = 1e-5 and the biased variance; logits of padded rows v >= V are
 not part of the softmax and get zero gradient; weight decay is decoupled and uses the
 pre-update parameter; gradient clipping scales all gradients by clip/||g|| when ||g|| > clip;
