@@ -11,7 +11,10 @@ weights, grads and AdamW state), AdamW lr 6e-4, betas (0.9, 0.95), wd 0.1, clip 
 Prints one JSON line: tokens/s, ms/step and model-FLOPs utilisation (6N + 6LCT FLOPs per token,
 the formula that reproduces the MFU column of the llm.c GPT-2 reproduction post), the roofline of
 the kernel class that takes the most time (timed with HIP events on the library's stream over the
-timed steps) and the CPU oracle timed on a bounded sample of the same workload.
+timed steps) and the CPU oracle timed on a bounded sample of the same workload. `calibration` holds
+rates of this part measured live next to the published peaks: the MFMA rate of the GEMM main loop
+on random and on zero operand bits, and a plain HBM copy; the roofline object also gives the
+dominant class's fraction of the matching sustained rate.
 """
 import argparse
 import json
@@ -163,6 +166,44 @@ def cpu_baseline(w):
             "all_threads_forward_tokens_per_s": round(ntok / fwd, 3)}
 
 
+def calibrate(bd, torch, np):
+    """Sustained rates of this part, measured live: the GEMM main loop's MFMA work on random operand
+    bits and on zeros (gpt2op_mfma_rate: the matrix cores draw more power on random bits and the
+    clock follows the power), and a plain 16-byte streaming copy (gpt2op_copy), read + write."""
+    lib = bd.load()
+    st = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(7)
+    # bf16 bits: random sign and mantissa, exponent 2^-7 (values of the size a trained layer sees)
+    rnd = (rng.integers(0, 1 << 16, 32768, dtype=np.uint32) & 0x807F | 0x3C00).astype(np.uint16)
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, host in (("random_operands", rnd), ("zero_operands", np.zeros(32768, np.uint16))):
+        ops = torch.tensor(host.view(np.int16), device="cuda")
+        ms = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bd.check(lib.gpt2op_mfma_rate(ops.data_ptr(), out.data_ptr(), blocks, iters, st), "mfma_rate")
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        res[name] = round(blocks * 8 * iters * 32 * 32768 / (min(ms[1:]) / 1e3) / 1e12, 1)
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ms = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bd.check(lib.gpt2op_copy(dst.data_ptr(), src.data_ptr(), n, st), "copy")
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    return {"mfma_bf16_tflops": res, "hbm_copy_tbs": round(2 * n / (min(ms[1:]) / 1e3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +307,10 @@ def main():
                  "copy")
         torch.cuda.synchronize()
 
+    cal = calibrate(bd, torch, np)
+    sustained = cal["mfma_bf16_tflops"]["random_operands"] * 1e12 if bound == "mfma" else cal["hbm_copy_tbs"] * 1e12
+    roof["sustained_peak"] = round(sustained / scale, 2)
+    roof["frac_of_sustained"] = round(achieved / sustained, 4)
     out = {
         "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak",
@@ -280,6 +325,7 @@ def main():
         "final_loss": round(float(losses[-1]), 5),
         "roofline": roof,
         "workspace_bytes": int(m.cfg.workspace_bytes),
+        "calibration": cal,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

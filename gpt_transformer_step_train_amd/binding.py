@@ -27,6 +27,7 @@ EXPORTS = [
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
     "gpt2op_attention_backward_colsum", "gpt2op_stochastic_round", "gpt2op_attention_backward_noalloc",
+    "gpt2op_mfma_rate",
 ]
 GPT2_NOALLOC_ATTN_SCRATCH_FLOATS = 1 << 20
 
@@ -97,6 +98,7 @@ def load(path=LIB_PATH):
         "gpt2op_attention_forward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 4),
         "gpt2op_attention_backward": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7),
         "gpt2op_attention_backward_noalloc": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 6),
+        "gpt2op_mfma_rate": (ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.c_int, _vp]),
         "gpt2op_stochastic_round": (ctypes.c_int, [_vp, _vp, _u64, _u64, _i32, _u64, _vp]),
         "gpt2op_attention_backward_colsum": (ctypes.c_int, [ctypes.c_int] * 5 + [_vp] * 7 + [ctypes.c_int, _vp, _u64,
                                                                                           _vp]),

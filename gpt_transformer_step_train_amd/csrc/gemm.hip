@@ -1092,6 +1092,70 @@ static hipError_t launch_pair_t(const GemmArgs& a0, const GemmArgs& a1, float* s
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------------------
+// Measurement utility (not part of the training step): the GEMM main loop's MFMA work without
+// its global traffic. Each 8-wave block copies 64 KiB of operand bits into LDS (two 256-row x
+// 64-k bf16 operand tiles, swizzled as the GEMM stores them), then every wave runs `iters`
+// rounds of the GEMM's k-loop over them: per round 4 k-steps of 4 + 2 fragment reads and 8
+// v_mfma_f32_32x32x16_bf16 (a 128 x 64 wave tile). Timed by the caller, it gives the MFMA rate
+// the part sustains for a given kind of operand data (the matrix cores draw more power on
+// random bits than on zeros, and the clock follows the power).
+__global__ __launch_bounds__(512) void mfma_rate_kernel(const u32x4* __restrict__ operands, int iters,
+                                                        float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[2 * 256 * 64];
+  for (int i = threadIdx.x; i < 2 * 256 * 64 / 8; i += 512) reinterpret_cast<u32x4*>(tile)[i] = operands[i];
+  __syncthreads();
+  using OP = Operand<bf16, true, 256, 64, 512>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int arow = (w >> 2) * 128 + (lane & 31), brow = (w & 3) * 64 + (lane & 31), kofs = (lane >> 5) * 8;
+  const bf16* As = tile;
+  const bf16* Bs = tile + 256 * 64;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = Mma<bf16>::load(As + OP::idx(arow + 32 * i, st * 16 + kofs));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = Mma<bf16>::load(Bs + OP::idx(brow + 32 * j, st * 16 + kofs));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = Mma<bf16>::mma(fa[i], fb[j], acc[i][j]);
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
+  sum = wave_sum(sum);
+  __syncthreads();  // the operand tiles are read no more: their first 32 bytes hold the wave sums
+  float* ws = reinterpret_cast<float*>(tile);
+  if (lane == 0) ws[w] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int i = 0; i < 8; ++i) t += ws[i];
+    out[blockIdx.x] = t;
+  }
+}
+
+hipError_t launch_mfma_rate(const void* operands, float* out, int blocks, int iters, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  mfma_rate_kernel<<<blocks, 512, 0, s>>>(reinterpret_cast<const u32x4*>(operands), iters, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_f32_pair(DType dt, bool a_kc, bool b_kc, const GemmArgs& a0, const GemmArgs& a1,
                                 float* scratch, size_t scratch_floats, hipStream_t s) {
   const bool ok = dt == DT_BF16 && a0.K == a1.K && a0.M > 0 && a0.N > 0 && a1.M > 0 && a1.N > 0 && a0.K > 0 &&

@@ -200,6 +200,9 @@ inline int trans_tiles(int rows, int cols) { return ((rows + 63) / 64) * ((cols 
 hipError_t launch_transpose_bf16(const TransItem* items, int nitems, int ntiles, const uint16_t* src, uint16_t* dst,
                                  hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+// measurement utility: blocks x 8 waves x iters x 32 MFMAs (32x32x16 bf16) on the 64 KiB of operand
+// bits at `operands`, read through LDS; out[block] receives a checksum
+hipError_t launch_mfma_rate(const void* operands, float* out, int blocks, int iters, hipStream_t s);
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
 
 }  // namespace g2

@@ -1413,6 +1413,12 @@ int gpt2op_copy(void* dst, const void* src, uint64_t bytes, void* stream) {
   return op_ret(launch_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int gpt2op_mfma_rate(const void* operands, float* out, int blocks, int iters, void* stream) {
+  if (!operands || !out || (uintptr_t)operands % 16 || blocks < 1 || blocks > (1 << 20) || iters < 0)
+    return fail(GPT2_EINVAL, "mfma_rate: need 16-byte aligned operands, out, 1 <= blocks <= 2^20, iters >= 0");
+  return op_ret(launch_mfma_rate(operands, out, blocks, iters, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int gpt2op_encoder_backward(int dtype, int B, int T, int max_seq, int C, int V, const int32_t* tok, const void* dout,
                             float* dwte, float* dwpe, int accumulate_wpe, uint32_t* keys, float* partial, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

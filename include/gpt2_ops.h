@@ -128,6 +128,16 @@ uint64_t gpt2op_encoder_backward_scratch(int BT, int C);
  * that converts the counters of any other kernel into bytes. */
 int gpt2op_copy(void* dst, const void* src, uint64_t bytes, void* stream);
 
+/* Measurement utility, not part of the training step: the matrix-core work of the GEMM main loop
+ * without its global traffic. Each of `blocks` blocks (8 waves) copies the 65536 bytes at
+ * `operands` (device, 16-byte aligned: two 256 x 64 bf16 operand tiles) into LDS, then every wave
+ * runs `iters` rounds of 4 k-steps, each of 6 LDS fragment reads and 8 v_mfma_f32_32x32x16_bf16:
+ * blocks * 8 * iters * 32 * 32768 FLOP in all, timed by the caller. out (device float [blocks])
+ * receives one checksum per block. The rate depends on the operand bits: the matrix cores draw
+ * more power on random bits than on zeros, and the clock follows the power. blocks in
+ * [1, 1 << 20], iters >= 0, else GPT2_EINVAL. */
+int gpt2op_mfma_rate(const void* operands, float* out, int blocks, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
