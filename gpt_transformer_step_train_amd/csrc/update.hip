@@ -487,14 +487,26 @@ hipError_t launch_gelu(DType dt, const void* in, void* out, size_t n, hipStream_
   return hipGetLastError();
 }
 
+// A plain streaming copy, the reference for what this part sustains on a read-and-write stream:
+// 1024 blocks striding over the buffer, each thread with four 16-byte loads in flight (straight-
+// line: an index past the end reads the last vector and is not stored).
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
                                                    size_t n16) {
-  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) dst[i] = src[i];
+  constexpr int U = 4;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[min(i + u * stride, n16 - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * stride < n16) dst[i + u * stride] = v[u];
+  }
 }
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   const size_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;
-  copy_kernel<<<(int)std::min<size_t>(8192, (n16 + 255) / 256), 256, 0, s>>>(
+  copy_kernel<<<(int)std::min<size_t>(1024, (n16 + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), n16);
   return hipGetLastError();
 }

@@ -605,3 +605,43 @@ def test_encoder_flags_out_of_range_token():
                                       out.data_ptr(), err.data_ptr(), stream()) == 0
     torch.cuda.synchronize()
     assert err.item() & 1
+
+
+# ---------------------------------------------------------------------------- measurement utilities
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, (1 << 20) * 5 + 48, (1 << 22) * 7])
+def test_copy_utility_copies_exactly(nbytes):
+    """gpt2op_copy (the bandwidth and counter reference) copies exactly `bytes`, including tails
+    shorter than a full round of its grid, and nothing past them."""
+    lib = bd.load()
+    rng = np.random.default_rng(nbytes % 1000)
+    src = torch.tensor(rng.integers(0, 256, nbytes + 64, dtype=np.uint8), device="cuda")
+    dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+    assert lib.gpt2op_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src[:nbytes]) and not dst[nbytes:].any()
+    assert lib.gpt2op_copy(dst.data_ptr() + 8, src.data_ptr(), 32, stream()) == bd.GPT2_EINVAL
+    assert lib.gpt2op_copy(dst.data_ptr(), src.data_ptr(), 40, stream()) == bd.GPT2_EINVAL
+
+
+def test_mfma_rate_utility():
+    """gpt2op_mfma_rate runs the main loop's MFMAs on the given operand bits: zero operands give zero
+    checksums, the same operands the same checksums twice, and bad arguments are refused."""
+    lib = bd.load()
+    rng = np.random.default_rng(3)
+    bits = (rng.integers(0, 1 << 16, 32768, dtype=np.uint32) & 0x807F | 0x3C00).astype(np.uint16)
+    ops = torch.tensor(bits.view(np.int16), device="cuda")
+    zeros = torch.zeros(32768, dtype=torch.int16, device="cuda")
+    out = torch.full((64,), float("nan"), dtype=torch.float32, device="cuda")
+    assert lib.gpt2op_mfma_rate(zeros.data_ptr(), out.data_ptr(), 64, 3, stream()) == 0
+    torch.cuda.synchronize()
+    assert not out.any()
+    outs = []
+    for _ in range(2):
+        assert lib.gpt2op_mfma_rate(ops.data_ptr(), out.data_ptr(), 64, 3, stream()) == 0
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert torch.isfinite(outs[0]).all() and torch.equal(outs[0], outs[1]) and outs[0].abs().sum() > 0
+    assert lib.gpt2op_mfma_rate(ops.data_ptr(), out.data_ptr(), 0, 3, stream()) == bd.GPT2_EINVAL
+    assert lib.gpt2op_mfma_rate(ops.data_ptr() + 8, out.data_ptr(), 4, 3, stream()) == bd.GPT2_EINVAL
+    assert lib.gpt2op_mfma_rate(ops.data_ptr(), out.data_ptr(), 4, -1, stream()) == bd.GPT2_EINVAL
