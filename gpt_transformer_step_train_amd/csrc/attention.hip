@@ -24,6 +24,8 @@
 //    meets is read from an LDS tile stored transposed, in the same key order.
 //  * fp32 (any hs <= 64): one thread per query (forward, dQ) or per key (dK/dV), K/V or Q/dO
 //    tiles staged in LDS; exact fp32 math for the fp32 training configurations.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -287,32 +289,40 @@ __device__ __forceinline__ void attn_block_map(int& bh, int& rank) {
   }
 }
 
+// Buffer resource over rows row0 .. nrows - 1 of a row-major bf16 matrix with ld elements per row,
+// starting at m: a load at a byte offset past those rows returns zeros and a store there is
+// dropped, so tiles that run past T need no clamping, selects or branches. All arguments must be
+// uniform over the wave (the resource lives in scalar registers). The launchers keep
+// T * 3C * 2 bytes below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* m, long ld, int row0, int nrows) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(m) + (size_t)row0 * ld, (short)0,
+                                           (int)(max(nrows - row0, 0) * ld * 2), 0x00020000);
+}
+
 // A 64 x 64 bf16 tile piece: rows r, r + 16, r + 32, r + 48 (r = p % 16) x 8 columns per thread
 // (128 pieces per tile). The 16 lanes of one 16-byte LDS store cycle write 16 consecutive rows of
 // one column chunk, which the 144-byte row pitch spreads over distinct banks (rows 4 apart, as in
 // a 4-row piece, would put every fourth lane on the same banks).
-// The loads are straight-line (rows past nrows read the last row) and the rows past nrows are
-// zeroed only when the piece is stored: a guarded load, or a select on the loaded value, would
-// make the wave wait for the load right after issuing it instead of one tile later.
+// Rows past nrows read as zeros (buffer range check). The per-thread byte offsets are fixed; a
+// tile moves only the resource's base, which is scalar work.
 struct Piece {
   u32x4 r[4];
-  int nvalid;  // rows of this thread's 4 that are in range: rg + 16 j < nvalid
+  int off[4];  // byte offsets of this thread's rows rg + 16 j, columns cg .. cg + 7, from the tile's row 0
   __device__ __forceinline__ static int rgrp(int p) { return p & 15; }
   __device__ __forceinline__ static int cgrp(int p) { return (p >> 4) * 8; }
-  __device__ __forceinline__ void load(const uint16_t* src, long ld, int row0, int nrows, int p) {
-    const int rg = rgrp(p), cg = cgrp(p);
-    nvalid = nrows - row0;
+  __device__ __forceinline__ void init(long ld, int p) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = min(row0 + rg + 16 * j, nrows - 1);
-      r[j] = *reinterpret_cast<const u32x4*>(src + (size_t)row * ld + cg);
-    }
+    for (int j = 0; j < 4; ++j) off[j] = (int)(((rgrp(p) + 16 * j) * ld + cgrp(p)) * 2);
+  }
+  __device__ __forceinline__ void load(const uint16_t* src, long ld, int row0, int nrows) {
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src, ld, row0, nrows);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, 0));
   }
   __device__ __forceinline__ void store_rows(uint16_t* lds, int p) const {  // lds[row][col]
     const int rg = rgrp(p), cg = cgrp(p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(lds + (rg + 16 * j) * LDP + cg) = rg + 16 * j < nvalid ? r[j] : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(lds + (rg + 16 * j) * LDP + cg) = r[j];
   }
 };
 
@@ -359,17 +369,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
   const int ntiles = cdiv(kend, KT);
   Piece pc;
   const int p = tid & 127;
-  const bool is_k = tid < 128;
-  auto load_tile = [&](int kt) {
-    pc.load(base + (is_k ? C : 2 * C) + h * HD, C3, kt * KT, T, p);
-  };
-  load_tile(0);
+  const bool is_k = w < 2;  // waves 0, 1 stage K, waves 2, 3 stage V (uniform per wave)
+  pc.init(C3, p);
+  const uint16_t* src = base + (is_k ? C : 2 * C) + h * HD;
+  pc.load(src, C3, 0, T);
   pc.store_rows(is_k ? Ksb[0] : Vsb[0], p);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // one 64-key tile; only the last two tiles (keys from q0 on) hold keys after some query of the
+  // block, so the others are compiled without the mask
+  auto tile = [&](int kt, auto diag) {
     const uint16_t* Ks = Ksb[kt & 1];
     const uint16_t* Vs = Vsb[kt & 1];
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if (kt + 1 < ntiles) pc.load(src, C3, (kt + 1) * KT, T);
     // both 32-key halves of the tile at once: two independent S chains, one max, one rescale
     const int kb0 = kt * KT;
     if (kb0 <= qw0 + 31) {  // else the whole tile is in the future of this wave's queries
@@ -385,11 +396,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
         sc[i] = st[0][i];
         sc[16 + i] = st[1][i];
       }
-      if (kb0 + 63 > qw0) {  // diagonal tile: mask keys after the query
+      if constexpr (decltype(diag)::value) {
+        if (kb0 + 63 > qw0) {  // mask keys after the query
+          // key = kb0 + 32 (i >> 4) + acc_row(i & 15, g) > myq: one compare with a constant per entry
+          const int lim = myq - kb0 - 4 * g;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int key = kb0 + (i >> 4) * 32 + acc_row(i & 15, g);
-          if (key > myq) sc[i] = -INFINITY;
+          for (int i = 0; i < 32; ++i)
+            if ((i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3) > lim) sc[i] = -INFINITY;
         }
       }
       float mloc = sc[0];
@@ -426,7 +439,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(int T, int H, const uint
     // barrier that ended it): one barrier per tile
     if (kt + 1 < ntiles) pc.store_rows(is_k ? Ksb[(kt + 1) & 1] : Vsb[(kt + 1) & 1], p);
     __syncthreads();
-  }
+  };
+  const int nplain = min(ntiles, 2 * qt);  // tiles wholly before the block's first query
+  for (int kt = 0; kt < nplain; ++kt) tile(kt, std::false_type{});
+  for (int kt = nplain; kt < ntiles; ++kt) tile(kt, std::true_type{});
   const float l_tot = pair_sum(g == 0 ? lsum[0] : 0.f);
   if (myq < T) {
     const float inv = 1.f / l_tot;
@@ -496,6 +512,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   const int k0 = kt_blk * BQ;
   const int kw0 = k0 + 32 * w;
   const int mykey = kw0 + l32;
+  const int kdiag = mykey - 4 * g;
   const float c2 = LOG2E / sqrtf((float)HD);
 
   // K and V of this lane's key as B operands (S = Q K^T, dP = dO V^T)
@@ -514,25 +531,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
   const int ntiles = cdiv(T - qstart, KT);
   Piece pc;
   const int p = tid & 127;
-  const bool is_q = tid < 128;
+  const bool is_q = w < 2;  // waves 0, 1 stage Q, waves 2, 3 stage dO (uniform per wave)
+  const uint16_t* src = (is_q ? base : dbase) + h * HD;
+  const long lds_ld = is_q ? C3 : (long)C;
+  pc.init(lds_ld, p);
   float lnext = 0.f, dnext = 0.f;  // LSE and D of query tid of the next tile (tid < 64)
-  // Q or dO rows by a pointer select and LSE / D of query qt0 + tid % 64 from a clamped index, all
-  // straight-line (see Piece); out-of-range values are dropped when the tile is stored
+  // LSE / D of query qt0 + tid % 64 from a clamped index (straight-line; replaced for rows past T
+  // when stored)
   int lrow = 0;
   auto load_tile = [&](int it) {
     const int qt0 = qstart + it * KT;
-    pc.load((is_q ? base : dbase) + h * HD, is_q ? C3 : (long)C, qt0, T, p);
+    pc.load(src, lds_ld, qt0, T);
     lrow = qt0 + (tid & (KT - 1));
     const size_t li = (size_t)bh * T + min(lrow, T - 1);
     lnext = lse[li];
     dnext = dvec[li];
   };
-  if (ntiles > 0) load_tile(0);
-  for (int it = 0; it < ntiles; ++it) {
+  // one 64-query tile; only the first two tiles (queries below k0 + 128) hold queries before
+  // some key of the block, so the others are compiled without the mask
+  auto tile = [&](int it, auto diag) {
     const int qt0 = qstart + it * KT;
     pc.store_rows(is_q ? Qs : dOs, p);
     if (tid < KT) {
-      Ls[tid] = lrow < T ? lnext * LOG2E : 0.f;
+      Ls[tid] = lrow < T ? lnext * LOG2E : INFINITY;  // a query past T: probability exp2(-inf) = 0
       Dsh[tid] = lrow < T ? dnext : 0.f;
     }
     __syncthreads();
@@ -559,12 +580,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
 #pragma unroll
         for (int e = 0; e < 4; ++e) pr[4 * r4 + e] = fast_exp2(sacc[4 * r4 + e] * c2 - l4[e]);
       }
-      // some (q, key) pairs of the sub-block masked or out of range (uniform over the wave)
-      if (qq0 < kw0 + 31 || qq0 + 32 > T) {
+      if constexpr (decltype(diag)::value) {
+        // some keys of the wave follow some queries of the sub-block (uniform over the wave);
+        // queries past T already have probability 0 from their infinite LSE.
+        // key <= q = qq0 + acc_row(i, g)  <=>  8 (i >> 2) + (i & 3) >= mykey - qq0 - 4g
+        if (qq0 < kw0 + 31) {
+          const int lim = kdiag - qq0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = qq0 + acc_row(i, g);
-          pr[i] = (mykey <= q && q < T) ? pr[i] : 0.f;
+          for (int i = 0; i < 16; ++i) pr[i] = (i >> 2) * 8 + (i & 3) >= lim ? pr[i] : 0.f;
         }
       }
 #pragma unroll
@@ -586,24 +609,28 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv_bf16(int T, int H, const u
       }
     }
     __syncthreads();
-  }
-  // store: accumulator rows = keys, columns = d
+  };
+  if (ntiles > 0) load_tile(0);
+  const int ndiag = min(ntiles, 2);
+  for (int it = 0; it < ndiag; ++it) tile(it, std::true_type{});
+  for (int it = ndiag; it < ntiles; ++it) tile(it, std::false_type{});
+  // store: accumulator rows = keys, columns = d. Keys past T have dK = dV = 0 (every probability
+  // of theirs is masked), so they add nothing to the column sums, and their stores fall outside
+  // the resource and are dropped.
   const float sc = 1.0f / sqrtf((float)HD);
   float sk[2] = {0.f, 0.f}, sv[2] = {0.f, 0.f};  // column sums over this lane's keys (as stored)
+  const __amdgpu_buffer_rsrc_t ors = rows_rsrc(dqkv + (size_t)b * T * C3 + h * HD, C3, kw0, T);
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = db * 32 + l32;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = kw0 + acc_row(i, g);
-      if (key < T) {
-        uint16_t* dst = dqkv + ((size_t)b * T + key) * C3 + h * HD + d;
-        const uint16_t k16 = f2bf(dk[db][i] * sc), v16 = f2bf(dv[db][i]);
-        dst[C] = k16;
-        dst[2 * C] = v16;
-        sk[db] += bf2f(k16);
-        sv[db] += bf2f(v16);
-      }
+      const int o = (int)((acc_row(i, g) * C3 + C + d) * 2);
+      const uint16_t k16 = f2bf(dk[db][i] * sc), v16 = f2bf(dv[db][i]);
+      __builtin_amdgcn_raw_buffer_store_b16(k16, ors, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(v16, ors, o + 2 * C, 0, 0);
+      sk[db] += bf2f(k16);
+      sv[db] += bf2f(v16);
     }
   }
   if (cs) bias_partial(cs, b * gridDim.x + kt_blk, C3, C + h * HD, sk, sv, reinterpret_cast<float*>(Qs), w, lane);
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
     orow[s] = *reinterpret_cast<const u32x4*>(out + ((size_t)b * T + qrow) * C + h * HD + 16 * s + 8 * g);
   }
   const size_t qi = (size_t)bh * T + qrow;
-  const float L2 = lse[qi] * LOG2E;
+  const float L2 = myq < T ? lse[qi] * LOG2E : INFINITY;  // a query past T: probabilities exp2(-inf) = 0
   // D of this query: the lane holds 32 of the row's 64 (dO, O) pairs, lane ^ 32 the other 32
   float dpart = 0.f;
 #pragma unroll
@@ -671,17 +698,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
   const int ntiles = cdiv(kend, KT);
   Piece pc;
   const int p = tid & 127;
-  const bool is_k = tid < 128;
-  auto load_tile = [&](int kt) { pc.load(base + (is_k ? C : 2 * C) + h * HD, C3, kt * KT, T, p); };
-  load_tile(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  const bool is_k = w < 2;  // waves 0, 1 stage K, waves 2, 3 stage V (uniform per wave)
+  const uint16_t* src = base + (is_k ? C : 2 * C) + h * HD;
+  pc.init(C3, p);
+  // one 64-key tile; only the last two tiles (keys from q0 on) hold keys after some query of the
+  // block, so the others are compiled without the mask
+  auto tile = [&](int kt, auto diag) {
     pc.store_rows(is_k ? Ks : Vs, p);
     __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if (kt + 1 < ntiles) pc.load(src, C3, (kt + 1) * KT, T);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int kb = kt * KT + sb * 32;
-      if (kb > qw0 + 31) continue;
+      if (decltype(diag)::value && kb > qw0 + 31) continue;
       f32x16 st = zero16(), dpt = zero16();  // rows = keys, cols = queries
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -691,11 +720,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(st[i] * c2 - L2);
-      if (kb + 31 > qw0 || qw0 + 32 > T) {  // some pairs masked or out of range (uniform)
+      if constexpr (decltype(diag)::value) {
+        // some keys of the sub-block follow some queries of the wave (uniform); queries past T
+        // already have probability 0. key = kb + acc_row(i, g) <= myq  <=>  8 (i >> 2) + (i & 3) <= lim
+        if (kb + 31 > qw0) {
+          const int lim = myq - kb - 4 * g;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + acc_row(i, g);
-          ds[i] = (key <= myq && myq < T) ? ds[i] : 0.f;
+          for (int i = 0; i < 16; ++i) ds[i] = (i >> 2) * 8 + (i & 3) <= lim ? ds[i] : 0.f;
         }
       }
 #pragma unroll
@@ -709,32 +740,40 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_q_bf16(int T, int H, const ui
       }
     }
     __syncthreads();
-  }
+  };
+  pc.load(src, C3, 0, T);
+  const int nplain = min(ntiles, 2 * qt);  // tiles wholly before the block's first query
+  for (int kt = 0; kt < nplain; ++kt) tile(kt, std::false_type{});
+  for (int kt = nplain; kt < ntiles; ++kt) tile(kt, std::true_type{});
+  // queries past T have dQ = 0 (all their probabilities are 0): they add nothing to the column
+  // sums, and their stores fall outside the resource and are dropped
   const float sc = 1.0f / sqrtf((float)HD);
   float sq[2] = {0.f, 0.f};  // column sums over this lane's queries (as stored)
+  const __amdgpu_buffer_rsrc_t ors = rows_rsrc(dqkv + (size_t)b * T * C3 + h * HD, C3, qw0, T);
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = db * 32 + l32;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int q = qw0 + acc_row(i, g);
-      if (q < T) {
-        const uint16_t q16 = f2bf(dq[db][i] * sc);
-        dqkv[((size_t)b * T + q) * C3 + h * HD + d] = q16;
-        sq[db] += bf2f(q16);
-      }
+      const uint16_t q16 = f2bf(dq[db][i] * sc);
+      __builtin_amdgcn_raw_buffer_store_b16(q16, ors, (int)((acc_row(i, g) * C3 + d) * 2), 0, 0);
+      sq[db] += bf2f(q16);
     }
   }
   if (cs) bias_partial(cs, b * gridDim.x + qt, C3, h * HD, sq, nullptr, reinterpret_cast<float*>(Ks), w, lane);
 }
 
 // =====================================================================================
+// The bf16 kernels address one sequence's [T, 3C] rows through buffer resources with 32-bit byte
+// counts and offsets.
+static bool bf16_rows_fit(int T, int H) { return (long)T * 3 * H * HD * 2 < (1L << 31); }
+
 hipError_t launch_attention_fwd(DType dt, int B, int T, int H, int hs, const void* qkv, void* out, float* lse,
                                 hipStream_t s) {
   if (B < 0 || T < 0 || H < 1) return hipErrorInvalidValue;
   if (B == 0 || T == 0) return hipSuccess;
   if (dt == DT_BF16) {
-    if (hs != HD) return hipErrorInvalidValue;
+    if (hs != HD || !bf16_rows_fit(T, H)) return hipErrorInvalidValue;
     dim3 grid(cdiv(T, BQ), B * H);
     attn_fwd_bf16<<<grid, 256, 0, s>>>(T, H, reinterpret_cast<const uint16_t*>(qkv),
                                        reinterpret_cast<uint16_t*>(out), lse);
@@ -762,7 +801,7 @@ hipError_t launch_attention_bwd(DType dt, int B, int T, int H, int hs, const voi
   if (B == 0 || T == 0) return hipSuccess;
   const int BT = B * T;
   if (dt == DT_BF16) {
-    if (hs != HD) return hipErrorInvalidValue;
+    if (hs != HD || !bf16_rows_fit(T, H)) return hipErrorInvalidValue;
     // D = rowsum(dO * O) comes out of the dQ kernel, which therefore runs first; ATT_BWD_PRE alone
     // has nothing left to do
     dim3 grid(cdiv(T, BQ), B * H);
