@@ -56,9 +56,6 @@ template <> struct Mma<float> {
   }
 };
 
-#ifndef GEMM_BIG_WAVES
-#define GEMM_BIG_WAVES 8
-#endif
 constexpr int GROUP_M = 8;
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int TKR = 4;  // transposed piece: TKR k-rows x VEC row-contiguous elements
@@ -296,7 +293,7 @@ template <typename T, int BM_, int BN_, bool AKC, bool BKC> struct Cfg {
   // waves per block, in a WGM x WGN grid over the tile: 2 x (NW/2), except 256 x 192 (4 x 2,
   // 64 x 96 per wave)
   static constexpr bool BIG = sizeof(T) == 2 && BM == 256 && (BN == 256 || BN == 192);
-  static constexpr int NW = BIG ? GEMM_BIG_WAVES : 4;
+  static constexpr int NW = BIG ? 8 : 4;
   static constexpr int NTHR = 64 * NW, WGM = BN == 192 ? 4 : 2, WGN = NW / WGM;
   static constexpr int TM = BM / WGM, TN = BN / WGN;
   static constexpr int FM = TM / 32, FN = TN / 32;
@@ -927,9 +924,6 @@ static bool use_big(DType dt, bool kc_both, int M, int N) {
   return t >= (kc_both ? 128 : 384);
 }
 
-#ifndef GEMM_DW_BIG
-#define GEMM_DW_BIG 1
-#endif
 // Split-K factor for the fp32 weight-gradient products. The blocks run in ceil(tiles s / NCU)
 // rounds of K / s each, and every split adds an fp32 partial of M x N that is written and read
 // back once; pick the s that minimises that time (K per split >= 512, partials within scratch).
@@ -1026,7 +1020,7 @@ template <typename T, bool AKC, bool BKC>
 static hipError_t launch_sel(Epi epi, const GemmArgs& a, float* scratch, size_t sf, hipStream_t s) {
   // split-K weight gradients (their M x N is small): 256 x 256 tiles unless there are fewer than
   // 16 of them (C x C), where the 128 x 128 tile's smaller partials win
-  if (epi == EPI_F32 && scratch && GEMM_DW_BIG && sizeof(T) == 2 && (long)cdiv(a.M, 256) * cdiv(a.N, 256) >= 16)
+  if (epi == EPI_F32 && scratch && sizeof(T) == 2 && (long)cdiv(a.M, 256) * cdiv(a.N, 256) >= 16)
     return launch_t<T, 256, 256, AKC, BKC>(epi, a, scratch, sf, s);
   if (epi != EPI_F32 && use_big(sizeof(T) == 2 ? DT_BF16 : DT_F32, AKC && BKC, a.M, a.N)) {
     // K-contiguous products whose 256-wide column tiles leave CUs idle in the last round

@@ -170,12 +170,7 @@ hipError_t launch_adamw(const WorkItem* items, int nitems, float* p, const float
                         hipStream_t s);
 // AdamW over ADAM_TR x ADAM_TC tiles of the weight matrices that also have a transposed bf16 copy:
 // the update of launch_adamw, plus the transposed copy written from the same registers through LDS.
-#ifndef ADAM_TR
-#define ADAM_TR 64
-#endif
-#ifndef ADAM_TC
-#define ADAM_TC 64
-#endif
+constexpr int ADAM_TR = 64, ADAM_TC = 64;
 struct AdamTile {
   uint64_t off;      // first element of the tile in the flat parameter vector
   uint64_t dst_off;  // element (c0, r0) of the transposed copy
