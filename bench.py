@@ -27,13 +27,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s (published)
 PEAK_HBM = 8.0e12       # MI355X HBM3E, bytes/s (published)
-METRIC = "training tokens/sec + bf16 MFU, GPT-2 124M B=16 T=1024 on 1 MI355X"
-
 WORKLOADS = {
-    "gpt2-124m": dict(L=12, H=12, C=768, V=50257, Vp=50304, T=1024, B=16, accum=1),
-    "gpt2-350m": dict(L=24, H=16, C=1024, V=50257, Vp=50304, T=1024, B=16, accum=1),
-    "gpt2-1558m": dict(L=48, H=25, C=1600, V=50257, Vp=50304, T=1024, B=16, accum=64),
+    "gpt2-124m": dict(name="124M", L=12, H=12, C=768, V=50257, Vp=50304, T=1024, B=16, accum=1),
+    "gpt2-350m": dict(name="350M", L=24, H=16, C=1024, V=50257, Vp=50304, T=1024, B=16, accum=1),
+    "gpt2-1558m": dict(name="1558M", L=48, H=25, C=1600, V=50257, Vp=50304, T=1024, B=16, accum=64),
 }
+
+
+def metric_name(w):
+    return f"training tokens/sec + bf16 MFU, GPT-2 {w['name']} B={w['B']} T={w['T']} on 1 MI355X"
 HP = dict(lr=6e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1)
 
 
@@ -96,10 +98,11 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(cls):
-    """HBM bytes per launch of kernel class `cls` from the counter summaries under profiles/ (lines
-    'TRAFFIC class=... fetch_bytes=... write_bytes=... sources_sha256=...'), or None when there is
-    none for this class or the sources changed since the counters were taken."""
+def measured_traffic(cls, workload):
+    """HBM bytes per launch of kernel class `cls` in `workload` from the counter summaries under
+    profiles/ (lines 'TRAFFIC workload=... class=... fetch_bytes=... write_bytes=...
+    sources_sha256=...'), or None when there is none for this class and workload or the sources
+    changed since the counters were taken."""
     import glob
     digest = None
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -107,7 +110,7 @@ def measured_traffic(cls):
             if not line.startswith("TRAFFIC "):
                 continue
             kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
-            if kv.get("class") != cls:
+            if kv.get("class") != cls or kv.get("workload") != workload:
                 continue
             digest = digest or sources_sha256()
             if kv.get("sources_sha256") != digest:
@@ -297,7 +300,7 @@ def main():
     roof = {"bound": bound, "kernel": name, "launches_per_step": int(cnt[dom] // args.steps),
             "avg_launch_us": round(avg_s * 1e6, 2), "achieved": round(achieved / scale, 2),
             "peak": peak / scale, "unit": unit, "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(name)}
+            "traffic": measured_traffic(name, args.workload)}
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -312,7 +315,7 @@ def main():
     roof["sustained_peak"] = round(sustained / scale, 2)
     roof["frac_of_sustained"] = round(achieved / sustained, 4)
     out = {
-        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric_name(w), "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload} train step, B={w['B']} T={w['T']} grad_accum={w['accum']}, "
