@@ -7,7 +7,7 @@ Calls only oracle/ (and the seeded input generators). Run from the repository ro
     python tests/golden/make_goldens.py cfg3grad  # GPT-2 124M, B=16: gradients at init    (~3 min)
     python tests/golden/make_goldens.py grad1558  # GPT-2 1558M, one sequence: gradients  (~10 min, ~48 GB)
     python tests/golden/make_goldens.py cfg4      # GPT-2 350M, B=16: 10 updates          (~1.5 h)
-    python tests/golden/make_goldens.py cfg4rounded  # the same from the bf16-rounded init, 5 updates (~40 min)
+    python tests/golden/make_goldens.py cfg4rounded  # the same from the bf16-rounded init           (~1.5 h)
 
 cfg2 -> tests/golden/gpt2_124m_fp32_b4_step1.npz: the loss, the pre-clip gradient norm, and
         for every tensor its max |g| plus g, and theta/m/v after one AdamW update, at 64
@@ -22,8 +22,8 @@ grad1558 -> tests/golden/gpt2_1558m_seq0_grads.npz: the same for the first seque
         of GPT-2 1558M at init.
 cfg4 -> tests/golden/gpt2_350m_b16_10steps.json: the per-update mean losses and norms of 10 updates
         of GPT-2 350M at B=16 with the hyper-parameters of cfg3.
-cfg4rounded -> tests/golden/gpt2_350m_b16_bf16init_5steps.json: the first 5 of those updates from the
-        same init rounded to bf16: the oracle's own sensitivity to a perturbation of bf16 size.
+cfg4rounded -> tests/golden/gpt2_350m_b16_bf16init_10steps.json: the same 10 updates from the same
+        init rounded to bf16: the oracle's own sensitivity to a perturbation of bf16 size.
 Inputs: parameters from the seed-1337 normal(0, 0.02) init, Zipf(1.1) token stream of seed 42
 (micro-step s uses stream positions s*(B*T+1) ...).
 """
@@ -144,7 +144,7 @@ def make_cfg4():
                       f, indent=1)
 
 
-def make_cfg4_rounded(steps=5):
+def make_cfg4_rounded(steps=10):
     """cfg4's run from the same init rounded to bf16 (round to nearest even): how far the exact
     trajectory itself moves under a perturbation of the size bf16 rounding makes."""
     cfg, B, T = O.CFG_350M, 16, 1024
@@ -166,7 +166,7 @@ def make_cfg4_rounded(steps=5):
         norms.append(norm)
         print(f"cfg4 bf16-rounded init, step {s + 1}: loss {loss:.6f} norm {norm:.4f} ({time.time() - t0:.0f} s)",
               flush=True)
-        with open(os.path.join(HERE, "gpt2_350m_b16_bf16init_5steps.json"), "w") as f:
+        with open(os.path.join(HERE, "gpt2_350m_b16_bf16init_10steps.json"), "w") as f:
             json.dump({"config": "GPT-2 350M, B=16, T=1024, Zipf(1.1) seed 42, init seed 1337 rounded to bf16",
                        "hyper": dict(lr=lr, b1=b1, b2=b2, eps=eps, wd=wd, clip=clip),
                        "losses": losses, "norms": norms, "complete": len(losses) == steps}, f, indent=1)

@@ -21,7 +21,9 @@ compare 64 seeded entries of it, plus the tensor's own max |g|.
     gradient;
   * GPT-2 124M, B = 16 (the benchmarked workload) and GPT-2 1558M, one sequence, at init:
     loss, norm and sampled gradients against stored oracle values;
-  * GPT-2 350M, B = 16: ten updates, losses within 2e-2 of the oracle's and norms within 5 %.
+  * GPT-2 350M, B = 16: ten updates against the oracle's trajectory; after the loss spike of
+    update 3 each update's band widens by twice the oracle's own sensitivity there (its run from
+    the bf16-rounded init).
 """
 import json
 import os
@@ -233,9 +235,16 @@ def test_1558m_bf16_one_sequence_gradients_at_init_vs_oracle():
 
 
 def test_350m_bf16_b16_ten_updates_vs_oracle():
-    path = os.path.join(GOLDEN, "gpt2_350m_b16_10steps.json")
-    gold = json.load(open(path))
-    assert gold["complete"]
+    """GPT-2 350M, B=16, bf16, 10 updates at lr 6e-4 with no warm-up, against the oracle. The loss
+    spikes at update 3 and the run is chaotic for a few updates after it: the oracle's own run from
+    the same init rounded to bf16 (one perturbation of the size bf16 rounding makes) ends up ~0.4
+    away in loss at update 4. Update k is held to 2e-2 plus twice the distance between those two
+    oracle runs at update k (0.77 at update 4, 0.03-0.09 at updates 5-10); the first three updates
+    come before the spike's effect and take 2e-2 alone. Gradient norms likewise: 5 % plus twice the
+    relative distance of the two oracle runs' norms at that update."""
+    gold = json.load(open(os.path.join(GOLDEN, "gpt2_350m_b16_10steps.json")))
+    pert = json.load(open(os.path.join(GOLDEN, "gpt2_350m_b16_bf16init_10steps.json")))
+    assert gold["complete"] and pert["complete"] and pert["hyper"] == gold["hyper"]
     h = gold["hyper"]
     cfg = O.CFG_350M
     m = model(cfg, 16, 1024, bd.GPT2_BF16, clip=h["clip"])
@@ -247,8 +256,14 @@ def test_350m_bf16_b16_ten_updates_vs_oracle():
         m.backward()
         m.step(h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], s + 1)
         norms.append(bd.gpt2_grad_norm())
-    print("350M losses", [round(x, 4) for x in losses], "oracle", [round(x, 4) for x in gold["losses"]], flush=True)
-    dl = np.abs(np.array(losses) - np.array(gold["losses"]))
-    assert dl.max() <= BF16_LOSS_BAND, (losses, gold["losses"])
-    assert np.all(np.abs(np.array(norms) / np.array(gold["norms"]) - 1) <= 5e-2), (norms, gold["norms"])
+    ref_l, pert_l = np.array(gold["losses"]), np.array(pert["losses"])
+    ref_n, pert_n = np.array(gold["norms"]), np.array(pert["norms"])
+    band_l = BF16_LOSS_BAND + 2 * np.abs(pert_l - ref_l)
+    band_n = 5e-2 + 2 * np.abs(pert_n / ref_n - 1)
+    print("350M losses", [round(x, 4) for x in losses], "oracle", [round(x, 4) for x in ref_l],
+          "bands", [round(x, 4) for x in band_l], flush=True)
+    dl = np.abs(np.array(losses) - ref_l)
+    assert np.all(dl[:3] <= BF16_LOSS_BAND), (losses, gold["losses"])
+    assert np.all(dl <= band_l), (losses, gold["losses"], band_l)
+    assert np.all(np.abs(np.array(norms) / ref_n - 1) <= band_n), (norms, gold["norms"], band_n)
     del m
