@@ -23,6 +23,7 @@ EXPORTS = [
     "gpt2_last_status", "gpt2_last_error", "gpt2_num_params", "gpt2_get_params", "gpt2_set_params",
     "gpt2_get_grads", "gpt2_get_adam_state", "gpt2_get_logits", "gpt2_free", "gpt2_profile_enable",
     "gpt2_profile_read", "gpt2_skip_update", "gpt2_save", "gpt2_load", "gpt2_lr_schedule", "gpt2_outlier_reset", "gpt2_outlier_update",
+    "gpt2_grad_sumsq_range", "gpt2_adamw_step_range",
     "gpt2op_gemm", "gpt2op_layernorm_forward", "gpt2op_layernorm_backward", "gpt2op_layernorm_backward_scratch",
     "gpt2op_attention_forward", "gpt2op_attention_backward", "gpt2op_cross_entropy", "gpt2op_encoder_forward",
     "gpt2op_encoder_backward", "gpt2op_encoder_backward_scratch", "gpt2op_copy", "gpt2op_gemm_colsum",
@@ -83,6 +84,9 @@ def load(path=LIB_PATH):
         "gpt2_profile_enable": (ctypes.c_int, [ctypes.c_uint32]),
         "gpt2_profile_read": (ctypes.c_int, [_vp, _vp, _i32]),
         "gpt2_skip_update": (ctypes.c_int, []),
+        "gpt2_grad_sumsq_range": (ctypes.c_int, [_u64, _u64, ctypes.POINTER(ctypes.c_double)]),
+        "gpt2_adamw_step_range": (ctypes.c_int, [_f32, _f32, _f32, _f32, _f32, _i32, _u64, _u64, ctypes.c_double,
+                                                 ctypes.c_int]),
         "gpt2_save": (ctypes.c_int, [ctypes.c_char_p, _i32, _u64]),
         "gpt2_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(_u64)]),
         "gpt2_lr_schedule": (_f32, [_i32, _f32, _i32, _i32, _f32]),
@@ -179,6 +183,17 @@ def gpt2_grad_norm():
 
 def gpt2_skip_update():
     return load().gpt2_skip_update()
+
+
+def gpt2_grad_sumsq_range(begin, end):
+    """Returns (status, sum of g^2 over [begin, end))."""
+    out = ctypes.c_double(0.0)
+    rc = load().gpt2_grad_sumsq_range(begin, end, ctypes.byref(out))
+    return rc, out.value
+
+
+def gpt2_adamw_step_range(lr, b1, b2, eps, wd, t, begin, end, global_sumsq, finish):
+    return load().gpt2_adamw_step_range(lr, b1, b2, eps, wd, t, begin, end, global_sumsq, int(finish))
 
 
 def gpt2_save(path, t, cursor):

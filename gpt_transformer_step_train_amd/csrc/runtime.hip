@@ -92,6 +92,17 @@ struct Model {
   double* norm_partial = nullptr;
   double* norm2 = nullptr;
   float* clip_scale = nullptr;
+  // one rank's share of a sharded update (gpt2_adamw_step_range): the flat work items cut to the
+  // range, and the device copies of the caller's squared global norm and the clip scale from it
+  std::vector<WorkItem> range_host;
+  WorkItem* range_items = nullptr;
+  double* range_norm2 = nullptr;
+  float* range_scale = nullptr;
+  struct {
+    double n2;
+    float scale;
+  } range_vals{};
+  bool transposed_stale = false;  // a range update changed weights whose transposed copies it does not write
   float* loss_dev = nullptr;
   float* dloss_dev = nullptr;
   int* nvalid_dev = nullptr;
@@ -359,6 +370,9 @@ size_t plan(const gpt2_config* c, Model* m, char* base) {
   M->norm_partial = (double*)take(NORM_PARTS * 8);
   M->norm2 = (double*)take(8);
   M->clip_scale = (float*)take(4);
+  M->range_items = (WorkItem*)take(nitems * sizeof(WorkItem));  // a range cuts each item to at most one piece
+  M->range_norm2 = (double*)take(8);
+  M->range_scale = (float*)take(4);
   M->loss_dev = (float*)take(4);
   M->dloss_dev = (float*)take(4);
   M->nvalid_dev = (int*)take(4);
@@ -481,6 +495,10 @@ int forward_impl(const int32_t* tokens, const int32_t* targets) {
   const int BT = g.BT, C = g.C, L = g.L;
   const size_t es = g.es;
   hipStream_t s = g.stream;
+  if (g.transposed_stale) {  // after range updates: the backward reads the transposed copies
+    HIPCHK(refresh_transposed());
+    g.transposed_stale = false;
+  }
   set_scalars_kernel<<<1, 1, 0, s>>>(g.err_dev);
   {
       ProfScope ps_(GPT2_K_ENCODER_FWD);
@@ -873,16 +891,7 @@ int gpt2_backward(void) {
   return ok();
 }
 
-int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t) {
-  RUN(check_ready());
-  if (t < 1) return fail(GPT2_EINVAL, "t must be >= 1");
-  if (g.micro == 0) return fail(GPT2_ESTATE, "gpt2_adamw_step needs at least one gpt2_backward since the last update");
-  hipStream_t s = g.stream;
-  {
-      ProfScope ps_(GPT2_K_GRAD_NORM);
-      HIPCHK(launch_sumsq_partial(g.grads, g.N, g.norm_partial, NORM_PARTS, s));
-    }
-  HIPCHK(launch_grad_norm_finish(g.norm_partial, NORM_PARTS, g.norm2, g.clip_scale, g.cfg.grad_clip, s));
+static AdamArgs adam_args(float lr, float b1, float b2, float eps, float wd, int32_t t) {
   AdamArgs a;
   a.lr = lr;
   a.b1 = b1;
@@ -895,6 +904,20 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
   a.no_master = g.cfg.no_master;
   a.t = t;
   a.sr_seed = g.seed ^ 0xD1B54A32D192ED03ull;
+  return a;
+}
+
+int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t) {
+  RUN(check_ready());
+  if (t < 1) return fail(GPT2_EINVAL, "t must be >= 1");
+  if (g.micro == 0) return fail(GPT2_ESTATE, "gpt2_adamw_step needs at least one gpt2_backward since the last update");
+  hipStream_t s = g.stream;
+  {
+      ProfScope ps_(GPT2_K_GRAD_NORM);
+      HIPCHK(launch_sumsq_partial(g.grads, g.N, g.norm_partial, NORM_PARTS, s));
+    }
+  HIPCHK(launch_grad_norm_finish(g.norm_partial, NORM_PARTS, g.norm2, g.clip_scale, g.cfg.grad_clip, s));
+  const AdamArgs a = adam_args(lr, b1, b2, eps, wd, t);
   {
       ProfScope ps_(GPT2_K_ADAMW);
       if (g.shadow_t) {  // flat items for the small tensors, tiles (with their transposed copies) for the matrices
@@ -902,6 +925,7 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
                             g.clip_scale, g.norm2, a, s));
         HIPCHK(launch_adamw_tiles(g.adam_tiles, (int)g.adam_tiles_host.size(), g.params, g.grads, g.m, g.v, g.shadow,
                                   g.shadow_t, g.clip_scale, g.norm2, a, s));
+        g.transposed_stale = false;  // the tiles rewrote every transposed copy
       } else {
         HIPCHK(launch_adamw(g.items, (int)g.items_host.size(), g.params, g.grads, g.m, g.v, g.shadow, g.clip_scale,
                             g.norm2, a, s));
@@ -924,6 +948,67 @@ float gpt2_grad_norm(void) {
   return (float)sqrt(n2);
 }
 
+
+// ------------------------------------------------------------------ one rank's share of a sharded update
+static int range_check(uint64_t begin, uint64_t end) {
+  if (begin > end || end > g.N || begin % 4 || end % 4)
+    return fail(GPT2_EINVAL, "need 0 <= begin <= end <= num_params (%zu), both multiples of 4", g.N);
+  return GPT2_OK;
+}
+
+int gpt2_grad_sumsq_range(uint64_t begin, uint64_t end, double* sumsq) {
+  RUN(check_ready());
+  if (!sumsq) return fail(GPT2_EINVAL, "sumsq is NULL");
+  RUN(range_check(begin, end));
+  hipStream_t s = g.stream;
+  // the partial sums and their fixed-order finish of the full norm, over the range
+  HIPCHK(launch_sumsq_partial(g.grads + begin, end - begin, g.norm_partial, NORM_PARTS, s));
+  HIPCHK(launch_grad_norm_finish(g.norm_partial, NORM_PARTS, g.range_norm2, g.range_scale, 0.f, s));
+  HIPCHK(hipMemcpyAsync(&g.range_vals.n2, g.range_norm2, 8, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  *sumsq = g.range_vals.n2;
+  return ok();
+}
+
+int gpt2_adamw_step_range(float lr, float b1, float b2, float eps, float wd, int32_t t, uint64_t begin, uint64_t end,
+                          double global_sumsq, int finish) {
+  RUN(check_ready());
+  if (t < 1) return fail(GPT2_EINVAL, "t must be >= 1");
+  if (g.micro == 0)
+    return fail(GPT2_ESTATE, "gpt2_adamw_step_range needs at least one gpt2_backward since the last update");
+  RUN(range_check(begin, end));
+  hipStream_t s = g.stream;
+  HIPCHK(hipStreamSynchronize(s));  // the host copies below are free to change
+  // the clip scale from the caller's global norm, as the norm kernel forms it for the full update
+  const double nrm = sqrt(global_sumsq);
+  const float clip = g.cfg.grad_clip;
+  g.range_vals.n2 = global_sumsq;
+  g.range_vals.scale = (clip > 0.f && nrm > (double)clip) ? (float)((double)clip / nrm) : 1.0f;
+  HIPCHK(hipMemcpyAsync(g.range_norm2, &g.range_vals.n2, 8, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(g.range_scale, &g.range_vals.scale, 4, hipMemcpyHostToDevice, s));
+  // the flat work items (runs of one tensor, each with its tensor's decay flag) cut to the range
+  g.range_host.clear();
+  for (const WorkItem& it : g.items_host) {
+    const uint64_t lo = std::max<uint64_t>(it.off, begin), hi = std::min<uint64_t>(it.off + it.len, end);
+    if (lo >= hi) continue;
+    WorkItem r = it;
+    r.off = lo;
+    r.len = (uint32_t)(hi - lo);
+    r.normal0 = it.normal0 + (lo - it.off);
+    g.range_host.push_back(r);
+  }
+  if (!g.range_host.empty()) {
+    HIPCHK(hipMemcpyAsync(g.range_items, g.range_host.data(), g.range_host.size() * sizeof(WorkItem),
+                          hipMemcpyHostToDevice, s));
+    ProfScope ps_(GPT2_K_ADAMW);
+    HIPCHK(launch_adamw(g.range_items, (int)g.range_host.size(), g.params, g.grads, g.m, g.v, g.shadow,
+                        g.range_scale, g.range_norm2, adam_args(lr, b1, b2, eps, wd, t), s));
+    if (g.shadow_t) g.transposed_stale = true;
+  }
+  HIPCHK(hipStreamSynchronize(s));
+  if (finish) g.micro = 0;
+  return ok();
+}
 
 int gpt2_profile_enable(uint32_t mask) {
   RUN(check_ready());

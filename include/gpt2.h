@@ -126,6 +126,30 @@ int gpt2_adamw_step(float lr, float b1, float b2, float eps, float wd, int32_t t
  * Host-side state only. */
 int gpt2_skip_update(void);
 
+/* One data-parallel rank's share of a sharded update, as ZeRO-1 runs it ("Karpathy 用 C 复现 GPT-2：
+ * 单卡 24 小时 $672", section 参数指南, flag -z: the optimizer state split over the ranks, each rank
+ * updating its own slice of the parameters): on one GPU, a contiguous slice [begin, end) of the
+ * flat parameter vector (the layout of gpt2_get_params), whose ends may cut through tensors; weight
+ * decay still follows the tensor each element belongs to. begin and end must be multiples of 4
+ * with begin <= end <= gpt2_num_params(), else GPT2_EINVAL. Both calls are synchronous.
+ *
+ * gpt2_grad_sumsq_range: *sumsq = the sum of g^2 over the slice (double, the kernels and fixed
+ * summation order of the full update's norm; over [0, N) it is exactly the squared norm the full
+ * update uses). The sum of all ranks' values is the squared global norm a rank would get from an
+ * all-reduce.
+ *
+ * gpt2_adamw_step_range: the update of gpt2_adamw_step restricted to the slice, with the clip
+ * scale formed from global_sumsq (the squared global gradient norm) exactly as the full update
+ * forms it from its own norm; writes the fp32 master, m, v and the bf16 copy of the slice (bit for
+ * bit what gpt2_adamw_step writes there, given the same global_sumsq). The transposed bf16 weight
+ * copies the backward reads are rewritten from the bf16 copy at the next gpt2_forward. finish != 0
+ * ends the update as gpt2_adamw_step does (the next gpt2_backward overwrites the gradients); a
+ * sharded update is one call per slice with finish set on the last. Needs a gpt2_backward since
+ * the last update (GPT2_ESTATE). */
+int gpt2_grad_sumsq_range(uint64_t begin, uint64_t end, double* sumsq);
+int gpt2_adamw_step_range(float lr, float b1, float b2, float eps, float wd, int32_t t, uint64_t begin, uint64_t end,
+                          double global_sumsq, int finish);
+
 /* Checkpoint and bitwise resume ("Karpathy 用 C 复现 GPT-2：单卡 24 小时 $672", section 参数指南:
  * -n checkpoints every n steps, -y 1 resumes, and determinism makes a resumed run continue
  * exactly). gpt2_save writes the fp32 master parameters, AdamW's m and v, the caller's update
