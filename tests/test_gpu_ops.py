@@ -376,8 +376,11 @@ def test_layernorm_forward_backward(dt, rows, C, has_b):
 
 # ---------------------------------------------------------------------------- attention
 
+# bf16 shapes: ragged last tiles (T = 33, 200, 777) with several sequences, whose rows past T must
+# read as zeros rather than the next sequence's rows; the 350M (16) and 1558M (25) head counts
 ATT_CASES = [(bd.GPT2_FP32, 2, 3, 4, 4), (bd.GPT2_FP32, 1, 130, 2, 64), (bd.GPT2_BF16, 2, 256, 2, 64),
-             (bd.GPT2_BF16, 1, 200, 3, 64), (bd.GPT2_BF16, 1, 1024, 1, 64), (bd.GPT2_BF16, 1, 33, 1, 64)]
+             (bd.GPT2_BF16, 1, 200, 3, 64), (bd.GPT2_BF16, 1, 1024, 1, 64), (bd.GPT2_BF16, 1, 33, 1, 64),
+             (bd.GPT2_BF16, 1, 1024, 16, 64), (bd.GPT2_BF16, 3, 777, 25, 64)]
 
 
 @pytest.mark.parametrize("dt,B,T,H,hs", ATT_CASES)
