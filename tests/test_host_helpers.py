@@ -81,3 +81,10 @@ def test_library_outlier_detector_matches_oracle(lib):
 def test_skip_update_needs_a_model(lib):
     bd.gpt2_free()
     assert bd.gpt2_skip_update() == bd.GPT2_ESTATE
+
+
+def test_sharded_update_calls_need_a_model(lib):
+    """Without a model both calls of the sharded update refuse before any GPU work."""
+    bd.gpt2_free()
+    assert bd.gpt2_grad_sumsq_range(0, 0)[0] == bd.GPT2_ESTATE
+    assert bd.gpt2_adamw_step_range(1e-3, 0.9, 0.95, 1e-8, 0.0, 1, 0, 0, 1.0, 1) == bd.GPT2_ESTATE
